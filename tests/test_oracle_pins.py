@@ -1,0 +1,346 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: worked examples
+derived by hand (tests/golden), closed forms, library routines on special cases,
+brute force on tiny inputs and invariants.  CPU only.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sfi_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(20260312)
+
+
+def _rand_qkv(Hq=4, Hkv=2, n=37, D=8, scale=1.0, seed=0):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((Hq, D)) * scale
+    K = r.standard_normal((Hkv, n, D)) * scale
+    V = r.standard_normal((Hkv, n, D))
+    return q, K, V
+
+
+# ---------------------------------------------------------------------------- attention
+def test_attention_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "fusion_and_softmax.json")))["attention"]
+    q = np.array([[1.0, 0.0]])
+    K = np.array([[[0.0, 0.0], [math.sqrt(2) * math.log(3), 0.0]]])
+    V = np.array([g["v"]])
+    o, z, lse, p = O.attention(q, K, V)
+    np.testing.assert_allclose(p[0], g["p"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(o[0], g["o"], rtol=0, atol=1e-14)
+    assert abs(lse[0] - math.log(4)) < 1e-15
+
+
+def test_softmax_sums_to_one_and_lse():
+    q, K, V = _rand_qkv(scale=3.0)
+    o, z, lse, p = O.attention(q, K, V)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    assert (p >= 0).all()
+    # lse is the log of the partition function of z, evaluated directly
+    np.testing.assert_allclose(lse, [math.log(sum(math.exp(x) for x in row)) for row in z],
+                               rtol=1e-13)
+
+
+def test_attention_matches_torch_sdpa_fp64():
+    Hq, Hkv, n, D = 8, 2, 53, 16
+    q, K, V = _rand_qkv(Hq, Hkv, n, D, scale=2.0, seed=3)
+    o, _, _, _ = O.attention(q, K, V)
+    G = Hq // Hkv
+    tq = torch.from_numpy(q)[None, :, None, :]                   # [1, Hq, 1, D]
+    tk = torch.from_numpy(K).repeat_interleave(G, dim=0)[None]   # [1, Hq, n, D]
+    tv = torch.from_numpy(V).repeat_interleave(G, dim=0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0, :, 0].numpy()
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_explicit_loops_tiny():
+    q, K, V = _rand_qkv(2, 1, 5, 3, seed=5)
+    o, z, lse, p = O.attention(q, K, V)
+    for h in range(2):
+        zz = [sum(q[h][d] * K[0][j][d] for d in range(3)) / math.sqrt(3) for j in range(5)]
+        ee = [math.exp(x) for x in zz]
+        tot = sum(ee)
+        for d in range(3):
+            ref = sum(ee[j] / tot * V[0][j][d] for j in range(5))
+            assert abs(o[h][d] - ref) < 1e-13
+        np.testing.assert_allclose(z[h], zz, rtol=1e-13)
+
+
+def test_attention_key_permutation_invariance():
+    q, K, V = _rand_qkv(seed=7)
+    perm = rng.permutation(K.shape[1])
+    o1, z1, l1, _ = O.attention(q, K, V)
+    o2, z2, l2, _ = O.attention(q, K[:, perm], V[:, perm])
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+    np.testing.assert_allclose(z1[:, perm], z2, atol=1e-13)
+
+
+def test_lse_merge_of_splits_equals_unsplit():
+    q, K, V = _rand_qkv(n=61, seed=9, scale=2.5)
+    o, _, lse, _ = O.attention(q, K, V)
+    cuts = [0, 7, 30, 31, 61]
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        oo, _, ll, _ = O.attention(q, K[:, a:b], V[:, a:b])
+        parts.append((oo, ll))
+    om, lm = O.merge_segments(parts)
+    np.testing.assert_allclose(om, o, atol=1e-13)
+    np.testing.assert_allclose(lm, lse, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------ schedule
+def _schedule_by_segments(flags, budget):
+    """Independent construction: slow steps are step 0, the flagged steps, and then every
+    (budget+1)-th step inside each gap between consecutive such anchors."""
+    B, S = flags.shape
+    out = np.zeros((B, S), np.uint8)
+    for b in range(B):
+        anchors = sorted({0} | {s for s in range(S) if flags[b, s]})
+        anchors.append(S)
+        for a0, a1 in zip(anchors[:-1], anchors[1:]):
+            for s in range(a0, a1, budget + 1):
+                out[b, s] = 1
+    return out
+
+
+@pytest.mark.parametrize("budget", [0, 1, 3, 8, 32])
+def test_schedule_against_direct_construction(budget):
+    flags = (rng.random((5, 300)) < 0.07).astype(np.uint8)
+    m = O.schedule(flags, budget)
+    np.testing.assert_array_equal(m, _schedule_by_segments(flags, budget))
+    for b in range(5):
+        run = 0
+        for s in range(300):
+            run = 0 if m[b, s] else run + 1
+            assert run <= budget
+        assert m[b, 0] == 1
+        assert all(m[b, s] == 1 for s in range(300) if flags[b, s])
+
+
+def test_schedule_budget_zero_is_all_slow():
+    assert O.schedule(np.zeros((2, 9), np.uint8), 0).all()
+
+
+# ------------------------------------------------------------------------------ Selector
+def test_evidence_is_distribution():
+    q, K, V = _rand_qkv(Hq=8, Hkv=2, n=40, seed=11)
+    _, _, _, p = O.attention(q, K, V)
+    f = O.evidence(p, 2)
+    np.testing.assert_allclose(f.sum(axis=1), 1.0, atol=1e-14)
+    assert (f >= 0).all()
+    # one query head per KV head: f is that head's distribution
+    np.testing.assert_allclose(O.evidence(p, 8), p, atol=0)
+
+
+def test_key_norms_library():
+    K = rng.standard_normal((3, 20, 16))
+    np.testing.assert_allclose(O.key_norms(K), np.sqrt((K ** 2).sum(-1)), rtol=1e-14)
+
+
+def test_prior_invariants():
+    norms = np.exp(rng.standard_normal((3, 50)))
+    r = O.prior(norms)
+    np.testing.assert_allclose(r.sum(axis=1), 1.0, atol=1e-14)
+    assert (r > 0).all()
+    # equal norms: depends on position only and grows with distance from the newest
+    re = O.prior(np.full((2, 50), 1.7))
+    np.testing.assert_allclose(re[0], re[1], atol=0)
+    assert (np.diff(re[0]) < 0).all()
+    # a larger key norm lowers that position's prior (key-norm suppression)
+    n2 = norms.copy()
+    n2[1, 20] *= 4.0
+    r2 = O.prior(n2)
+    assert r2[1, 20] < r[1, 20]
+    # common rescaling of every norm does not change the distribution
+    np.testing.assert_allclose(O.prior(norms * 3.0), r, rtol=1e-13)
+    # the 1e-6 floor keeps zero-norm keys finite
+    z = norms.copy()
+    z[0, 3] = 0.0
+    assert np.isfinite(O.prior(z)).all()
+
+
+def test_fusion_worked_example_and_endpoints():
+    g = json.load(open(os.path.join(GOLDEN, "fusion_and_softmax.json")))["fusion"]
+    s = O.fuse(np.array(g["f"]), np.array(g["r"]), g["lambda"])
+    np.testing.assert_allclose(s, g["s"], atol=1e-16)
+    f = rng.dirichlet(np.ones(30), size=2)
+    r = rng.dirichlet(np.ones(30), size=2)
+    np.testing.assert_array_equal(O.fuse(f, r, 0.0), f)
+    np.testing.assert_array_equal(O.fuse(f, r, 1.0), r)
+    np.testing.assert_allclose(O.fuse(f, r, 0.3).sum(axis=1), 1.0, atol=1e-14)
+
+
+def _kl_objective(s, f, r, lam):
+    s = np.clip(s, 1e-300, None)
+    return (1 - lam) * np.sum(f * np.log(f / s)) + lam * np.sum(r * np.log(r / s))
+
+
+@pytest.mark.parametrize("lam", [0.1, 0.3, 0.7])
+def test_fusion_is_kl_minimiser(lam):
+    from scipy.optimize import minimize
+    for n in (3, 7, 12):
+        f = rng.dirichlet(np.ones(n))
+        r = rng.dirichlet(np.ones(n))
+        s_star = O.fuse(f, r, lam)
+        res = minimize(lambda x: _kl_objective(x, f, r, lam), np.full(n, 1.0 / n),
+                       method="SLSQP", bounds=[(1e-12, 1)] * n,
+                       constraints=[{"type": "eq", "fun": lambda x: x.sum() - 1}],
+                       options={"ftol": 1e-15, "maxiter": 1000})
+        np.testing.assert_allclose(res.x, s_star, atol=1e-6)
+        base = _kl_objective(s_star, f, r, lam)
+        for _ in range(200):
+            d = rng.standard_normal(n)
+            d -= d.mean()
+            d *= 1e-3 * s_star.min() / np.abs(d).max()
+            assert _kl_objective(s_star + d, f, r, lam) >= base - 1e-15
+
+
+def test_refine_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "selector_worked_example.json")))
+    s = np.array(g["scores"], float)
+    lo, hi = O.candidates(g["N"], g["n_sink"], g["n_recent"])
+    assert (lo, hi) == (2, 10)
+    ref = O.refine(s, lo, hi, g["R"], g["alpha_soft"], g["alpha_cross"])
+    np.testing.assert_array_equal(ref.dom.astype(int), g["dom"])
+    owner = np.where(~ref.exc[0], 0, 1)
+    np.testing.assert_array_equal(owner, g["owner"])
+    np.testing.assert_allclose(np.exp(ref.ellp), np.array(g["refined"], float), rtol=1e-14)
+    for K, key in ((3, "top3"), (2, "top2")):
+        sel = O.select_from_scores(s, g["N"], g["n_sink"], g["n_recent"], K, g["R"],
+                                   g["alpha_soft"], g["alpha_cross"])
+        np.testing.assert_array_equal(sel, g[key])
+
+
+def test_refine_identity_at_zero_alpha():
+    s = rng.dirichlet(np.ones(80), size=3)
+    ref = O.refine(s, 4, 70, 4, 0.0, 0.0)
+    np.testing.assert_array_equal(ref.ellp, np.log(s[:, 4:70]))
+
+
+def test_refine_soft_one_keeps_only_local_maxima():
+    from scipy.ndimage import maximum_filter1d
+    for R in (1, 3, 8):
+        s = rng.dirichlet(np.ones(120), size=3)
+        lo, hi = 5, 100
+        ref = O.refine(s, lo, hi, R, 1.0, 0.0)
+        ell = np.log(s[:, lo:hi])
+        mx = maximum_filter1d(ell, size=2 * R + 1, axis=1, mode="constant", cval=-np.inf)
+        np.testing.assert_array_equal(np.isfinite(ref.ellp), ell >= mx)
+
+
+def test_refine_cross_one_keeps_only_owned():
+    s = rng.dirichlet(np.ones(90), size=4)
+    lo, hi = 3, 80
+    ref = O.refine(s, lo, hi, 2, 0.0, 1.0)
+    owner = np.argmax(s[:, lo:hi], axis=0)
+    for g in range(4):
+        np.testing.assert_array_equal(np.isfinite(ref.ellp[g]), owner == g)
+    # each head owns >= K candidates here, so the selections are pairwise disjoint
+    counts = np.bincount(owner, minlength=4)
+    K = int(counts.min())
+    sel = O.topk(ref.ellp, lo, K)
+    sets = [set(row.tolist()) for row in sel]
+    for a, b in itertools.combinations(range(4), 2):
+        assert not (sets[a] & sets[b])
+
+
+def test_refine_single_head_has_no_exclusivity():
+    s = rng.dirichlet(np.ones(30), size=1)
+    ref = O.refine(s, 0, 30, 2, 0.0, 0.9)
+    assert not ref.exc.any()
+
+
+def _brute_topk(vals, K):
+    n = len(vals)
+    best = None
+    for sub in itertools.combinations(range(n), K):
+        key = (sum(vals[i] for i in sub), tuple(-i for i in sub))
+        if best is None or key > best[0]:
+            best = (key, sub)
+    return list(best[1])
+
+
+def test_topk_brute_force_with_ties():
+    for trial in range(60):
+        n = int(rng.integers(1, 11))
+        K = int(rng.integers(1, n + 1))
+        # small integers force many exact ties
+        vals = rng.integers(-3, 4, size=n).astype(float)
+        sel = O.topk(vals[None, :], 10, K)[0]
+        assert list(sel - 10) == _brute_topk(list(vals), K)
+
+
+def test_topk_padding_and_order():
+    ellp = np.log(rng.dirichlet(np.ones(6), size=2))
+    sel = O.topk(ellp, 4, 9)
+    assert (sel[:, 6:] == -1).all()
+    assert (np.diff(sel[:, :6], axis=1) > 0).all()
+    assert set(sel[0, :6]) == set(range(4, 10))
+    sel0 = O.topk(np.zeros((2, 0)), 4, 3)
+    assert (sel0 == -1).all()
+
+
+def test_topk_with_neg_inf_scores():
+    v = np.array([[-np.inf, 0.0, -np.inf, -1.0, -np.inf]])
+    np.testing.assert_array_equal(O.topk(v, 0, 3)[0], [0, 1, 3])
+
+
+# ---------------------------------------------------------------------------------- pack
+def test_pack_rows_are_stored_rows():
+    K = rng.standard_normal((2, 50, 8)).astype(np.float32)
+    V = rng.standard_normal((2, 50, 8)).astype(np.float32)
+    sel = np.array([[7, 9, 30, -1], [5, 6, 40, 41]])
+    pos, pk, pv = O.pack(K, V, sel, 3)
+    assert list(pos[0]) == [0, 1, 2, 7, 9, 30]
+    assert list(pos[1]) == [0, 1, 2, 5, 6, 40, 41]
+    for g in range(2):
+        for i, j in enumerate(pos[g]):
+            assert pk[g][i].tobytes() == K[g, j].tobytes()
+            assert pv[g][i].tobytes() == V[g, j].tobytes()
+
+
+# ---------------------------------------------------------------------------- fast step
+def test_fast_two_segments_equal_single_pass():
+    q, K, V = _rand_qkv(Hq=6, Hkv=3, n=70, D=8, seed=13, scale=2.0)
+    packed = [np.array([0, 1, 5, 9, 20]), np.array([0, 1, 2, 3]), np.array([0, 1, 44])]
+    a = O.fast_attention(q, K, V, packed, 50, 70)
+    b = O.fast_attention_single_pass(q, K, V, packed, 50, 70)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-13)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-13)
+
+
+def test_fast_equals_dense_when_k_covers_candidates():
+    """spec invariant: with K >= |C| every fast step equals dense attention."""
+    Hq, Hkv, D, ctx, S = 4, 2, 8, 60, 25
+    r = np.random.default_rng(17)
+    K = r.standard_normal((Hkv, ctx + S, D)) * 2
+    V = r.standard_normal((Hkv, ctx + S, D))
+    q = r.standard_normal((S, Hq, D)) * 2
+    flags = (r.random(S) < 0.2).astype(np.uint8)
+    recs = O.run_sequence(q, K, V, flags, ctx, 3, 8, 10_000, 2, 0.5, 0.5, 0.3, 5)
+    assert any(rc.mode == 0 for rc in recs) and sum(rc.mode for rc in recs) > 1
+    for rc in recs:
+        o, _, lse, _ = O.attention(q[rc.step], K[:, :rc.N], V[:, :rc.N])
+        np.testing.assert_allclose(rc.o, o, atol=1e-12)
+        np.testing.assert_allclose(rc.lse, lse, atol=1e-12)
+
+
+def test_fast_memory_partitions_history():
+    """Sink, candidates and the frozen-edge recent window cover [0, N) exactly once."""
+    for N0, W, ns in ((100, 10, 4), (10, 20, 4), (5, 1, 4), (64, 60, 4)):
+        lo, hi = O.candidates(N0, ns, W)
+        rs = O.recent_start_at(N0, ns, W)
+        assert hi == rs
+        for c in range(0, 6):
+            N = N0 + c
+            cover = list(range(0, ns)) + list(range(lo, hi)) + list(range(rs, N))
+            assert sorted(cover) == list(range(N)) or N0 < ns
