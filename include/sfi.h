@@ -1,0 +1,191 @@
+/*
+ * sfi.h -- C ABI of the Slow-Fast Inference (SFI) decode path on MI355X (gfx950).
+ *
+ * The method (pages: "Slow-Fast Inference: Training-Free Inference Acceleration via
+ * Within-Sentence Support Stability", cited by summary language and section):
+ *   - slow steps run dense attention over the whole history and hand their attention
+ *     evidence to the Selector (es "2. Metodología / Pasos Lentos", zh "2.1 慢步骤");
+ *   - the Selector fuses that evidence f with a cached-statistics prior r as
+ *     s = (1-λ) f + λ r, refines the log-scores with soft-NMS and cross-head exclusivity
+ *     and takes a Top-K per head (zh "2.2 训练无感的 Selector", nl "De Selector");
+ *   - sink and selected rows are packed into a contiguous buffer; fast steps attend to
+ *     that buffer plus the recent window read from the paged cache (zh "2.3 系统级优化",
+ *     nl "Systeemontwerp en Kernel-optimalisatie").
+ *
+ * Conventions shared by every entry point
+ *   Memory     Every pointer argument except `shape`/`params` is DEVICE memory owned by
+ *              the caller.  The library never allocates, frees or retains memory and
+ *              keeps no mutable global state; it is safe to call from several threads on
+ *              different streams.
+ *   Streams    `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *              work and never synchronise; buffers must stay alive until the stream has
+ *              passed the work.
+ *   Batch rows `seq_ids[0..n_seqs)` (device, int32) lists the batch rows b a call serves,
+ *              so one decode step can send slow and fast sequences to different calls.
+ *              Per-row tensors are indexed by b.  n_seqs == 0 is a no-op returning SFI_OK.
+ *   Errors     Host-side checks run before anything is enqueued and return a negative
+ *              code with nothing enqueued.  After enqueueing, a launch failure reported
+ *              by hipGetLastError is returned as SFI_E_HIP.  Device-side contracts (seq
+ *              lengths within bounds, valid pages, indices in range) are trusted.
+ *   Layouts    (all row-major, innermost last)
+ *     q            f32  [batch, Hq, D]
+ *     k_cache      elt  [num_pages, Hkv, 16, D]   page p holds 16 consecutive positions
+ *     v_cache      elt  [num_pages, Hkv, 16, D]
+ *     block_table  i32  [batch, max_pages_per_seq]  position j of row b lives in physical
+ *                       page block_table[b][j / 16], slot j % 16
+ *     seq_lens     i32  [batch]   KV length N_b; position N_b-1 is the current token
+ *     out          f32  [batch, Hq, D]
+ *     lse          f32  [batch, Hq]   natural-log partition function of the logits
+ *     logits       f32  [batch, Hq, logits_stride]  z = q·k / sqrt(D)
+ *     key_norm     f32  [batch, Hkv, norm_stride]   ||k||_2 of every stored key row
+ *     sel_idx      i32  [batch, Hkv, top_k]   ascending positions, then -1 padding
+ *     packed_k/v   elt  [batch, Hkv, packed_cap, D]   packed_cap = round_up(n_sink+top_k, 16)
+ *     packed_pos   i32  [batch, Hkv, packed_cap]
+ *     packed_len   i32  [batch, Hkv]
+ *     recent_start i32  [batch]
+ *   Query head h reads KV head h / G, G = Hq / Hkv.  "elt" is bf16 or f32 per
+ *   sfi_shape.dtype.  q, K/V, packed and out pointers must be 16-byte aligned;
+ *   logits/key_norm strides must be multiples of 4 elements.
+ */
+#ifndef SFI_H
+#define SFI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SFI_ABI_VERSION 1
+
+enum sfi_status {
+  SFI_OK = 0,
+  SFI_E_ARG = -1,          /* NULL pointer, non-positive dims, Hq % Hkv != 0, bad params  */
+  SFI_E_UNSUPPORTED = -2,  /* D not in {64,128}, dtype, G > 16, page_size != 16          */
+  SFI_E_ALIGN = -3,        /* a pointer or stride breaks the alignment rules above       */
+  SFI_E_WORKSPACE = -4,    /* workspace NULL or smaller than the matching *_ws() query   */
+  SFI_E_CAPACITY = -5,     /* a length exceeds what the buffers or block table can hold  */
+  SFI_E_HIP = -6           /* a kernel launch failed                                     */
+};
+
+enum sfi_dtype { SFI_BF16 = 0, SFI_F32 = 1 };
+
+typedef struct {
+  int32_t batch;              /* rows of block_table / seq_lens                           */
+  int32_t num_q_heads;        /* Hq                                                       */
+  int32_t num_kv_heads;       /* Hkv, Hq % Hkv == 0 and G = Hq / Hkv <= 16               */
+  int32_t head_dim;           /* D in {64, 128}                                           */
+  int32_t page_size;          /* must be 16                                               */
+  int32_t max_pages_per_seq;  /* columns of block_table                                   */
+  int32_t dtype;              /* enum sfi_dtype: element type of every K/V buffer         */
+} sfi_shape;
+
+typedef struct {
+  int32_t n_sink;       /* sink rows [0, n_sink) always in the fast memory (>= 0)         */
+  int32_t n_recent;     /* recent window W: candidates are [n_sink, N - W) (>= 0)         */
+  int32_t top_k;        /* K selected positions per KV head (>= 1)                        */
+  int32_t nms_radius;   /* soft-NMS radius R (>= 0)                                       */
+  float lambda;         /* fusion weight of the prior, in [0, 1]                          */
+  float alpha_soft;     /* soft-NMS penalty: a dominated score is scaled by 1 - alpha     */
+  float alpha_cross;    /* exclusivity penalty: a non-owner score is scaled by 1 - alpha  */
+} sfi_select_params;
+
+/* ABI version (SFI_ABI_VERSION) and a static description of a status code. */
+int sfi_abi_version(void);
+const char* sfi_status_str(int code);
+
+/* Workspace sizes in bytes for the calls below (pure host functions, 0 if the arguments
+ * are invalid).  The workspace needs no initialisation and holds nothing between calls. */
+size_t sfi_slow_attn_ws(const sfi_shape* shape, int32_t n_seqs, int32_t max_seq_len);
+size_t sfi_fast_attn_ws(const sfi_shape* shape, int32_t n_seqs, int32_t packed_cap,
+                        int32_t max_recent);
+size_t sfi_select_ws(const sfi_shape* shape, const sfi_select_params* params,
+                     int32_t n_seqs, int32_t max_seq_len);
+
+/* Round-up of n_sink + top_k to a multiple of 16: rows per (b, KV head) of the packed
+ * buffers. */
+int32_t sfi_packed_cap(const sfi_select_params* params);
+
+/*
+ * sfi_key_norms -- cached key statistic ||k_{b,g,j}||_2 for positions [pos_begin, pos_end)
+ * of every KV head of the listed rows (the Selector's prior reads key norms kept with the
+ * cache, zh "2.2 输入 ... 缓存的统计信息").  Run at prefill / append time.
+ * key_norm[b][g][j] is written for j in [pos_begin, min(pos_end, N_b)).
+ */
+int sfi_key_norms(const sfi_shape* shape, const void* k_cache, const int32_t* block_table,
+                  const int32_t* seq_lens, const int32_t* seq_ids, int32_t n_seqs,
+                  int32_t pos_begin, int32_t pos_end, float* key_norm, int64_t norm_stride,
+                  void* stream);
+
+/*
+ * sfi_slow_attn -- dense decode attention of a slow step over all N_b positions of each
+ * listed row (es "Pasos Lentos": dense attention over the whole accessible history).
+ * Writes out[b] and lse[b]; when `logits` is not NULL also z[b][h][j] for j < N_b, the
+ * evidence the Selector reads.  With logits == NULL this is the Full-KV dense step.
+ * max_seq_len >= every listed N_b sizes the split of the work (<= max_pages_per_seq*16).
+ * ws: sfi_slow_attn_ws(shape, n_seqs, max_seq_len) bytes.
+ */
+int sfi_slow_attn(const sfi_shape* shape, const float* q, const void* k_cache,
+                  const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                  const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len, float* out,
+                  float* logits, int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/*
+ * sfi_select -- the training-free Selector of a slow step (zh "2.2", fr "2.B",
+ * nl "De Selector"), per listed row b and KV head g, at N = N_b:
+ *   f(g,j)  = mean over the G query heads of g of exp(z(h,j) - lse(h))
+ *   r(g,j)  = phi_key * phi_pos / sum_{j'<N} phi_key * phi_pos,
+ *             phi_key = 1 / max(key_norm, 1e-6), phi_pos = 1 + ln(1 + (N - 1 - j))
+ *   s       = (1 - lambda) f + lambda r                       (the closed-form fusion)
+ *   on candidates C = [n_sink, N - n_recent):
+ *   s'      = s * (1-alpha_soft)^dom * (1-alpha_cross)^exc   (log-score refinement)
+ *             dom: a candidate within nms_radius in the same head has a strictly larger s
+ *             exc: g is not the owner of j (the head with the largest s at j, lowest g
+ *                  on ties)
+ *   sel_idx = the min(top_k, |C|) candidates with the largest s' (ties to the lower
+ *             position), ascending, then -1 up to top_k.
+ * logits/lse come from sfi_slow_attn of the same step.  When dbg_scores is not NULL it
+ * receives s as f32 [batch, Hkv, logits_stride] for j < N_b.
+ * ws: sfi_select_ws(shape, params, n_seqs, max_seq_len) bytes.
+ */
+int sfi_select(const sfi_shape* shape, const sfi_select_params* params, const float* logits,
+               int64_t logits_stride, const float* lse, const float* key_norm,
+               int64_t norm_stride, const int32_t* seq_lens, const int32_t* seq_ids,
+               int32_t n_seqs, int32_t max_seq_len, int32_t* sel_idx, float* dbg_scores,
+               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sfi_pack -- gather the sink rows [0, n_sink) and the selected rows sel_idx[b][g][*]
+ * (ascending, -1 padded) from the paged cache into the contiguous buffers
+ * (zh "2.3 将 Sink 和 Selected Tokens 打包到连续的紧凑缓冲区").  Row i of packed_k/v[b][g]
+ * is a byte copy of the cache row at packed_pos[b][g][i]; rows past packed_len[b][g] are
+ * zero with packed_pos -1.  sel_idx must hold its valid entries first (as sfi_select
+ * writes it).  packed_cap must equal sfi_packed_cap(params).
+ */
+int sfi_pack(const sfi_shape* shape, const sfi_select_params* params, const void* k_cache,
+             const void* v_cache, const int32_t* block_table, const int32_t* sel_idx,
+             const int32_t* seq_ids, int32_t n_seqs, void* packed_k, void* packed_v,
+             int32_t* packed_pos, int32_t* packed_len, int32_t packed_cap, void* stream);
+
+/*
+ * sfi_fast_attn -- two-segment attention of a fast step (zh "2.3 两段式"): segment A is
+ * rows [0, packed_len[b][g]) of the packed buffers, read contiguously; segment B is
+ * positions [recent_start[b], N_b) read from the paged cache.  The two partial results
+ * are merged by log-sum-exp into out[b] (and lse[b] if not NULL).
+ * max_recent >= every listed N_b - recent_start[b] sizes the split of segment B.
+ * ws: sfi_fast_attn_ws(shape, n_seqs, packed_cap, max_recent) bytes.
+ */
+int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
+                  const void* packed_v, const int32_t* packed_len, int32_t packed_cap,
+                  const void* k_cache, const void* v_cache, const int32_t* block_table,
+                  const int32_t* recent_start, const int32_t* seq_lens,
+                  const int32_t* seq_ids, int32_t n_seqs, int32_t max_recent, float* out,
+                  float* lse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFI_H */

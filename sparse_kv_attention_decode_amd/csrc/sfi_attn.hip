@@ -1,0 +1,549 @@
+// Split-K decode attention for SFI slow steps (dense, over the paged cache) and fast
+// steps (two segments: the packed sink+selected buffer and the recent window in pages).
+//
+// Slow steps attend densely to the whole history and expose their logits as the
+// Selector's evidence (es "2. Metodología / Pasos Lentos", zh "2.1 慢步骤 / 2.2 输入");
+// fast steps attend to the compact contiguous buffer plus the recent tokens read straight
+// from the paged cache (zh "2.3 两段式", nl "Memory-Coalesced Kernel").
+//
+// One wavefront owns one split: a run of 16-row tiles of one (row b, KV head g).  All
+// G <= 16 query heads of g share the K/V reads.  bf16 caches go through MFMA:
+//   * logits   z[16 rows x 16 heads] = K_tile(16x D) * Q^T, as D/32 steps of
+//     v_mfma_f32_16x16x32_bf16.  q is split exactly into three bf16 terms (hi+mid+lo,
+//     truncation, so hi+mid+lo == q), and every bf16 x bf16 product is exact in fp32,
+//     which keeps z at fp32 accuracy.
+//   * V^T      the same MFMA against 0/1 selection matrices turns the row-major V tile
+//     into the column layout the PV product needs (exact: one nonzero term per output).
+//   * PV       O^T[dim][head] += V^T * P^T with v_mfma_f32_16x16x16bf16, P split into two
+//     bf16 terms (relative error < 2^-16).
+//   Lane l = 16*qd + r holds row r of each loaded K/V tile (16 B per 32-dim step: every
+//   wave load reads 16 contiguous 64-byte segments) and, after the products, logits and
+//   probabilities of head r at rows 4*qd .. 4*qd+3.
+// fp32 caches use a plain VALU path with the same partial-result format.
+// Each split writes its running (max m, sum l, unnormalised o); a merge kernel combines
+// the splits of every query head with log-sum-exp weights.
+#include "sfi_device.h"
+#include "sfi_internal.h"
+
+#include <math.h>
+
+namespace sfi {
+
+static_assert(kMaxG == kMaxGroup, "one MFMA tile covers every query head of a KV head");
+
+namespace {
+
+struct SplitRange {
+  bool packed;
+  int row_lo, row_hi;  // valid logical rows
+  int t0, t1;          // tile range [t0, t1): rows [16 t, 16 t + 16)
+};
+
+__device__ __forceinline__ SplitRange split_range(const AttnParams& p, int b, int g, int split,
+                                                  int N) {
+  SplitRange sr;
+  if (!p.fast) {
+    sr.packed = false;
+    sr.row_lo = 0;
+    sr.row_hi = N;
+    const int ntile = (N + kPage - 1) / kPage;
+    sr.t0 = split * p.tps;
+    sr.t1 = min(sr.t0 + p.tps, ntile);
+  } else if (split < p.nsplit_a) {
+    const int plen = uniform(p.packed_len[b * p.Hkv + g]);
+    sr.packed = true;
+    sr.row_lo = 0;
+    sr.row_hi = plen;
+    const int ntile = (plen + kPage - 1) / kPage;
+    sr.t0 = split * p.tps;
+    sr.t1 = min(sr.t0 + p.tps, ntile);
+  } else {
+    const int rs = uniform(p.recent_start[b]);
+    sr.packed = false;
+    sr.row_lo = rs;
+    sr.row_hi = N;
+    const int first = rs / kPage;
+    const int last = (N + kPage - 1) / kPage;
+    sr.t0 = first + (split - p.nsplit_a) * p.tps;
+    sr.t1 = min(sr.t0 + p.tps, last);
+  }
+  return sr;
+}
+
+__device__ __forceinline__ void write_empty_partial(const AttnParams& p, size_t pidx, int D,
+                                                    int lane) {
+  for (int h = lane; h < p.G; h += kWave) {
+    p.part_m[pidx * p.G + h] = -INFINITY;
+    p.part_l[pidx * p.G + h] = 0.f;
+  }
+  float* o = p.part_o + pidx * p.G * D;
+  for (int k = lane; k < p.G * D; k += kWave) o[k] = 0.f;
+}
+
+// Split x into hi + mid + lo, three truncated bf16 values whose sum is exactly x.
+__device__ __forceinline__ void split3(float x, float& hi, float& mid, float& lo) {
+  hi = trunc_bf16(x);
+  const float r1 = x - hi;
+  mid = trunc_bf16(r1);
+  lo = trunc_bf16(r1 - mid);
+}
+
+template <int D, bool WRITE_Z>
+__global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
+  constexpr int NC = D / 32;   // 32-dim steps of the logit product
+  constexpr int NT = D / 16;   // 16-dim output tiles of the PV product
+  const int lane = threadIdx.x & 63;
+  const int work = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (work >= p.n_seqs * p.Hkv * p.nsplit) return;
+  const int split = work % p.nsplit;
+  const int ig = work / p.nsplit;
+  const int g = ig % p.Hkv;
+  const int i = ig / p.Hkv;
+  const int b = uniform(p.seq_ids[i]);
+  const int N = uniform(p.seq_lens[b]);
+  const int r = lane & 15;
+  const int qd = lane >> 4;
+  const size_t pidx = (size_t)ig * p.nsplit + split;
+
+  const SplitRange sr = split_range(p, b, g, split, N);
+  if (sr.t0 >= sr.t1) {
+    write_empty_partial(p, pidx, D, lane);
+    return;
+  }
+
+  // Query operand: lane (qd, r) holds head r, dims 32c + 8qd .. +8, pre-scaled by 1/sqrt(D).
+  u32x4_t qh[NC], qm[NC], ql[NC];
+  {
+    const bool hv = r < p.G;
+    const float* qrow = p.q + ((size_t)b * p.Hq + (size_t)g * p.G + (hv ? r : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float x[8];
+      if (hv) {
+        const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * c + 8 * qd);
+        const float4 bq = *reinterpret_cast<const float4*>(qrow + 32 * c + 8 * qd + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = bq.x; x[5] = bq.y; x[6] = bq.z; x[7] = bq.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = 0.f;
+      }
+      float h8[8], m8[8], l8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) split3(x[j] * p.scale, h8[j], m8[j], l8[j]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        qh[c][w] = pack_hi16(h8[2 * w], h8[2 * w + 1]);
+        qm[c][w] = pack_hi16(m8[2 * w], m8[2 * w + 1]);
+        ql[c][w] = pack_hi16(l8[2 * w], l8[2 * w + 1]);
+      }
+    }
+  }
+  // Selection matrices E_e[k][n] = (k == n + 16 e), lane (qd, r): k = 8qd + j, n = r.
+  u32x4_t sel[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int k0 = 8 * qd + 2 * w;
+      const uint32_t lo = (k0 == r + 16 * e) ? 0x3f80u : 0u;
+      const uint32_t hi = (k0 + 1 == r + 16 * e) ? 0x3f80u : 0u;
+      sel[e][w] = lo | (hi << 16);
+    }
+  }
+
+  f32x4_t O[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) O[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  if (sr.packed) {
+    const size_t off = ((size_t)b * p.Hkv + g) * (size_t)p.packed_cap * D;
+    kbase = reinterpret_cast<const uint16_t*>(p.packed_k) + off;
+    vbase = reinterpret_cast<const uint16_t*>(p.packed_v) + off;
+  } else {
+    kbase = reinterpret_cast<const uint16_t*>(p.k_cache);
+    vbase = reinterpret_cast<const uint16_t*>(p.v_cache);
+  }
+  const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+  const int lane_off = r * D + 8 * qd;
+  float* zrow = (WRITE_Z && r < p.G)
+                    ? p.logits + ((size_t)b * p.Hq + (size_t)g * p.G + r) * p.logits_stride
+                    : nullptr;
+
+  auto tile_offset = [&](int t) -> size_t {
+    if (sr.packed) return (size_t)t * kPage * D;
+    const int page = uniform(bt[t]);
+    return ((size_t)page * p.Hkv + g) * (size_t)(kPage * D);
+  };
+
+  u32x4_t kr[NC], vr[NC];
+  {
+    const size_t off = tile_offset(sr.t0) + lane_off;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kr[c] = *reinterpret_cast<const u32x4_t*>(kbase + off + 32 * c);
+      vr[c] = *reinterpret_cast<const u32x4_t*>(vbase + off + 32 * c);
+    }
+  }
+
+  for (int t = sr.t0; t < sr.t1; ++t) {
+    // Prefetch the next tile while this one is consumed.
+    u32x4_t kn[NC], vn[NC];
+    if (t + 1 < sr.t1) {
+      const size_t off = tile_offset(t + 1) + lane_off;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        kn[c] = *reinterpret_cast<const u32x4_t*>(kbase + off + 32 * c);
+        vn[c] = *reinterpret_cast<const u32x4_t*>(vbase + off + 32 * c);
+      }
+    }
+    const int pos0 = t * kPage;
+    const bool full = pos0 >= sr.row_lo && pos0 + kPage <= sr.row_hi;
+    if (!full) {
+      const int pr = pos0 + r;
+      if (pr < sr.row_lo || pr >= sr.row_hi) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) vr[c] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+    // Logits: D[m = row][n = head].  Accumulate the small terms first.
+    f32x4_t za = {0.f, 0.f, 0.f, 0.f}, zb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) zb = mfma32(kr[c], ql[c], zb);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) zb = mfma32(kr[c], qm[c], zb);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) za = mfma32(kr[c], qh[c], za);
+    float z[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) z[k] = za[k] + zb[k];
+    if (!full) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int pr = pos0 + 4 * qd + k;
+        if (pr < sr.row_lo || pr >= sr.row_hi) z[k] = -INFINITY;
+      }
+    }
+    if (WRITE_Z && zrow) {
+      if (full) {
+        *reinterpret_cast<float4*>(zrow + pos0 + 4 * qd) = make_float4(z[0], z[1], z[2], z[3]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int pr = pos0 + 4 * qd + k;
+          if (pr >= sr.row_lo && pr < sr.row_hi) zrow[pr] = z[k];
+        }
+      }
+    }
+    // V^T tiles: lane (qd, r) gets V[row 4qd + k][dim 16 tt + r], k = 0..3.
+    u32x2_t vt[NT];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const f32x4_t tr = mfma32(vr[c], sel[e], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        vt[2 * c + e] = u32x2_t{pack_hi16(tr[0], tr[1]), pack_hi16(tr[2], tr[3])};
+      }
+    }
+    // Online softmax of head r over this tile.
+    float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __expf(m_run - m_use);
+    float pv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pv[k] = __expf(z[k] - m_use);
+    l_run = l_run * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) O[tt][k] *= alpha;
+      }
+    }
+    m_run = m_new;
+    // P^T operand, split into hi + lo bf16 terms.
+    float pl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pl[k] = pv[k] - trunc_bf16(pv[k]);
+    const u32x2_t ph2 = {pack_hi16(pv[0], pv[1]), pack_hi16(pv[2], pv[3])};
+    const u32x2_t pl2 = {pack_hi16(pl[0], pl[1]), pack_hi16(pl[2], pl[3])};
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      O[tt] = mfma16(vt[tt], pl2, O[tt]);
+      O[tt] = mfma16(vt[tt], ph2, O[tt]);
+    }
+    if (t + 1 < sr.t1) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        kr[c] = kn[c];
+        vr[c] = vn[c];
+      }
+    }
+  }
+
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (r < p.G) {
+    if (qd == 0) {
+      p.part_m[pidx * p.G + r] = m_run;
+      p.part_l[pidx * p.G + r] = l_tot;
+    }
+    float* o = p.part_o + (pidx * p.G + r) * D + 4 * qd;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      *reinterpret_cast<float4*>(o + 16 * tt) = make_float4(O[tt][0], O[tt][1], O[tt][2], O[tt][3]);
+  }
+}
+
+// fp32 caches: one wavefront per split, VALU only.
+template <int D, bool WRITE_Z>
+__global__ __launch_bounds__(64) void k_attn_partial_f32(AttnParams p) {
+  constexpr int DD = D / kWave;
+  __shared__ float qs[kMaxG][D];
+  __shared__ float zt[kMaxG][kPage];
+  const int lane = threadIdx.x;
+  const int work = blockIdx.x;
+  if (work >= p.n_seqs * p.Hkv * p.nsplit) return;
+  const int split = work % p.nsplit;
+  const int ig = work / p.nsplit;
+  const int g = ig % p.Hkv;
+  const int i = ig / p.Hkv;
+  const int b = uniform(p.seq_ids[i]);
+  const int N = uniform(p.seq_lens[b]);
+  const size_t pidx = (size_t)ig * p.nsplit + split;
+  const SplitRange sr = split_range(p, b, g, split, N);
+  if (sr.t0 >= sr.t1) {
+    write_empty_partial(p, pidx, D, lane);
+    return;
+  }
+  const int G = p.G;
+  for (int k = lane; k < G * D; k += kWave) {
+    const int h = k / D, d = k % D;
+    qs[h][d] = p.q[((size_t)b * p.Hq + (size_t)g * G + h) * D + d] * p.scale;
+  }
+  __syncthreads();
+
+  const float* kbase;
+  const float* vbase;
+  if (sr.packed) {
+    const size_t off = ((size_t)b * p.Hkv + g) * (size_t)p.packed_cap * D;
+    kbase = reinterpret_cast<const float*>(p.packed_k) + off;
+    vbase = reinterpret_cast<const float*>(p.packed_v) + off;
+  } else {
+    kbase = reinterpret_cast<const float*>(p.k_cache);
+    vbase = reinterpret_cast<const float*>(p.v_cache);
+  }
+  const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+
+  float m_run[kMaxG], l_run[kMaxG], acc[kMaxG][DD];
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int dd = 0; dd < DD; ++dd) acc[h][dd] = 0.f;
+  }
+  const int r = lane & 15, hq = lane >> 4;
+  for (int t = sr.t0; t < sr.t1; ++t) {
+    size_t toff;
+    if (sr.packed) {
+      toff = (size_t)t * kPage * D;
+    } else {
+      const int page = uniform(bt[t]);
+      toff = ((size_t)page * p.Hkv + g) * (size_t)(kPage * D);
+    }
+    const int pos0 = t * kPage;
+    for (int hb = 0; hb < G; hb += 4) {
+      const int h = hb + hq;
+      if (h < G) {
+        const int pr = pos0 + r;
+        float z = -INFINITY;
+        if (pr >= sr.row_lo && pr < sr.row_hi) {
+          const float* krow = kbase + toff + (size_t)r * D;
+          float a = 0.f;
+          for (int d = 0; d < D; ++d) a = fmaf(krow[d], qs[h][d], a);
+          z = a;
+          if (WRITE_Z && p.logits)
+            p.logits[((size_t)b * p.Hq + (size_t)g * G + h) * p.logits_stride + pr] = z;
+        }
+        zt[h][r] = z;
+      }
+    }
+    __syncthreads();
+    float v[kPage][DD];
+#pragma unroll
+    for (int rr = 0; rr < kPage; ++rr) {
+      const int pr = pos0 + rr;
+      const bool ok = pr >= sr.row_lo && pr < sr.row_hi;
+#pragma unroll
+      for (int dd = 0; dd < DD; ++dd)
+        v[rr][dd] = ok ? vbase[toff + (size_t)rr * D + lane + kWave * dd] : 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+      if (h < G) {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int rr = 0; rr < kPage; ++rr) mt = fmaxf(mt, zt[h][rr]);
+        const float m_new = fmaxf(m_run[h], mt);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = expf(m_run[h] - m_use);
+        float ls = 0.f;
+#pragma unroll
+        for (int dd = 0; dd < DD; ++dd) acc[h][dd] *= alpha;
+#pragma unroll
+        for (int rr = 0; rr < kPage; ++rr) {
+          const float pr = expf(zt[h][rr] - m_use);
+          ls += pr;
+#pragma unroll
+          for (int dd = 0; dd < DD; ++dd) acc[h][dd] = fmaf(pr, v[rr][dd], acc[h][dd]);
+        }
+        l_run[h] = l_run[h] * alpha + ls;
+        m_run[h] = m_new;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    if (h < G) {
+      if (lane == 0) {
+        p.part_m[pidx * G + h] = m_run[h];
+        p.part_l[pidx * G + h] = l_run[h];
+      }
+#pragma unroll
+      for (int dd = 0; dd < DD; ++dd) p.part_o[(pidx * G + h) * D + lane + kWave * dd] = acc[h][dd];
+    }
+  }
+}
+
+// One block per (listed row, query head): log-sum-exp merge of the split partials.
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm,
+                                                    const float* __restrict__ pl,
+                                                    const float* __restrict__ po, int nsplit,
+                                                    int Hq, int Hkv, int G, int D,
+                                                    const int32_t* __restrict__ seq_ids,
+                                                    float* __restrict__ out,
+                                                    float* __restrict__ lse) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x / Hq;
+  const int h = blockIdx.x % Hq;
+  const int g = h / G, hh = h % G;
+  const int b = seq_ids[i];
+  const size_t base = ((size_t)i * Hkv + g) * nsplit;
+
+  float mx = -INFINITY;
+  for (int s = tid; s < nsplit; s += 256) mx = fmaxf(mx, pm[(base + s) * G + hh]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+  for (int s = tid; s < nsplit; s += 256) {
+    const float m = pm[(base + s) * G + hh];
+    L += pl[(base + s) * G + hh] * __expf(m - Mu);
+  }
+  red[tid] = L;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  const float Lt = red[0];
+  __syncthreads();
+  const int ngrp = 256 / D;
+  const int d = tid % D, grp = tid / D;
+  float acc = 0.f;
+  for (int s = grp; s < nsplit; s += ngrp) {
+    const float m = pm[(base + s) * G + hh];
+    const float w = __expf(m - Mu);
+    acc += w * po[((base + s) * G + hh) * D + d];
+  }
+  red[tid] = acc;
+  __syncthreads();
+  if (grp == 0) {
+    for (int q = 1; q < ngrp; ++q) acc += red[q * D + d];
+    out[((size_t)b * Hq + h) * D + d] = Lt > 0.f ? acc / Lt : 0.f;
+    if (d == 0 && lse) lse[(size_t)b * Hq + h] = Lt > 0.f ? Mu + logf(Lt) : -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t launch_partial(const AttnParams& p, int dtype, hipStream_t stream) {
+  const int works = p.n_seqs * p.Hkv * p.nsplit;
+  const bool wz = p.logits != nullptr;
+  if (dtype == SFI_BF16) {
+    const int blocks = (works + 3) / 4;
+    if (wz)
+      hipLaunchKernelGGL((k_attn_partial_bf16<D, true>), dim3(blocks), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((k_attn_partial_bf16<D, false>), dim3(blocks), dim3(256), 0, stream, p);
+  } else {
+    if (wz)
+      hipLaunchKernelGGL((k_attn_partial_f32<D, true>), dim3(works), dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((k_attn_partial_f32<D, false>), dim3(works), dim3(64), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+SplitPlan plan_slow(const sfi_shape& s, int n_seqs, int max_seq_len) {
+  SplitPlan sp;
+  const int ntile = (max_seq_len + kPage - 1) / kPage;
+  const long total = (long)n_seqs * s.num_kv_heads * ntile;
+  int tps = (int)((total + 2047) / 2048);
+  tps = tps < 4 ? 4 : (tps > 64 ? 64 : tps);
+  sp.tps = tps;
+  sp.nsplit = (ntile + tps - 1) / tps;
+  sp.nsplit_a = 0;
+  return sp;
+}
+
+SplitPlan plan_fast(const sfi_shape& s, int n_seqs, int packed_cap, int max_recent) {
+  SplitPlan sp;
+  const int ta = packed_cap / kPage;
+  const int tb = (max_recent + kPage - 1) / kPage + 1;  // +1: the window need not start on a page
+  const long total = (long)n_seqs * s.num_kv_heads * (ta + tb);
+  int tps = (int)((total + 2047) / 2048);
+  tps = tps < 4 ? 4 : (tps > 64 ? 64 : tps);
+  sp.tps = tps;
+  sp.nsplit_a = (ta + tps - 1) / tps;
+  sp.nsplit = sp.nsplit_a + (tb + tps - 1) / tps;
+  return sp;
+}
+
+size_t partial_bytes(const sfi_shape& s, int n_seqs, int nsplit) {
+  const size_t G = (size_t)(s.num_q_heads / s.num_kv_heads);
+  const size_t units = (size_t)n_seqs * s.num_kv_heads * nsplit * G;
+  const size_t ml = ((units * sizeof(float) + 255) / 256) * 256;
+  return 2 * ml + units * s.head_dim * sizeof(float);
+}
+
+hipError_t launch_attention(const AttnParams& p0, int head_dim, int dtype, float* out,
+                            float* lse, hipStream_t stream) {
+  AttnParams p = p0;
+  hipError_t e = head_dim == 64 ? launch_partial<64>(p, dtype, stream)
+                                : launch_partial<128>(p, dtype, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_attn_merge, dim3(p.n_seqs * p.Hq), dim3(256), 0, stream, p.part_m,
+                     p.part_l, p.part_o, p.nsplit, p.Hq, p.Hkv, p.G, head_dim, p.seq_ids, out,
+                     lse);
+  return hipGetLastError();
+}
+
+}  // namespace sfi

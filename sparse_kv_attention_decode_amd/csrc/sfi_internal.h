@@ -1,0 +1,81 @@
+// Host-side interfaces between the C ABI shell and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sfi.h"
+
+namespace sfi {
+
+constexpr int kMaxGroup = 16;  // query heads per KV head supported by the kernels
+
+// Work decomposition of one attention call: every (listed row, KV head) pair is cut into
+// `nsplit` splits of `tps` 16-row tiles; each split is one wavefront.  For a fast call the
+// first `nsplit_a` splits cover the packed segment and the rest the recent segment.
+struct SplitPlan {
+  int tps = 0;
+  int nsplit = 0;
+  int nsplit_a = 0;
+};
+
+SplitPlan plan_slow(const sfi_shape& s, int n_seqs, int max_seq_len);
+SplitPlan plan_fast(const sfi_shape& s, int n_seqs, int packed_cap, int max_recent);
+// Bytes of the per-split partial results (m, l, o) of one attention call.
+size_t partial_bytes(const sfi_shape& s, int n_seqs, int nsplit);
+
+struct AttnParams {
+  const float* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* seq_ids;
+  const void* packed_k;        // fast only
+  const void* packed_v;        // fast only
+  const int32_t* packed_len;   // fast only
+  const int32_t* recent_start; // fast only
+  float* logits;               // slow only, may be null
+  int64_t logits_stride;
+  float* part_m;
+  float* part_l;
+  float* part_o;
+  int max_pages;
+  int packed_cap;
+  int n_seqs, Hq, Hkv, G;
+  int tps, nsplit, nsplit_a;
+  int fast;
+  float scale;
+};
+
+hipError_t launch_attention(const AttnParams& p, int head_dim, int dtype, float* out,
+                            float* lse, hipStream_t stream);
+
+hipError_t launch_key_norms(const sfi_shape& s, const void* k_cache,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* seq_ids, int n_seqs, int pos_begin, int pos_end,
+                            float* key_norm, int64_t norm_stride, hipStream_t stream);
+
+struct SelectLayout {
+  int nchunk = 0;        // prior-normaliser chunks per (row, KV head)
+  int64_t kstride = 0;   // key slots per (row, KV head)
+  size_t zpart_off = 0, keys_off = 0, total = 0;
+};
+SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len);
+constexpr int kScoreTile = 256;
+size_t score_lds_bytes(int num_kv_heads, int num_q_heads, int nms_radius);
+
+hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm,
+                         const float* logits, int64_t logits_stride, const float* lse,
+                         const float* key_norm, int64_t norm_stride, const int32_t* seq_lens,
+                         const int32_t* seq_ids, int n_seqs, int max_seq_len,
+                         int32_t* sel_idx, float* dbg_scores, void* ws, hipStream_t stream);
+
+hipError_t launch_pack(const sfi_shape& s, const sfi_select_params& prm, const void* k_cache,
+                       const void* v_cache, const int32_t* block_table, const int32_t* sel_idx,
+                       const int32_t* seq_ids, int n_seqs, void* packed_k, void* packed_v,
+                       int32_t* packed_pos, int32_t* packed_len, int packed_cap,
+                       hipStream_t stream);
+
+}  // namespace sfi

@@ -1,0 +1,217 @@
+"""Decode-step driver of the SFI path: slow/fast schedule on the host, kernels on two HIP
+streams of one GPU.
+
+Step s of every listed sequence is SLOW when s == 0, when its boundary flag is set, or when
+`refresh_budget` fast steps have run since its last slow step, and FAST otherwise (es
+"Pasos Lentos", zh "2.1 触发机制").  A slow step runs dense attention and then the Selector
+and the pack for that layer; a fast step runs two-segment attention over the packed
+buffer and the recent window.
+
+Overlap (es "3. Optimización del Sistema / Pipeline Asíncrono", zh "2.3 异步流水线"): the
+attention of every layer is issued on stream 1; the Selector and pack of layer i are
+issued on stream 2 after an event recorded behind layer i's slow attention, so they run
+while stream 1 continues with layer i+1.  Before layer i's next attention, stream 1 waits
+for layer i's pack event.  Both streams have the default priority.
+
+All per-step tables (sequence lengths, recent-window starts, slow/fast row lists) are
+built on the host from the seeded flags and copied to the device once, so a step issues
+kernels only.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import lib as L
+
+
+def schedule(flags: np.ndarray, budget: int) -> np.ndarray:
+    """mode[b, s] = 1 for SLOW, 0 for FAST."""
+    B, S = flags.shape
+    mode = np.zeros((B, S), np.uint8)
+    for b in range(B):
+        since = 0
+        for s in range(S):
+            slow = s == 0 or bool(flags[b, s]) or since == budget
+            mode[b, s] = 1 if slow else 0
+            since = 0 if slow else since + 1
+    return mode
+
+
+@dataclass
+class Plan:
+    """Host tables of one trajectory."""
+    mode: np.ndarray          # [B, S]
+    seq_len: np.ndarray       # [S, B]
+    recent_start: np.ndarray  # [S, B] (valid at fast steps)
+    slow_ids: List[np.ndarray] = field(default_factory=list)
+    fast_ids: List[np.ndarray] = field(default_factory=list)
+    max_recent: int = 0
+
+
+def make_plan(flags: np.ndarray, context: int, budget: int, n_sink: int, n_recent: int) -> Plan:
+    mode = schedule(flags, budget)
+    B, S = mode.shape
+    seq_len = np.zeros((S, B), np.int32)
+    rstart = np.zeros((S, B), np.int32)
+    max_recent = 1
+    cur = np.full(B, n_sink, np.int64)
+    for s in range(S):
+        N = context + s
+        seq_len[s, :] = N
+        for b in range(B):
+            if mode[b, s]:
+                # frozen left edge of the recent segment for the following fast steps
+                cur[b] = max(n_sink, N - n_recent)
+            else:
+                max_recent = max(max_recent, N - int(cur[b]))
+            rstart[s, b] = cur[b]
+    plan = Plan(mode, seq_len, rstart, max_recent=max_recent)
+    for s in range(S):
+        plan.slow_ids.append(np.nonzero(mode[:, s])[0].astype(np.int32))
+        plan.fast_ids.append(np.nonzero(mode[:, s] == 0)[0].astype(np.int32))
+    return plan
+
+
+class LayerBuffers:
+    """Device state of one attention layer."""
+
+    def __init__(self, eng: "Engine", k_cache, v_cache, block_table, q_all):
+        w, dev = eng.w, eng.device
+        B, Hq, Hkv, D = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.block_table = block_table.to(dev, torch.int32).contiguous()
+        self.q_all = q_all                       # [S, B, Hq, D] fp32
+        self.key_norm = torch.zeros(B, Hkv, eng.stride, dtype=torch.float32, device=dev)
+        self.logits = torch.zeros(B, Hq, eng.stride, dtype=torch.float32, device=dev)
+        self.lse = torch.zeros(B, Hq, dtype=torch.float32, device=dev)
+        self.sel_idx = torch.full((B, Hkv, w.top_k), -1, dtype=torch.int32, device=dev)
+        dt = k_cache.dtype
+        self.packed_k = torch.zeros(B, Hkv, eng.packed_cap, D, dtype=dt, device=dev)
+        self.packed_v = torch.zeros(B, Hkv, eng.packed_cap, D, dtype=dt, device=dev)
+        self.packed_pos = torch.full((B, Hkv, eng.packed_cap), -1, dtype=torch.int32, device=dev)
+        self.packed_len = torch.zeros(B, Hkv, dtype=torch.int32, device=dev)
+        self.out = torch.zeros(B, Hq, D, dtype=torch.float32, device=dev)
+        self.ev_attn = torch.cuda.Event()
+        self.ev_pack = torch.cuda.Event()
+        self.pack_pending = False
+
+
+class Engine:
+    def __init__(self, w, flags, device="cuda", two_streams: bool = True,
+                 dbg_scores: bool = False):
+        self.w = w
+        self.device = torch.device(device)
+        self.two_streams = two_streams
+        flags_np = np.asarray(flags.cpu() if torch.is_tensor(flags) else flags)
+        self.plan = make_plan(flags_np, w.context, w.refresh_budget, w.n_sink, w.n_recent)
+        self.shape = L.make_shape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                  w.pages_per_seq, w.dtype)
+        self.params = L.make_params(w.n_sink, w.n_recent, w.top_k, w.nms_radius, w.lam,
+                                    w.alpha_soft, w.alpha_cross)
+        self.packed_cap = L.sfi_packed_cap(self.params)
+        self.max_len = w.total_len
+        self.stride = (self.max_len + 63) // 64 * 64
+        self.max_recent = self.plan.max_recent
+        dev = self.device
+        S, B = w.steps, w.batch
+        self.seq_len_d = torch.from_numpy(self.plan.seq_len).to(dev)
+        self.rstart_d = torch.from_numpy(self.plan.recent_start).to(dev)
+        slow = np.zeros((S, B), np.int32)
+        fast = np.zeros((S, B), np.int32)
+        for s in range(S):
+            slow[s, :len(self.plan.slow_ids[s])] = self.plan.slow_ids[s]
+            fast[s, :len(self.plan.fast_ids[s])] = self.plan.fast_ids[s]
+        self.slow_ids_d = torch.from_numpy(slow).to(dev)
+        self.fast_ids_d = torch.from_numpy(fast).to(dev)
+        self.all_ids_d = torch.arange(B, dtype=torch.int32, device=dev)
+        # The split plan depends on the number of rows in a call, so size each workspace
+        # for the largest requirement over every row count a step can pass.
+        self.ws_slow = L.workspace(max(L.sfi_slow_attn_ws(self.shape, n, self.max_len)
+                                       for n in range(1, B + 1)), dev)
+        self.ws_fast = L.workspace(
+            max(L.sfi_fast_attn_ws(self.shape, n, self.packed_cap, self.max_recent)
+                for n in range(1, B + 1)), dev)
+        self.ws_sel = L.workspace(max(L.sfi_select_ws(self.shape, self.params, n, self.max_len)
+                                      for n in range(1, B + 1)), dev)
+        self.stream1 = torch.cuda.Stream(device=dev)
+        self.stream2 = torch.cuda.Stream(device=dev) if two_streams else self.stream1
+        self.layers: List[LayerBuffers] = []
+        self.dbg = dbg_scores
+        self.dbg_buf: Optional[torch.Tensor] = None
+        if dbg_scores:
+            self.dbg_buf = torch.zeros(B, w.num_kv_heads, self.stride, dtype=torch.float32,
+                                       device=dev)
+
+    def add_layer(self, k_cache, v_cache, block_table, q_all) -> LayerBuffers:
+        lb = LayerBuffers(self, k_cache, v_cache, block_table, q_all)
+        # cached key statistic for every stored position (prefill-time work)
+        full = torch.full((self.w.batch,), self.max_len, dtype=torch.int32, device=self.device)
+        with torch.cuda.stream(self.stream1):
+            L.sfi_key_norms(self.shape, lb.k_cache, lb.block_table, full, self.all_ids_d,
+                            self.w.batch, 0, self.max_len, lb.key_norm, self.stride,
+                            stream=self.stream1)
+        self.stream1.synchronize()
+        self.layers.append(lb)
+        return lb
+
+    # ------------------------------------------------------------------------ one step
+    def step(self, s: int, dense_only: bool = False) -> None:
+        """Issue decode step s of every layer (no host synchronisation).
+
+        dense_only runs the Full-KV baseline: dense attention for every sequence, no
+        Selector, no logits.
+        """
+        w, shp = self.w, self.shape
+        slow_ids = self.plan.slow_ids[s]
+        fast_ids = self.plan.fast_ids[s]
+        n_slow, n_fast = len(slow_ids), len(fast_ids)
+        seq_len = self.seq_len_d[s]
+        rstart = self.rstart_d[s]
+        s1, s2 = self.stream1, self.stream2
+        for lb in self.layers:
+            q = lb.q_all[s]
+            if dense_only:
+                L.sfi_slow_attn(shp, q, lb.k_cache, lb.v_cache, lb.block_table, seq_len,
+                                self.all_ids_d, w.batch, self.max_len, lb.out, None, 0, lb.lse,
+                                self.ws_slow, stream=s1)
+                continue
+            if lb.pack_pending:
+                s1.wait_event(lb.ev_pack)
+                lb.pack_pending = False
+            if n_fast:
+                L.sfi_fast_attn(shp, q, lb.packed_k, lb.packed_v, lb.packed_len,
+                                self.packed_cap, lb.k_cache, lb.v_cache, lb.block_table,
+                                rstart, seq_len, self.fast_ids_d[s], n_fast, self.max_recent,
+                                lb.out, None, self.ws_fast, stream=s1)
+            if n_slow:
+                ids = self.slow_ids_d[s]
+                L.sfi_slow_attn(shp, q, lb.k_cache, lb.v_cache, lb.block_table, seq_len, ids,
+                                n_slow, self.max_len, lb.out, lb.logits, self.stride, lb.lse,
+                                self.ws_slow, stream=s1)
+                if s2 is not s1:
+                    lb.ev_attn.record(s1)
+                    s2.wait_event(lb.ev_attn)
+                dbg = self.dbg_buf if self.dbg else None
+                L.sfi_select(shp, self.params, lb.logits, self.stride, lb.lse, lb.key_norm,
+                             self.stride, seq_len, ids, n_slow, self.max_len, lb.sel_idx, dbg,
+                             self.ws_sel, stream=s2)
+                L.sfi_pack(shp, self.params, lb.k_cache, lb.v_cache, lb.block_table,
+                           lb.sel_idx, ids, n_slow, lb.packed_k, lb.packed_v, lb.packed_pos,
+                           lb.packed_len, self.packed_cap, stream=s2)
+                if s2 is not s1:
+                    lb.ev_pack.record(s2)
+                    lb.pack_pending = True
+
+    def join(self) -> None:
+        """Make stream 1 wait for every outstanding Selector/pack."""
+        for lb in self.layers:
+            if lb.pack_pending:
+                self.stream1.wait_event(lb.ev_pack)
+                lb.pack_pending = False
+
+    def mode(self, s: int) -> np.ndarray:
+        return self.plan.mode[:, s]

@@ -1,0 +1,199 @@
+"""Host-side checks of the C ABI: the library loads, exports every function include/sfi.h
+declares, and rejects bad arguments with the documented codes before launching anything.
+No GPU is needed: every call here fails validation (or is a pure host query)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_kv_attention_decode_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sfi.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(sfi_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.load()
+    declared = _declared_functions()
+    assert len(declared) >= 11
+    assert sorted(L.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert L.sfi_abi_version() == 1
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert L.status_str(code) and L.status_str(code) != "unknown status"
+    assert L.status_str(42) == "unknown status"
+
+
+def _shape(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, max_pages_per_seq=64,
+                dtype="bf16")
+    base.update(kw)
+    return L.make_shape(**base)
+
+
+def _params(**kw):
+    base = dict(n_sink=4, n_recent=64, top_k=128, nms_radius=4, lam=0.3, alpha_soft=0.5,
+                alpha_cross=0.5)
+    base.update(kw)
+    return L.make_params(**base)
+
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address; never dereferenced
+MIS = (1 << 20) + 4     # misaligned
+
+
+def _slow(shape, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, ids=FAKE, n=1, maxlen=100, out=FAKE,
+             logits=FAKE, stride=128, lse=FAKE, ws=FAKE, wsb=1 << 40)
+    a.update(over)
+    return L.load().sfi_slow_attn(ctypes.byref(shape), a["q"], a["k"], a["v"], a["bt"], a["sl"],
+                                  a["ids"], a["n"], a["maxlen"], a["out"], a["logits"],
+                                  a["stride"], a["lse"], a["ws"], a["wsb"], None)
+
+
+def test_slow_attn_validation():
+    s = _shape()
+    assert _slow(s, q=None) == L.SFI_E_ARG
+    assert _slow(s, lse=None) == L.SFI_E_ARG
+    assert _slow(_shape(num_q_heads=7)) == L.SFI_E_ARG
+    assert _slow(_shape(num_kv_heads=0)) == L.SFI_E_ARG
+    assert _slow(_shape(head_dim=96)) == L.SFI_E_UNSUPPORTED
+    assert _slow(_shape(num_q_heads=64, num_kv_heads=2)) == L.SFI_E_UNSUPPORTED   # G = 32
+    assert _slow(_shape(dtype=7)) == L.SFI_E_UNSUPPORTED
+    s16 = _shape()
+    s16.page_size = 32
+    assert _slow(s16) == L.SFI_E_UNSUPPORTED
+    assert _slow(s, n=3) == L.SFI_E_ARG                    # more rows than the batch
+    assert _slow(s, n=-1) == L.SFI_E_ARG
+    assert _slow(s, maxlen=0) == L.SFI_E_ARG
+    assert _slow(s, maxlen=64 * 16 + 1) == L.SFI_E_CAPACITY
+    assert _slow(s, q=MIS) == L.SFI_E_ALIGN
+    assert _slow(s, k=MIS) == L.SFI_E_ALIGN
+    assert _slow(s, logits=MIS) == L.SFI_E_ALIGN
+    assert _slow(s, stride=130) == L.SFI_E_ALIGN
+    assert _slow(s, stride=96) == L.SFI_E_CAPACITY         # stride < max_seq_len
+    assert _slow(s, ws=None) == L.SFI_E_WORKSPACE
+    need = L.sfi_slow_attn_ws(s, 1, 100)
+    assert need > 0
+    assert _slow(s, wsb=need - 1) == L.SFI_E_WORKSPACE
+    assert _slow(s, ws=FAKE + 16) == L.SFI_E_WORKSPACE     # not 256-byte aligned
+    assert _slow(s, n=0, wsb=need) == L.SFI_OK             # no rows: nothing to launch
+
+
+def test_workspace_queries_reject_bad_arguments():
+    s, p = _shape(), _params()
+    assert L.sfi_slow_attn_ws(_shape(head_dim=80), 1, 10) == 0
+    assert L.sfi_slow_attn_ws(s, 1, 64 * 16 + 1) == 0
+    assert L.sfi_select_ws(s, _params(top_k=0), 1, 10) == 0
+    assert L.sfi_fast_attn_ws(s, 1, 17, 10) == 0
+    assert L.sfi_fast_attn_ws(s, 1, 144, 10) > 0
+    assert L.sfi_packed_cap(p) == 144
+    assert L.sfi_packed_cap(_params(n_sink=0, top_k=16)) == 16
+    assert L.sfi_packed_cap(_params(alpha_soft=1.5)) == 0
+
+
+def _select(shape, params, **over):
+    a = dict(logits=FAKE, lstride=128, lse=FAKE, norm=FAKE, nstride=128, sl=FAKE, ids=FAKE, n=1,
+             maxlen=100, sel=FAKE, dbg=None, ws=FAKE, wsb=1 << 40)
+    a.update(over)
+    return L.load().sfi_select(ctypes.byref(shape), ctypes.byref(params), a["logits"],
+                               a["lstride"], a["lse"], a["norm"], a["nstride"], a["sl"], a["ids"],
+                               a["n"], a["maxlen"], a["sel"], a["dbg"], a["ws"], a["wsb"], None)
+
+
+def test_select_validation():
+    s, p = _shape(), _params()
+    assert _select(s, p, logits=None) == L.SFI_E_ARG
+    assert _select(s, _params(top_k=0)) == L.SFI_E_ARG
+    assert _select(s, _params(nms_radius=-1)) == L.SFI_E_ARG
+    assert _select(s, _params(lam=1.5)) == L.SFI_E_ARG
+    assert _select(s, _params(lam=float("nan"))) == L.SFI_E_ARG
+    assert _select(s, _params(alpha_soft=-0.1)) == L.SFI_E_ARG
+    assert _select(s, _params(alpha_cross=2.0)) == L.SFI_E_ARG
+    assert _select(s, _params(n_sink=-1)) == L.SFI_E_ARG
+    assert _select(s, p, lstride=64) == L.SFI_E_CAPACITY
+    assert _select(s, p, nstride=130) == L.SFI_E_ALIGN
+    assert _select(s, _params(nms_radius=5000)) == L.SFI_E_UNSUPPORTED
+    assert _select(s, p, wsb=10) == L.SFI_E_WORKSPACE
+    assert _select(s, p, n=0) == L.SFI_OK
+
+
+def _pack(shape, params, **over):
+    a = dict(k=FAKE, v=FAKE, bt=FAKE, sel=FAKE, ids=FAKE, n=1, pk=FAKE, pv=FAKE, pp=FAKE,
+             pl=FAKE, cap=L.sfi_packed_cap(params))
+    a.update(over)
+    return L.load().sfi_pack(ctypes.byref(shape), ctypes.byref(params), a["k"], a["v"], a["bt"],
+                             a["sel"], a["ids"], a["n"], a["pk"], a["pv"], a["pp"], a["pl"],
+                             a["cap"], None)
+
+
+def test_pack_validation():
+    s, p = _shape(), _params()
+    assert _pack(s, p, sel=None) == L.SFI_E_ARG
+    assert _pack(s, p, cap=128) == L.SFI_E_CAPACITY
+    assert _pack(s, p, pk=MIS) == L.SFI_E_ALIGN
+    assert _pack(s, p, n=5) == L.SFI_E_ARG
+    assert _pack(s, p, n=0) == L.SFI_OK
+
+
+def _fast(shape, **over):
+    a = dict(q=FAKE, pk=FAKE, pv=FAKE, pl=FAKE, cap=144, k=FAKE, v=FAKE, bt=FAKE, rs=FAKE,
+             sl=FAKE, ids=FAKE, n=1, maxrec=100, out=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
+    a.update(over)
+    return L.load().sfi_fast_attn(ctypes.byref(shape), a["q"], a["pk"], a["pv"], a["pl"],
+                                  a["cap"], a["k"], a["v"], a["bt"], a["rs"], a["sl"], a["ids"],
+                                  a["n"], a["maxrec"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                  None)
+
+
+def test_fast_attn_validation():
+    s = _shape()
+    assert _fast(s, rs=None) == L.SFI_E_ARG
+    assert _fast(s, cap=100) == L.SFI_E_CAPACITY
+    assert _fast(s, cap=0) == L.SFI_E_CAPACITY
+    assert _fast(s, maxrec=-1) == L.SFI_E_ARG
+    assert _fast(s, maxrec=64 * 16 + 1) == L.SFI_E_CAPACITY
+    assert _fast(s, pv=MIS) == L.SFI_E_ALIGN
+    assert _fast(s, wsb=0) == L.SFI_E_WORKSPACE
+    assert _fast(s, n=0) == L.SFI_OK
+
+
+def test_key_norms_validation():
+    s = _shape()
+    lib = L.load()
+
+    def call(**over):
+        a = dict(k=FAKE, bt=FAKE, sl=FAKE, ids=FAKE, n=1, pb=0, pe=100, out=FAKE, stride=128)
+        a.update(over)
+        return lib.sfi_key_norms(ctypes.byref(s), a["k"], a["bt"], a["sl"], a["ids"], a["n"],
+                                 a["pb"], a["pe"], a["out"], a["stride"], None)
+
+    assert call(out=None) == L.SFI_E_ARG
+    assert call(pb=10, pe=5) == L.SFI_E_ARG
+    assert call(pe=64 * 16 + 1, stride=2048) == L.SFI_E_CAPACITY
+    assert call(stride=64) == L.SFI_E_CAPACITY
+    assert call(k=MIS) == L.SFI_E_ALIGN
+    assert call(pb=7, pe=7) == L.SFI_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.reload(L)
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError, match="missing"):
+            mod.load(str(tmp_path / "nope.so"))
+    finally:
+        importlib.reload(L)

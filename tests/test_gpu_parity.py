@@ -1,0 +1,365 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on one MI355X.
+
+Inputs come from the seeded generator on the GPU; the oracle reads host fp64 copies of
+the very same stored values.  Comparison rules are in sfi_testlib.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sfi_oracle as O
+from workload import get
+from workload.gen import make_layer
+from sfi_testlib import (check_lse, check_logits, check_out, explain_selection_diff,
+                         host64, oracle_layer_arrays)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from sparse_kv_attention_decode_amd import lib as L
+    from sparse_kv_attention_decode_amd.engine import Engine
+
+
+def _setup(w, dbg=False, two_streams=True, layer=0):
+    d = make_layer(w, layer, device="cuda")
+    eng = Engine(w, d["flags"], two_streams=two_streams, dbg_scores=dbg)
+    lb = eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
+    return d, eng, lb
+
+
+def _slow(eng, lb, q, N, ids=None):
+    B = eng.w.batch
+    seq_len = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    ids = eng.all_ids_d if ids is None else ids
+    L.sfi_slow_attn(eng.shape, q, lb.k_cache, lb.v_cache, lb.block_table, seq_len, ids,
+                    ids.numel(), eng.max_len, lb.out, lb.logits, eng.stride, lb.lse,
+                    eng.ws_slow)
+    return seq_len
+
+
+SMALL = ["tiny_fp32_1k", "qwen3_0p6b_8k"]
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    """Bit pattern of a bf16 / fp32 tensor, for byte-exact comparisons."""
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_key_norms(name):
+    w = get(name)
+    d, eng, lb = _setup(w)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        ref = O.key_norms(host64(d["K"][b]))
+        got = host64(lb.key_norm[b, :, :w.total_len])
+        np.testing.assert_allclose(got, ref, rtol=1e-6)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_slow_attention(name):
+    w = get(name)
+    d, eng, lb = _setup(w)
+    for s in (0, 1, 7, w.steps - 1):
+        N = w.seq_len(s)
+        _slow(eng, lb, d["q"][s], N)
+        torch.cuda.synchronize()
+        for b in range(w.batch):
+            q, K, V = oracle_layer_arrays(d, b)
+            o, z, lse, _ = O.attention(q[s], K[:, :N], V[:, :N])
+            check_out(host64(lb.out[b]), o)
+            check_lse(host64(lb.lse[b]), lse)
+            check_logits(host64(lb.logits[b, :, :N]), z, q[s], K[:, :N], w.head_dim)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_full_kv_mode_without_logits(name):
+    """logits == NULL: same output, nothing written to the logits buffer."""
+    w = get(name)
+    d, eng, lb = _setup(w)
+    N = w.seq_len(3)
+    lb.logits.fill_(7.0)
+    seq_len = torch.full((w.batch,), N, dtype=torch.int32, device="cuda")
+    L.sfi_slow_attn(eng.shape, d["q"][3], lb.k_cache, lb.v_cache, lb.block_table, seq_len,
+                    eng.all_ids_d, w.batch, eng.max_len, lb.out, None, 0, lb.lse, eng.ws_slow)
+    torch.cuda.synchronize()
+    assert bool((lb.logits == 7.0).all())
+    q, K, V = oracle_layer_arrays(d, 0)
+    o, _, lse, _ = O.attention(q[3], K[:, :N], V[:, :N])
+    check_out(host64(lb.out[0]), o)
+    check_lse(host64(lb.lse[0]), lse)
+
+
+def _select_and_check(w, d, eng, lb, s):
+    """Slow step s on the device + Selector; checks exact Top-K on the device scores and
+    the end-to-end near-tie rule against the oracle's own selection."""
+    N = w.seq_len(s)
+    seq_len = _slow(eng, lb, d["q"][s], N)
+    L.sfi_select(eng.shape, eng.params, lb.logits, eng.stride, lb.lse, lb.key_norm, eng.stride,
+                 seq_len, eng.all_ids_d, w.batch, eng.max_len, lb.sel_idx, eng.dbg_buf,
+                 eng.ws_sel)
+    torch.cuda.synchronize()
+    stats = []
+    for b in range(w.batch):
+        sel_gpu = lb.sel_idx[b].cpu().numpy()
+        s_gpu = host64(eng.dbg_buf[b, :, :N])
+        # exact Top-K on the device's own fused scores
+        ref_sel = O.select_from_scores(s_gpu, N, w.n_sink, w.n_recent, w.top_k, w.nms_radius,
+                                       w.alpha_soft, w.alpha_cross)
+        np.testing.assert_array_equal(sel_gpu, ref_sel)
+        # fused scores against the oracle pipeline
+        q, K, V = oracle_layer_arrays(d, b)
+        _, _, _, p = O.attention(q[s], K[:, :N], V[:, :N])
+        sel = O.select(p, O.key_norms(K[:, :N]), N, w.num_kv_heads, w.n_sink, w.n_recent,
+                       w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam)
+        np.testing.assert_allclose(s_gpu, sel.s, rtol=1e-3, atol=1e-12)
+        stats.append(explain_selection_diff(sel_gpu, sel, N))
+    return stats
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_select(name):
+    w = get(name)
+    d, eng, lb = _setup(w, dbg=True)
+    for s in (0, 9):
+        stats = _select_and_check(w, d, eng, lb, s)
+        print(name, "step", s, "(diff, kth-ties, decision-ties) per row:", stats)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_pack_bit_exact(name):
+    w = get(name)
+    d, eng, lb = _setup(w, dbg=True)
+    _select_and_check(w, d, eng, lb, 0)
+    L.sfi_pack(eng.shape, eng.params, lb.k_cache, lb.v_cache, lb.block_table, lb.sel_idx,
+               eng.all_ids_d, w.batch, lb.packed_k, lb.packed_v, lb.packed_pos, lb.packed_len,
+               eng.packed_cap)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        sel = lb.sel_idx[b].cpu().numpy()
+        pk = lb.packed_k[b].cpu()
+        pv = lb.packed_v[b].cpu()
+        ppos = lb.packed_pos[b].cpu().numpy()
+        plen = lb.packed_len[b].cpu().numpy()
+        Kb, Vb = d["K"][b].cpu(), d["V"][b].cpu()
+        for g in range(w.num_kv_heads):
+            pos = O.packed_positions(sel[g], w.n_sink)
+            n = len(pos)
+            assert plen[g] == n
+            np.testing.assert_array_equal(ppos[g, :n], pos)
+            assert (ppos[g, n:] == -1).all()
+            assert (np.diff(pos[w.n_sink:]) > 0).all()
+            idx = torch.from_numpy(pos)
+            assert torch.equal(_bits(pk[g, :n]), _bits(Kb[g, idx]))
+            assert torch.equal(_bits(pv[g, :n]), _bits(Vb[g, idx]))
+            assert bool((_bits(pk[g, n:]) == 0).all()) and bool((_bits(pv[g, n:]) == 0).all())
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_trajectory_lockstep(name):
+    """Every step of the seeded trajectory through the two-stream engine.  Slow steps:
+    dense output and the selection (near-tie rule); the oracle then continues with the
+    device's selection (teacher forcing) so the two cannot drift.  Fast steps: the
+    two-segment output against the oracle's fast step on the same memory."""
+    w = get(name)
+    d, eng, lb = _setup(w)
+    B = w.batch
+    host = [oracle_layer_arrays(d, b) for b in range(B)]
+    norms = [O.key_norms(K) for _, K, _ in host]
+    packed = [None] * B
+    rstart = [0] * B
+    worst = 0.0
+    n_slow = n_fast = 0
+    for s in range(w.steps):
+        eng.step(s)
+        torch.cuda.synchronize()
+        N = w.seq_len(s)
+        out = host64(lb.out)
+        mode = eng.mode(s)
+        for b in range(B):
+            q, K, V = host[b]
+            if mode[b]:
+                n_slow += 1
+                o, z, lse, p = O.attention(q[s], K[:, :N], V[:, :N])
+                worst = max(worst, check_out(out[b], o, f"slow s={s} b={b}"))
+                sel = O.select(p, norms[b][:, :N], N, w.num_kv_heads, w.n_sink, w.n_recent,
+                               w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam)
+                sel_gpu = lb.sel_idx[b].cpu().numpy()
+                explain_selection_diff(sel_gpu, sel, N)
+                packed[b] = [O.packed_positions(sel_gpu[g], w.n_sink)
+                             for g in range(w.num_kv_heads)]
+                rstart[b] = O.recent_start_at(N, w.n_sink, w.n_recent)
+            else:
+                n_fast += 1
+                o, lse = O.fast_attention(q[s], K, V, packed[b], rstart[b], N)
+                worst = max(worst, check_out(out[b], o, f"fast s={s} b={b}"))
+    print(f"{name}: {n_slow} slow / {n_fast} fast steps, worst row rel err {worst:.2e}")
+
+
+def test_two_streams_bit_identical_to_one_stream():
+    """Race check of the overlap: the two-stream schedule must give bit-identical results
+    to the same work serialised on one stream."""
+    w = get("qwen3_0p6b_8k").replace(steps=64)
+    outs = []
+    for two in (True, False):
+        d, eng, lb = _setup(w, two_streams=two)
+        res = []
+        for s in range(w.steps):
+            eng.step(s)
+            eng.join()
+            torch.cuda.synchronize()
+            res.append(lb.out.clone())
+            if eng.mode(s)[0]:
+                res.append(lb.sel_idx.clone())
+        outs.append(res)
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_fast_equals_dense_when_k_covers_candidates():
+    """spec invariant on the device: with K >= |C| every fast step equals the dense
+    step (same positions, so equal up to fp32 rounding)."""
+    w = get("qwen3_0p6b_8k").replace(steps=40, top_k=9000, context=2048)
+    d, eng, lb = _setup(w)
+    for s in range(w.steps):
+        eng.step(s)
+        torch.cuda.synchronize()
+        fast_out = lb.out.clone()
+        _slow(eng, lb, d["q"][s], w.seq_len(s))
+        torch.cuda.synchronize()
+        err = (fast_out - lb.out).abs().amax(dim=-1) / lb.out.abs().amax(dim=-1)
+        assert float(err.max()) <= 2e-3, (s, float(err.max()))
+
+
+# ------------------------------------------------------------------------- edge cases
+EDGE = {
+    "empty_candidates": dict(context=40, n_recent=64, steps=6),            # N - W <= n_sink
+    "k_exceeds_candidates": dict(context=300, top_k=1000, steps=6),        # -1 padding
+    "no_sink": dict(n_sink=0, steps=6),
+    "no_recent_window": dict(n_recent=0, steps=6),
+    "ragged_tail": dict(context=1000 + 13, steps=5),                       # partial pages
+    "single_kv_head": dict(num_q_heads=8, num_kv_heads=1, steps=5),
+    "group_16": dict(num_q_heads=32, num_kv_heads=2, steps=5),
+    "head_dim_64_bf16": dict(head_dim=64, steps=5),
+    "f32_head_dim_128": dict(dtype="f32", head_dim=128, steps=5),
+    "alpha_one": dict(alpha_soft=1.0, alpha_cross=1.0, steps=5),
+    "alpha_zero": dict(alpha_soft=0.0, alpha_cross=0.0, steps=5),
+    "budget_zero": dict(refresh_budget=0, steps=5),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_edge_cases(case):
+    base = get("qwen3_0p6b_8k").replace(context=1024, top_k=128, n_recent=64, steps=8,
+                                        name="edge_" + case)
+    w = base.replace(**EDGE[case])
+    d, eng, lb = _setup(w, dbg=True)
+    _select_and_check(w, d, eng, lb, 0)
+    # run the trajectory through the engine and compare every step
+    d, eng, lb = _setup(w)
+    q, K, V = oracle_layer_arrays(d, 0)
+    norms = O.key_norms(K)
+    packed, rstart = None, 0
+    for s in range(w.steps):
+        eng.step(s)
+        torch.cuda.synchronize()
+        N = w.seq_len(s)
+        if eng.mode(s)[0]:
+            o, z, lse, p = O.attention(q[s], K[:, :N], V[:, :N])
+            sel = O.select(p, norms[:, :N], N, w.num_kv_heads, w.n_sink, w.n_recent, w.top_k,
+                           w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam)
+            sel_gpu = lb.sel_idx[0].cpu().numpy()
+            explain_selection_diff(sel_gpu, sel, N)
+            packed = [O.packed_positions(sel_gpu[g], w.n_sink) for g in range(w.num_kv_heads)]
+            rstart = O.recent_start_at(N, w.n_sink, w.n_recent)
+        else:
+            o, _ = O.fast_attention(q[s], K, V, packed, rstart, N)
+        check_out(host64(lb.out[0]), o, f"{case} s={s}")
+
+
+def test_ragged_batch_lengths():
+    """Rows of one call with different KV lengths (partial last pages, one row much
+    shorter than the call's max_seq_len)."""
+    w = get("qwen3_0p6b_8k").replace(batch=3, context=2000, steps=4, name="ragged_batch")
+    d, eng, lb = _setup(w, dbg=True)
+    lens = [2003, 517, 1290]
+    seq_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ids = torch.tensor([2, 0, 1], dtype=torch.int32, device="cuda")
+    q = d["q"][0]
+    L.sfi_slow_attn(eng.shape, q, lb.k_cache, lb.v_cache, lb.block_table, seq_len, ids, 3,
+                    eng.max_len, lb.out, lb.logits, eng.stride, lb.lse, eng.ws_slow)
+    L.sfi_select(eng.shape, eng.params, lb.logits, eng.stride, lb.lse, lb.key_norm, eng.stride,
+                 seq_len, ids, 3, eng.max_len, lb.sel_idx, eng.dbg_buf, eng.ws_sel)
+    torch.cuda.synchronize()
+    for b in range(3):
+        N = lens[b]
+        qh, K, V = oracle_layer_arrays(d, b)
+        o, z, lse, p = O.attention(qh[0], K[:, :N], V[:, :N])
+        check_out(host64(lb.out[b]), o, f"row {b}")
+        check_lse(host64(lb.lse[b]), lse)
+        s_gpu = host64(eng.dbg_buf[b, :, :N])
+        ref_sel = O.select_from_scores(s_gpu, N, w.n_sink, w.n_recent, w.top_k, w.nms_radius,
+                                       w.alpha_soft, w.alpha_cross)
+        np.testing.assert_array_equal(lb.sel_idx[b].cpu().numpy(), ref_sel)
+
+
+# ------------------------------------------------------------ full-size sampled checks
+FULL = ["qwen3_4b_32k_b4", "qwen3_4b_128k_36l", "g16_64k_b8"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    """At the full sizes and in the engine's launch configuration: step 0 (slow) of
+    layer 0 for the first and last row -- dense output, lse, exact Top-K on the device
+    scores, the near-tie rule end to end and the bit-exact pack -- then the first fast
+    step against the oracle's fast step on the device's memory."""
+    w = get(name)
+    d, eng, lb = _setup(w, dbg=True)
+    eng.step(0)
+    eng.join()
+    torch.cuda.synchronize()
+    rows = sorted({0, w.batch - 1})
+    N = w.seq_len(0)
+    # one extra Selector call with the debug scores on (same inputs, same kernels)
+    seq_len = torch.full((w.batch,), N, dtype=torch.int32, device="cuda")
+    sel_before = lb.sel_idx.clone()
+    L.sfi_select(eng.shape, eng.params, lb.logits, eng.stride, lb.lse, lb.key_norm, eng.stride,
+                 seq_len, eng.all_ids_d, w.batch, eng.max_len, lb.sel_idx, eng.dbg_buf,
+                 eng.ws_sel)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_before, lb.sel_idx)
+    out0 = host64(lb.out)
+    for b in rows:
+        q, K, V = oracle_layer_arrays(d, b)
+        o, z, lse, p = O.attention(q[0], K[:, :N], V[:, :N])
+        check_out(out0[b], o, f"{name} slow b={b}")
+        check_lse(host64(lb.lse[b]), lse)
+        s_gpu = host64(eng.dbg_buf[b, :, :N])
+        sel_gpu = lb.sel_idx[b].cpu().numpy()
+        np.testing.assert_array_equal(
+            sel_gpu, O.select_from_scores(s_gpu, N, w.n_sink, w.n_recent, w.top_k,
+                                          w.nms_radius, w.alpha_soft, w.alpha_cross))
+        sel = O.select(p, O.key_norms(K[:, :N]), N, w.num_kv_heads, w.n_sink, w.n_recent,
+                       w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam)
+        print(name, "row", b, "selection diff (n, kth, decision):",
+              explain_selection_diff(sel_gpu, sel, N))
+        pos = [O.packed_positions(sel_gpu[g], w.n_sink) for g in range(w.num_kv_heads)]
+        for g in range(w.num_kv_heads):
+            n = len(pos[g])
+            assert int(lb.packed_len[b, g]) == n
+            idx = torch.from_numpy(pos[g]).cuda()
+            assert torch.equal(_bits(lb.packed_k[b, g, :n]), _bits(d["K"][b, g, idx]))
+            assert torch.equal(_bits(lb.packed_v[b, g, :n]), _bits(d["V"][b, g, idx]))
+    # first fast step of those rows (if the schedule makes it fast)
+    eng.step(1)
+    torch.cuda.synchronize()
+    out1 = host64(lb.out)
+    for b in rows:
+        if eng.mode(1)[b]:
+            continue
+        q, K, V = oracle_layer_arrays(d, b)
+        sel_gpu = lb.sel_idx[b].cpu().numpy()
+        pos = [O.packed_positions(sel_gpu[g], w.n_sink) for g in range(w.num_kv_heads)]
+        o, _ = O.fast_attention(q[1], K, V, pos, O.recent_start_at(N, w.n_sink, w.n_recent),
+                                w.seq_len(1))
+        check_out(out1[b], o, f"{name} fast b={b}")
