@@ -40,9 +40,22 @@ def check_out(o_gpu: np.ndarray, o_ref: np.ndarray, what: str = "o"):
     return float(err.max())
 
 
-def check_lse(l_gpu, l_ref, what="lse"):
+def check_lse(l_gpu, l_ref, p=None, q=None, K=None, what="lse"):
+    """|dlse| <= max(LSE_TOL, Z_TOL * sum_j p_j |q||k_j| / sqrt(D)).
+
+    lse is a smooth maximum of the logits (d lse / d z_j = p_j), so its error is at most the
+    p-weighted logit error; with the logit bound of check_logits that is the second term.
+    p [Hq, N], q [Hq, D], K [Hkv, N, D] of the oracle give the bound per head."""
     d = np.abs(np.asarray(l_gpu, np.float64) - np.asarray(l_ref, np.float64))
-    assert d.max() <= LSE_TOL, f"{what}: max |dlse| {d.max():.3e}"
+    tol = np.full(d.shape, LSE_TOL)
+    if p is not None:
+        Hq, D = q.shape
+        G = Hq // K.shape[0]
+        kn = np.linalg.norm(K, axis=2)
+        qn = np.linalg.norm(q, axis=1)
+        for h in range(Hq):
+            tol[h] = max(LSE_TOL, Z_TOL * qn[h] * float(p[h] @ kn[h // G]) / np.sqrt(D))
+    assert (d <= tol).all(), f"{what}: |dlse| {d.max():.3e} vs tol {tol[d.argmax()]:.3e}"
     return float(d.max())
 
 

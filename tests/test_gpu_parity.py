@@ -66,9 +66,9 @@ def test_slow_attention(name):
         torch.cuda.synchronize()
         for b in range(w.batch):
             q, K, V = oracle_layer_arrays(d, b)
-            o, z, lse, _ = O.attention(q[s], K[:, :N], V[:, :N])
+            o, z, lse, p = O.attention(q[s], K[:, :N], V[:, :N])
             check_out(host64(lb.out[b]), o)
-            check_lse(host64(lb.lse[b]), lse)
+            check_lse(host64(lb.lse[b]), lse, p, q[s], K[:, :N])
             check_logits(host64(lb.logits[b, :, :N]), z, q[s], K[:, :N], w.head_dim)
 
 
@@ -85,9 +85,9 @@ def test_full_kv_mode_without_logits(name):
     torch.cuda.synchronize()
     assert bool((lb.logits == 7.0).all())
     q, K, V = oracle_layer_arrays(d, 0)
-    o, _, lse, _ = O.attention(q[3], K[:, :N], V[:, :N])
+    o, _, lse, p = O.attention(q[3], K[:, :N], V[:, :N])
     check_out(host64(lb.out[0]), o)
-    check_lse(host64(lb.lse[0]), lse)
+    check_lse(host64(lb.lse[0]), lse, p, q[3], K[:, :N])
 
 
 def _select_and_check(w, d, eng, lb, s):
@@ -296,7 +296,7 @@ def test_ragged_batch_lengths():
         qh, K, V = oracle_layer_arrays(d, b)
         o, z, lse, p = O.attention(qh[0], K[:, :N], V[:, :N])
         check_out(host64(lb.out[b]), o, f"row {b}")
-        check_lse(host64(lb.lse[b]), lse)
+        check_lse(host64(lb.lse[b]), lse, p, qh[0], K[:, :N])
         s_gpu = host64(eng.dbg_buf[b, :, :N])
         ref_sel = O.select_from_scores(s_gpu, N, w.n_sink, w.n_recent, w.top_k, w.nms_radius,
                                        w.alpha_soft, w.alpha_cross)
@@ -333,7 +333,7 @@ def test_full_size_sampled(name):
         q, K, V = oracle_layer_arrays(d, b)
         o, z, lse, p = O.attention(q[0], K[:, :N], V[:, :N])
         check_out(out0[b], o, f"{name} slow b={b}")
-        check_lse(host64(lb.lse[b]), lse)
+        check_lse(host64(lb.lse[b]), lse, p, q[0], K[:, :N])
         s_gpu = host64(eng.dbg_buf[b, :, :N])
         sel_gpu = lb.sel_idx[b].cpu().numpy()
         np.testing.assert_array_equal(
