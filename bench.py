@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Decode-throughput benchmark of the SFI hot path on one MI355X.
+
+One step is one decode step of every layer of the workload (the slow/fast schedule of the
+seeded trajectory decides, per sequence, between dense attention + Selector + pack and the
+two-segment fast attention).  Inputs (paged K/V of every layer, all queries, schedule
+tables) are resident in HBM before the timed region; the timed region issues exactly
+--steps steps on the engine's streams, bracketed by a device synchronisation.
+
+Printed: one JSON line.  `value` is layer decode steps per second (steps x layers /
+seconds).  `roofline` covers the dominant call, the fast-step attention: algorithmic bytes
+(packed rows + recent window of K and V, q in, o out) over the time between HIP events
+recorded around each call on the stream it runs on.  `cpu_baseline` is the fp64 oracle on
+a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def _parse():
+    from workload import BENCH_WORKLOAD
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed decode steps (default: the trajectory length)")
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default=BENCH_WORKLOAD)
+    ap.add_argument("--dense-steps", type=int, default=16,
+                    help="steps of the Full-KV dense baseline timed after the main run")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the oracle CPU baseline sample (0 disables it)")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="issue the Selector and pack on the attention stream")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a device copy of known size (for counter calibration)")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic per fast call measured with counters (optional)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": 3}))
+
+
+def cpu_baseline(w, d0, budget_s: float):
+    """Oracle (fp64 NumPy) on layer 0, first steps of the trajectory, on the host cores."""
+    import numpy as np
+    from oracle import sfi_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    b = 0
+    q = d0["q"][:, b].double().cpu().numpy()
+    K = d0["K"][b].double().cpu().numpy()
+    V = d0["V"][b].double().cpu().numpy()
+    flags = d0["flags"][b].cpu().numpy()
+    mode = O.schedule(flags[None, :], w.refresh_budget)[0]
+    norms = O.key_norms(K)
+    t0 = time.perf_counter()
+    done = 0
+    packed, rs = None, 0
+    for s in range(w.steps):
+        N = w.seq_len(s)
+        if mode[s]:
+            o, z, lse, p = O.attention(q[s], K[:, :N], V[:, :N])
+            sel = O.select(p, norms[:, :N], N, w.num_kv_heads, w.n_sink, w.n_recent, w.top_k,
+                           w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam)
+            packed = [O.packed_positions(sel.sel[g], w.n_sink) for g in range(w.num_kv_heads)]
+            rs = O.recent_start_at(N, w.n_sink, w.n_recent)
+        else:
+            O.fast_attention(q[s], K, V, packed, rs, N)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    n_slow = int(mode[:done].sum())
+    return {"value": done * w.batch / dt, "unit": "layer decode steps/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"layer 0, row 0, trajectory steps 0..{done - 1} ({n_slow} slow, "
+                      f"{done - n_slow} fast) in {dt:.1f} s, fp64 NumPy"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(sequences shard across GPUs with no exchange, see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    from workload import get
+    from workload.gen import make_layer
+    from sparse_kv_attention_decode_amd.engine import Engine
+
+    w = get(args.workload)
+    steps = args.steps if args.steps is not None else w.steps
+    t_setup = time.perf_counter()
+    d0 = None
+    eng = None
+    for layer in range(w.layers):
+        keep = layer == 0 and args.cpu_seconds > 0
+        d = make_layer(w, layer, device="cuda", keep_logical=keep)
+        if eng is None:
+            eng = Engine(w, d["flags"], two_streams=not args.one_stream)
+        eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
+        if keep:
+            d0 = {k: d[k] for k in ("q", "K", "V", "flags")}
+        del d
+        if layer % 6 == 5 or layer == w.layers - 1:
+            print(f"[bench] layer {layer + 1}/{w.layers} resident "
+                  f"({time.perf_counter() - t_setup:.1f} s)", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    S = w.steps
+
+    # warm-up: the first steps of the trajectory
+    for k in range(args.warmup):
+        eng.step(k % S)
+    eng.join()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` decode steps of every layer
+    timer = []
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        step_ev[k].record(eng.stream1)
+        eng.step(k % S, timer=timer)
+    eng.join()
+    step_ev[steps].record(eng.stream1)
+    torch.cuda.synchronize()
+    total_ms = step_ev[0].elapsed_time(step_ev[steps])
+
+    step_ms = [step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(steps)]
+    slow_step = [bool(eng.plan.mode[:, k % S].any()) for k in range(steps)]
+    fast_ms = [t for t, sl in zip(step_ms, slow_step) if not sl]
+    slow_ms = [t for t, sl in zip(step_ms, slow_step) if sl]
+
+    def agg(kind):
+        ts = [(e0.elapsed_time(e1), nb) for kd, e0, e1, nb in timer if kd == kind]
+        if not ts:
+            return None
+        tot_ms = sum(t for t, _ in ts)
+        tot_b = sum(b for _, b in ts)
+        return {"calls": len(ts), "avg_us": 1e3 * tot_ms / len(ts),
+                "gbs": tot_b / (tot_ms * 1e-3) / 1e9, "avg_bytes": tot_b / len(ts)}
+
+    fast = agg("fast")
+    slow = agg("slow")
+
+    # Full-KV dense baseline: dense attention of every layer, no Selector
+    dense = None
+    if args.dense_steps > 0:
+        dt = []
+        dense_timer = []
+        for k in range(args.dense_steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(eng.stream1)
+            eng.step(k % S, dense_only=True, timer=dense_timer)
+            e1.record(eng.stream1)
+            dt.append((e0, e1))
+        torch.cuda.synchronize()
+        dms = [a.elapsed_time(b) for a, b in dt]
+        dk = [(e0.elapsed_time(e1), nb) for _, e0, e1, nb in dense_timer]
+        dense = {"step_ms": sum(dms) / len(dms),
+                 "gbs": sum(b for _, b in dk) / (sum(t for t, _ in dk) * 1e-3) / 1e9}
+
+    ms_per_step = total_ms / steps
+    value = steps * w.layers / (total_ms * 1e-3)
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("workload") == w.name:
+                traffic = tj.get("bytes_per_call")
+        except Exception:
+            traffic = None
+    roof = None
+    if fast:
+        roof = {"bound": "hbm", "achieved": round(fast["gbs"], 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(fast["gbs"] / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "kernel": "sfi_fast_attn (fast-step two-segment attention)",
+                "avg_call_us": round(fast["avg_us"], 2),
+                "algorithmic_bytes_per_call": int(fast["avg_bytes"])}
+    cpu = None
+    if args.cpu_seconds > 0 and d0 is not None:
+        cpu = cpu_baseline(w, d0, args.cpu_seconds)
+
+    mean = lambda xs: (sum(xs) / len(xs)) if xs else None  # noqa: E731
+    line = {
+        "metric": "SFI decode steps/s per layer at 8K–128K ctx; achieved HBM GB/s vs peak",
+        "value": round(value, 2),
+        "unit": "layer decode steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded span-drift generator)",
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.batch,
+                   "context": w.context, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "top_k": w.top_k, "n_recent": w.n_recent,
+                   "streams": 1 if args.one_stream else 2},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": {
+            "stack_steps_per_s": round(steps / (total_ms * 1e-3), 3),
+            "fast_step_ms": mean(fast_ms), "slow_step_ms": mean(slow_ms),
+            "n_fast_steps": len(fast_ms), "n_slow_steps": len(slow_ms),
+            "fast_attn": fast, "slow_attn": slow,
+            "dense_step_ms": dense["step_ms"] if dense else None,
+            "dense_attn_gbs": dense["gbs"] if dense else None,
+            "fast_vs_dense": (dense["step_ms"] / mean(fast_ms)) if dense and fast_ms else None,
+            "mixed_vs_dense": (dense["step_ms"] / ms_per_step) if dense else None,
+            "setup_s": round(setup_s, 1),
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

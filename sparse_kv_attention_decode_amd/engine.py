@@ -47,18 +47,22 @@ class Plan:
     mode: np.ndarray          # [B, S]
     seq_len: np.ndarray       # [S, B]
     recent_start: np.ndarray  # [S, B] (valid at fast steps)
+    keff: np.ndarray = None   # [S, B] selected rows per KV head in the current memory
     slow_ids: List[np.ndarray] = field(default_factory=list)
     fast_ids: List[np.ndarray] = field(default_factory=list)
     max_recent: int = 0
 
 
-def make_plan(flags: np.ndarray, context: int, budget: int, n_sink: int, n_recent: int) -> Plan:
+def make_plan(flags: np.ndarray, context: int, budget: int, n_sink: int, n_recent: int,
+              top_k: int = 0) -> Plan:
     mode = schedule(flags, budget)
     B, S = mode.shape
     seq_len = np.zeros((S, B), np.int32)
     rstart = np.zeros((S, B), np.int32)
+    keff = np.zeros((S, B), np.int64)
     max_recent = 1
     cur = np.full(B, n_sink, np.int64)
+    cur_k = np.zeros(B, np.int64)
     for s in range(S):
         N = context + s
         seq_len[s, :] = N
@@ -66,10 +70,12 @@ def make_plan(flags: np.ndarray, context: int, budget: int, n_sink: int, n_recen
             if mode[b, s]:
                 # frozen left edge of the recent segment for the following fast steps
                 cur[b] = max(n_sink, N - n_recent)
+                cur_k[b] = min(top_k, max(0, N - n_recent - n_sink))
             else:
                 max_recent = max(max_recent, N - int(cur[b]))
             rstart[s, b] = cur[b]
-    plan = Plan(mode, seq_len, rstart, max_recent=max_recent)
+            keff[s, b] = cur_k[b]
+    plan = Plan(mode, seq_len, rstart, keff=keff, max_recent=max_recent)
     for s in range(S):
         plan.slow_ids.append(np.nonzero(mode[:, s])[0].astype(np.int32))
         plan.fast_ids.append(np.nonzero(mode[:, s] == 0)[0].astype(np.int32))
@@ -107,7 +113,8 @@ class Engine:
         self.device = torch.device(device)
         self.two_streams = two_streams
         flags_np = np.asarray(flags.cpu() if torch.is_tensor(flags) else flags)
-        self.plan = make_plan(flags_np, w.context, w.refresh_budget, w.n_sink, w.n_recent)
+        self.plan = make_plan(flags_np, w.context, w.refresh_budget, w.n_sink, w.n_recent,
+                              w.top_k)
         self.shape = L.make_shape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                   w.pages_per_seq, w.dtype)
         self.params = L.make_params(w.n_sink, w.n_recent, w.top_k, w.nms_radius, w.lam,
@@ -150,6 +157,10 @@ class Engine:
         lb = LayerBuffers(self, k_cache, v_cache, block_table, q_all)
         # cached key statistic for every stored position (prefill-time work)
         full = torch.full((self.w.batch,), self.max_len, dtype=torch.int32, device=self.device)
+        # The caches, block table, queries and the buffers above were written on the
+        # caller's stream; the engine streams are non-blocking, so order them after it.
+        # Stream 2 is ordered behind stream 1 through the per-layer attention events.
+        self.stream1.wait_stream(torch.cuda.current_stream(self.device))
         with torch.cuda.stream(self.stream1):
             L.sfi_key_norms(self.shape, lb.k_cache, lb.block_table, full, self.all_ids_d,
                             self.w.batch, 0, self.max_len, lb.key_norm, self.stride,
@@ -159,11 +170,32 @@ class Engine:
         return lb
 
     # ------------------------------------------------------------------------ one step
-    def step(self, s: int, dense_only: bool = False) -> None:
+    # ------------------------------------------------------------ algorithmic traffic
+    def fast_bytes(self, s: int) -> int:
+        """Bytes a fast attention call of step s must move: the packed rows and the recent
+        window of every fast row (K and V), plus q in and o out (fp32)."""
+        w, p = self.w, self.plan
+        e = w.elem_bytes
+        tot = 0
+        for b in p.fast_ids[s]:
+            rows = w.n_sink + int(p.keff[s, b]) + int(p.seq_len[s, b] - p.recent_start[s, b])
+            tot += w.num_kv_heads * rows * 2 * w.head_dim * e + 8 * w.num_q_heads * w.head_dim
+        return tot
+
+    def dense_bytes(self, s: int, ids) -> int:
+        """Bytes of dense attention over all N positions of the listed rows."""
+        w = self.w
+        e = w.elem_bytes
+        return sum(w.num_kv_heads * int(self.plan.seq_len[s, b]) * 2 * w.head_dim * e
+                   + 8 * w.num_q_heads * w.head_dim for b in ids)
+
+    # ------------------------------------------------------------------------ one step
+    def step(self, s: int, dense_only: bool = False, timer: Optional[list] = None) -> None:
         """Issue decode step s of every layer (no host synchronisation).
 
         dense_only runs the Full-KV baseline: dense attention for every sequence, no
-        Selector, no logits.
+        Selector, no logits.  When `timer` is a list, every attention call is bracketed by
+        two events on stream 1 and (kind, start, end, algorithmic bytes) is appended.
         """
         w, shp = self.w, self.shape
         slow_ids = self.plan.slow_ids[s]
@@ -172,26 +204,43 @@ class Engine:
         seq_len = self.seq_len_d[s]
         rstart = self.rstart_d[s]
         s1, s2 = self.stream1, self.stream2
+
+        def timed(kind, nbytes, fn):
+            if timer is None:
+                fn()
+                return
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s1)
+            fn()
+            e1.record(s1)
+            timer.append((kind, e0, e1, nbytes))
+
+        fb = self.fast_bytes(s) if (timer is not None and n_fast) else 0
+        db = self.dense_bytes(s, range(w.batch) if dense_only else slow_ids) \
+            if timer is not None else 0
         for lb in self.layers:
             q = lb.q_all[s]
             if dense_only:
-                L.sfi_slow_attn(shp, q, lb.k_cache, lb.v_cache, lb.block_table, seq_len,
-                                self.all_ids_d, w.batch, self.max_len, lb.out, None, 0, lb.lse,
-                                self.ws_slow, stream=s1)
+                timed("dense", db, lambda: L.sfi_slow_attn(
+                    shp, q, lb.k_cache, lb.v_cache, lb.block_table, seq_len, self.all_ids_d,
+                    w.batch, self.max_len, lb.out, None, 0, lb.lse, self.ws_slow, stream=s1))
                 continue
             if lb.pack_pending:
                 s1.wait_event(lb.ev_pack)
                 lb.pack_pending = False
             if n_fast:
-                L.sfi_fast_attn(shp, q, lb.packed_k, lb.packed_v, lb.packed_len,
-                                self.packed_cap, lb.k_cache, lb.v_cache, lb.block_table,
-                                rstart, seq_len, self.fast_ids_d[s], n_fast, self.max_recent,
-                                lb.out, None, self.ws_fast, stream=s1)
+                timed("fast", fb, lambda: L.sfi_fast_attn(
+                    shp, q, lb.packed_k, lb.packed_v, lb.packed_len, self.packed_cap,
+                    lb.k_cache, lb.v_cache, lb.block_table, rstart, seq_len,
+                    self.fast_ids_d[s], n_fast, self.max_recent, lb.out, None, self.ws_fast,
+                    stream=s1))
             if n_slow:
                 ids = self.slow_ids_d[s]
-                L.sfi_slow_attn(shp, q, lb.k_cache, lb.v_cache, lb.block_table, seq_len, ids,
-                                n_slow, self.max_len, lb.out, lb.logits, self.stride, lb.lse,
-                                self.ws_slow, stream=s1)
+                timed("slow", db, lambda: L.sfi_slow_attn(
+                    shp, q, lb.k_cache, lb.v_cache, lb.block_table, seq_len, ids, n_slow,
+                    self.max_len, lb.out, lb.logits, self.stride, lb.lse, self.ws_slow,
+                    stream=s1))
                 if s2 is not s1:
                     lb.ev_attn.record(s1)
                     s2.wait_event(lb.ev_attn)
