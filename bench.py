@@ -39,6 +39,9 @@ def _parse():
                     help="steps of the Full-KV dense baseline timed after the main run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle CPU baseline sample (0 disables it)")
+    ap.add_argument("--time-every", type=int, default=9,
+                    help="bracket the attention calls of every n-th layer with HIP events "
+                         "(0: none)")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue the Selector and pack on the attention stream")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -153,7 +156,10 @@ def main():
     torch.cuda.synchronize()
     for k in range(steps):
         step_ev[k].record(eng.stream1)
-        eng.step(k % S, timer=timer)
+        if args.time_every > 0:
+            eng.step(k % S, timer=timer, time_every=args.time_every)
+        else:
+            eng.step(k % S)
     eng.join()
     step_ev[steps].record(eng.stream1)
     torch.cuda.synchronize()

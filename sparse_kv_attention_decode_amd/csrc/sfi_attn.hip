@@ -6,8 +6,10 @@
 // fast steps attend to the compact contiguous buffer plus the recent tokens read straight
 // from the paged cache (zh "2.3 两段式", nl "Memory-Coalesced Kernel").
 //
-// One wavefront owns one split: a run of 16-row tiles of one (row b, KV head g).  All
-// G <= 16 query heads of g share the K/V reads.  bf16 caches go through MFMA:
+// One workgroup of four wavefronts owns one split: a run of 16-row tiles of one (row b,
+// KV head g); the waves take every fourth tile and merge their results in LDS, so each
+// split leaves one partial.  All G <= 16 query heads of g share the K/V reads.  bf16
+// caches go through MFMA:
 //   * logits   z[16 rows x 16 heads] = K_tile(16x D) * Q^T, as D/32 steps of
 //     v_mfma_f32_16x16x32_bf16.  q is split exactly into three bf16 terms (hi+mid+lo,
 //     truncation, so hi+mid+lo == q), and every bf16 x bf16 product is exact in fp32,
@@ -30,6 +32,8 @@
 namespace sfi {
 
 static_assert(kMaxG == kMaxGroup, "one MFMA tile covers every query head of a KV head");
+
+constexpr int kMaxTilesPerSplit = 512;  // page indices of one split staged in LDS
 
 namespace {
 
@@ -92,9 +96,18 @@ template <int D, bool WRITE_Z>
 __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
   constexpr int NC = D / 32;   // 32-dim steps of the logit product
   constexpr int NT = D / 16;   // 16-dim output tiles of the PV product
+  constexpr int NW = 4;        // wavefronts per workgroup; they share one split
+  __shared__ float sm_m[NW][kMaxG], sm_l[NW][kMaxG];
+  __shared__ float sm_o[NW - 1][kMaxG][D];
+  __shared__ int32_t sm_page[kMaxTilesPerSplit];
+  __shared__ u32x4_t sm_q[3][NC][kWave];  // query operand: hi, mid, lo terms
   const int lane = threadIdx.x & 63;
-  const int work = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (work >= p.n_seqs * p.Hkv * p.nsplit) return;
+  // Wave-uniform by construction; readfirstlane lets the compiler keep tile indices and
+  // page-table reads scalar (s_load, counted by lgkmcnt) instead of vector loads whose
+  // wait would also drain the in-flight K/V prefetch.
+  const int wave = uniform(threadIdx.x >> 6);
+  const int work = blockIdx.x;
+  if (work >= p.n_seqs * p.Hkv * p.nsplit) return;  // workgroup-uniform
   const int split = work % p.nsplit;
   const int ig = work / p.nsplit;
   const int g = ig % p.Hkv;
@@ -106,14 +119,57 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
   const size_t pidx = (size_t)ig * p.nsplit + split;
 
   const SplitRange sr = split_range(p, b, g, split, N);
-  if (sr.t0 >= sr.t1) {
-    write_empty_partial(p, pidx, D, lane);
+  if (sr.t0 >= sr.t1) {  // workgroup-uniform
+    if (wave == 0) write_empty_partial(p, pidx, D, lane);
     return;
   }
+  // Wave w takes tiles t0 + w, t0 + w + NW, ...
+  const int wt0 = sr.t0 + wave;
+  // Physical pages of the split, staged once in LDS: the per-tile lookups then wait on
+  // the LDS counter only and never on the in-flight K/V loads.
+  if (!sr.packed) {
+    const int32_t* btg = p.block_table + (size_t)b * p.max_pages + sr.t0;
+    for (int k = threadIdx.x; k < sr.t1 - sr.t0; k += 256) sm_page[k] = btg[k];
+  }
+  __syncthreads();
 
-  // Query operand: lane (qd, r) holds head r, dims 32c + 8qd .. +8, pre-scaled by 1/sqrt(D).
-  u32x4_t qh[NC], qm[NC], ql[NC];
-  {
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  if (sr.packed) {
+    const size_t off = ((size_t)b * p.Hkv + g) * (size_t)p.packed_cap * D;
+    kbase = reinterpret_cast<const uint16_t*>(p.packed_k) + off;
+    vbase = reinterpret_cast<const uint16_t*>(p.packed_v) + off;
+  } else {
+    kbase = reinterpret_cast<const uint16_t*>(p.k_cache);
+    vbase = reinterpret_cast<const uint16_t*>(p.v_cache);
+  }
+  const int lane_off = r * D + 8 * qd;
+  float* zrow = (WRITE_Z && r < p.G)
+                    ? p.logits + ((size_t)b * p.Hq + (size_t)g * p.G + r) * p.logits_stride
+                    : nullptr;
+
+  auto tile_offset = [&](int t) -> size_t {
+    if (sr.packed) return (size_t)t * kPage * D;
+    const int page = uniform(sm_page[t - sr.t0]);
+    return ((size_t)page * p.Hkv + g) * (size_t)(kPage * D);
+  };
+  auto load_tile = [&](int t, u32x4_t* kk, u32x4_t* vv) {
+    const size_t off = tile_offset(t) + lane_off;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kk[c] = *reinterpret_cast<const u32x4_t*>(kbase + off + 32 * c);
+      vv[c] = *reinterpret_cast<const u32x4_t*>(vbase + off + 32 * c);
+    }
+  };
+
+  // The wave's first tile is requested before the query is prepared, so its latency
+  // overlaps the prologue.
+  u32x4_t ka[NC], va[NC], kb[NC], vb[NC];
+  if (wt0 < sr.t1) load_tile(wt0, ka, va);
+
+  // Query operand, in LDS: lane (qd, r) of every wave reads head r, dims 32c + 8qd .. +8,
+  // pre-scaled by 1/sqrt(D) and split into three bf16 terms.  Wave 0 prepares it.
+  if (wave == 0) {
     const bool hv = r < p.G;
     const float* qrow = p.q + ((size_t)b * p.Hq + (size_t)g * p.G + (hv ? r : 0)) * D;
 #pragma unroll
@@ -131,12 +187,16 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
       float h8[8], m8[8], l8[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) split3(x[j] * p.scale, h8[j], m8[j], l8[j]);
+      u32x4_t qh, qm, ql;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        qh[c][w] = pack_hi16(h8[2 * w], h8[2 * w + 1]);
-        qm[c][w] = pack_hi16(m8[2 * w], m8[2 * w + 1]);
-        ql[c][w] = pack_hi16(l8[2 * w], l8[2 * w + 1]);
+        qh[w] = pack_hi16(h8[2 * w], h8[2 * w + 1]);
+        qm[w] = pack_hi16(m8[2 * w], m8[2 * w + 1]);
+        ql[w] = pack_hi16(l8[2 * w], l8[2 * w + 1]);
       }
+      sm_q[0][c][lane] = qh;
+      sm_q[1][c][lane] = qm;
+      sm_q[2][c][lane] = ql;
     }
   }
   // Selection matrices E_e[k][n] = (k == n + 16 e), lane (qd, r): k = 8qd + j, n = r.
@@ -156,49 +216,26 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) O[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  __syncthreads();
 
-  const uint16_t* kbase;
-  const uint16_t* vbase;
-  if (sr.packed) {
-    const size_t off = ((size_t)b * p.Hkv + g) * (size_t)p.packed_cap * D;
-    kbase = reinterpret_cast<const uint16_t*>(p.packed_k) + off;
-    vbase = reinterpret_cast<const uint16_t*>(p.packed_v) + off;
-  } else {
-    kbase = reinterpret_cast<const uint16_t*>(p.k_cache);
-    vbase = reinterpret_cast<const uint16_t*>(p.v_cache);
-  }
-  const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
-  const int lane_off = r * D + 8 * qd;
-  float* zrow = (WRITE_Z && r < p.G)
-                    ? p.logits + ((size_t)b * p.Hq + (size_t)g * p.G + r) * p.logits_stride
-                    : nullptr;
-
-  auto tile_offset = [&](int t) -> size_t {
-    if (sr.packed) return (size_t)t * kPage * D;
-    const int page = uniform(bt[t]);
-    return ((size_t)page * p.Hkv + g) * (size_t)(kPage * D);
-  };
-
-  u32x4_t kr[NC], vr[NC];
-  {
-    const size_t off = tile_offset(sr.t0) + lane_off;
+  // One tile step: request the wave's next tile t + NW into (kpf, vpf), then consume
+  // tile t from (kr, vr).  The two buffers swap roles by unrolling the loop twice, so no
+  // register copy ever waits on an outstanding load.
+  // The request is unconditional (the last tile is re-read at the end of the run) so the
+  // number of loads in flight, and with it the wait before tile t's products, does not
+  // depend on a branch.
+  auto step = [&](int t, u32x4_t* kr, u32x4_t* vr, u32x4_t* kpf, u32x4_t* vpf) {
+    load_tile(min(t + NW, sr.t1 - 1), kpf, vpf);
+    // Read the query operand from LDS every tile (an opaque lane index keeps the reads
+    // inside the loop, so the 48 registers they need are not held across it).
+    int ql_idx = lane;
+    asm volatile("" : "+v"(ql_idx));
+    u32x4_t qh[NC], qm[NC], ql[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      kr[c] = *reinterpret_cast<const u32x4_t*>(kbase + off + 32 * c);
-      vr[c] = *reinterpret_cast<const u32x4_t*>(vbase + off + 32 * c);
-    }
-  }
-
-  for (int t = sr.t0; t < sr.t1; ++t) {
-    // Prefetch the next tile while this one is consumed.
-    u32x4_t kn[NC], vn[NC];
-    if (t + 1 < sr.t1) {
-      const size_t off = tile_offset(t + 1) + lane_off;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        kn[c] = *reinterpret_cast<const u32x4_t*>(kbase + off + 32 * c);
-        vn[c] = *reinterpret_cast<const u32x4_t*>(vbase + off + 32 * c);
-      }
+      qh[c] = sm_q[0][c][ql_idx];
+      qm[c] = sm_q[1][c][ql_idx];
+      ql[c] = sm_q[2][c][ql_idx];
     }
     const int pos0 = t * kPage;
     const bool full = pos0 >= sr.row_lo && pos0 + kPage <= sr.row_hi;
@@ -278,27 +315,61 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
       O[tt] = mfma16(vt[tt], pl2, O[tt]);
       O[tt] = mfma16(vt[tt], ph2, O[tt]);
     }
-    if (t + 1 < sr.t1) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        kr[c] = kn[c];
-        vr[c] = vn[c];
-      }
-    }
+  };
+  for (int t = wt0; t < sr.t1; t += 2 * NW) {
+    step(t, ka, va, kb, vb);
+    if (t + NW >= sr.t1) break;
+    step(t + NW, kb, vb, ka, va);
   }
 
+  // Merge the four waves of the workgroup: common max, rescaled sums, one partial.
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (r < p.G) {
+  if (qd == 0) {
+    sm_m[wave][r] = m_run;
+    sm_l[wave][r] = l_tot;
+  }
+  __syncthreads();
+  float M = sm_m[0][r];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][r]);
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  const float sc = __expf(m_run - M_use);
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) O[tt][k] *= sc;
+  }
+  if (wave > 0 && r < p.G) {
+    float* so = &sm_o[wave - 1][r][4 * qd];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      *reinterpret_cast<float4*>(so + 16 * tt) = make_float4(O[tt][0], O[tt][1], O[tt][2], O[tt][3]);
+  }
+  __syncthreads();
+  if (wave == 0 && r < p.G) {
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += sm_l[w][r] * __expf(sm_m[w][r] - M_use);
     if (qd == 0) {
-      p.part_m[pidx * p.G + r] = m_run;
-      p.part_l[pidx * p.G + r] = l_tot;
+      p.part_m[pidx * p.G + r] = M;
+      p.part_l[pidx * p.G + r] = L;
     }
     float* o = p.part_o + (pidx * p.G + r) * D + 4 * qd;
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-      *reinterpret_cast<float4*>(o + 16 * tt) = make_float4(O[tt][0], O[tt][1], O[tt][2], O[tt][3]);
+    for (int tt = 0; tt < NT; ++tt) {
+      float4 a = make_float4(O[tt][0], O[tt][1], O[tt][2], O[tt][3]);
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) {
+        const float4 c = *reinterpret_cast<const float4*>(&sm_o[w][r][16 * tt + 4 * qd]);
+        a.x += c.x;
+        a.y += c.y;
+        a.z += c.z;
+        a.w += c.w;
+      }
+      *reinterpret_cast<float4*>(o + 16 * tt) = a;
+    }
   }
 }
 
@@ -425,6 +496,8 @@ __global__ __launch_bounds__(64) void k_attn_partial_f32(AttnParams p) {
 }
 
 // One block per (listed row, query head): log-sum-exp merge of the split partials.
+// Split weights exp(m_s - M) are staged in LDS; thread (grp, col) accumulates float4
+// column `col` of o over the splits s = grp (mod groups), then the groups are summed.
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm,
                                                     const float* __restrict__ pl,
                                                     const float* __restrict__ po, int nsplit,
@@ -432,7 +505,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm
                                                     const int32_t* __restrict__ seq_ids,
                                                     float* __restrict__ out,
                                                     float* __restrict__ lse) {
-  __shared__ float red[256];
+  constexpr int kChunk = 1024;
+  __shared__ float wts[kChunk];
+  __shared__ float red[8];
+  __shared__ float4 acc4[256];
   const int tid = threadIdx.x;
   const int i = blockIdx.x / Hq;
   const int h = blockIdx.x % Hq;
@@ -442,42 +518,56 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm
 
   float mx = -INFINITY;
   for (int s = tid; s < nsplit; s += 256) mx = fmaxf(mx, pm[(base + s) * G + hh]);
-  red[tid] = mx;
+  mx = wave_max_xor(mx, kWave);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
-  for (int s = tid; s < nsplit; s += 256) {
-    const float m = pm[(base + s) * G + hh];
-    L += pl[(base + s) * G + hh] * __expf(m - Mu);
-  }
-  red[tid] = L;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
+
+  const int cols = D / 4;
+  const int ngrp = 256 / cols;
+  const int col = tid % cols, grp = tid / cols;
+  const float4* po4 = reinterpret_cast<const float4*>(po);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+  for (int c0 = 0; c0 < nsplit; c0 += kChunk) {
+    const int n = min(kChunk, nsplit - c0);
+    for (int s = tid; s < n; s += 256) {
+      const size_t u = (base + c0 + s) * G + hh;
+      const float m = pm[u];
+      const float w = (m == -INFINITY) ? 0.f : __expf(m - Mu);
+      wts[s] = w;
+      L += w * pl[u];
+    }
+    __syncthreads();
+    for (int s = grp; s < n; s += ngrp) {
+      const float w = wts[s];
+      const float4 v = po4[((base + c0 + s) * G + hh) * cols + col];
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
+    }
     __syncthreads();
   }
-  const float Lt = red[0];
-  __syncthreads();
-  const int ngrp = 256 / D;
-  const int d = tid % D, grp = tid / D;
-  float acc = 0.f;
-  for (int s = grp; s < nsplit; s += ngrp) {
-    const float m = pm[(base + s) * G + hh];
-    const float w = __expf(m - Mu);
-    acc += w * po[((base + s) * G + hh) * D + d];
-  }
-  red[tid] = acc;
+  L = wave_sum_xor(L, kWave);
+  if ((tid & 63) == 0) red[4 + (tid >> 6)] = L;
+  acc4[tid] = acc;
   __syncthreads();
   if (grp == 0) {
-    for (int q = 1; q < ngrp; ++q) acc += red[q * D + d];
-    out[((size_t)b * Hq + h) * D + d] = Lt > 0.f ? acc / Lt : 0.f;
-    if (d == 0 && lse) lse[(size_t)b * Hq + h] = Lt > 0.f ? Mu + logf(Lt) : -INFINITY;
+    const float Lt = (red[4] + red[5]) + (red[6] + red[7]);
+    for (int q = 1; q < ngrp; ++q) {
+      const float4 v = acc4[q * cols + col];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    reinterpret_cast<float4*>(out + ((size_t)b * Hq + h) * D)[col] =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (col == 0 && lse) lse[(size_t)b * Hq + h] = Lt > 0.f ? Mu + logf(Lt) : -INFINITY;
   }
 }
 
@@ -486,11 +576,11 @@ hipError_t launch_partial(const AttnParams& p, int dtype, hipStream_t stream) {
   const int works = p.n_seqs * p.Hkv * p.nsplit;
   const bool wz = p.logits != nullptr;
   if (dtype == SFI_BF16) {
-    const int blocks = (works + 3) / 4;
+    // one workgroup (four wavefronts) per split
     if (wz)
-      hipLaunchKernelGGL((k_attn_partial_bf16<D, true>), dim3(blocks), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((k_attn_partial_bf16<D, true>), dim3(works), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((k_attn_partial_bf16<D, false>), dim3(blocks), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((k_attn_partial_bf16<D, false>), dim3(works), dim3(256), 0, stream, p);
   } else {
     if (wz)
       hipLaunchKernelGGL((k_attn_partial_f32<D, true>), dim3(works), dim3(64), 0, stream, p);
@@ -502,12 +592,21 @@ hipError_t launch_partial(const AttnParams& p, int dtype, hipStream_t stream) {
 
 }  // namespace
 
+// Tiles per split: aim at about kTargetSplits workgroups per call (two per CU on 256
+// CUs), with at least kMinTps tiles per workgroup.
+constexpr long kTargetSplits = 512;
+constexpr int kMinTps = 8;
+constexpr int kMaxTps = kMaxTilesPerSplit;
+
+static int tiles_per_split(long total) {
+  long tps = (total + kTargetSplits - 1) / kTargetSplits;
+  return (int)(tps < kMinTps ? kMinTps : (tps > kMaxTps ? kMaxTps : tps));
+}
+
 SplitPlan plan_slow(const sfi_shape& s, int n_seqs, int max_seq_len) {
   SplitPlan sp;
   const int ntile = (max_seq_len + kPage - 1) / kPage;
-  const long total = (long)n_seqs * s.num_kv_heads * ntile;
-  int tps = (int)((total + 2047) / 2048);
-  tps = tps < 4 ? 4 : (tps > 64 ? 64 : tps);
+  const int tps = tiles_per_split((long)n_seqs * s.num_kv_heads * ntile);
   sp.tps = tps;
   sp.nsplit = (ntile + tps - 1) / tps;
   sp.nsplit_a = 0;
@@ -518,9 +617,7 @@ SplitPlan plan_fast(const sfi_shape& s, int n_seqs, int packed_cap, int max_rece
   SplitPlan sp;
   const int ta = packed_cap / kPage;
   const int tb = (max_recent + kPage - 1) / kPage + 1;  // +1: the window need not start on a page
-  const long total = (long)n_seqs * s.num_kv_heads * (ta + tb);
-  int tps = (int)((total + 2047) / 2048);
-  tps = tps < 4 ? 4 : (tps > 64 ? 64 : tps);
+  const int tps = tiles_per_split((long)n_seqs * s.num_kv_heads * (ta + tb));
   sp.tps = tps;
   sp.nsplit_a = (ta + tps - 1) / tps;
   sp.nsplit = sp.nsplit_a + (tb + tps - 1) / tps;

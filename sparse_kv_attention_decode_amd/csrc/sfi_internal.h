@@ -63,8 +63,10 @@ struct SelectLayout {
   size_t zpart_off = 0, keys_off = 0, total = 0;
 };
 SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len);
-constexpr int kScoreTile = 256;
-size_t score_lds_bytes(int num_kv_heads, int num_q_heads, int nms_radius);
+// LDS of one scoring block: s for every KV head over `tile` positions plus a halo of
+// nms_radius on each side, the prior normalisers and the lse of every query head.
+size_t score_lds_bytes(int num_kv_heads, int num_q_heads, int nms_radius, int tile);
+constexpr size_t kScoreLdsLimit = 64 * 1024;
 
 hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm,
                          const float* logits, int64_t logits_stride, const float* lse,

@@ -17,13 +17,15 @@
 //
 // Kernels:
 //   k_sel_zsum   Z_g partial sums over chunks of 4096 positions.
-//   k_sel_score  one block per 256-position tile with an R-position halo, all KV heads at
-//                once (NMS couples neighbours, exclusivity couples heads): s into LDS,
-//                then the refined score s' as an order-preserving uint32 key (s' >= 0, so
-//                its IEEE bits already order like the value).
-//   k_sel_topk   one 1024-thread block per (b, g): radix select of the K-th largest key,
-//                8 bits per pass with an LDS histogram, then an ordered compaction that
-//                takes every key above the threshold and the lowest-position ties.
+//   k_sel_score  one block per 1024-position tile (256 when LDS is short) with an
+//                R-position halo, all KV heads at once (NMS couples neighbours,
+//                exclusivity couples heads): s into LDS, then the refined score s' as an
+//                order-preserving uint32 key (s' >= 0, so its IEEE bits already order
+//                like the value).
+//   k_sel_topk   one 1024-thread block per (b, g): radix select of the K-th largest key
+//                (an 11-bit histogram pass over global memory, then LDS-resident passes
+//                over the boundary bin), then one ordered pass that writes every key
+//                above the threshold and the lowest-position ties.
 #include "sfi_device.h"
 #include "sfi_internal.h"
 
@@ -34,7 +36,7 @@ namespace sfi {
 namespace {
 
 constexpr int kZChunk = 4096;
-constexpr int kTopkThreads = 1024;
+constexpr int kCandCapBytes = 48 * 1024;
 
 template <int BLOCK>
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -113,6 +115,12 @@ void launch_norms_t(const sfi_shape& s, const void* kc, const int32_t* bt, const
 }
 
 // ------------------------------------------------------------------------- prior norm Z
+// Z_g partial sums: one block per (row, KV head, chunk of 4096 positions); each thread
+// covers 16 positions with four float4 loads issued before any arithmetic.
+__device__ __forceinline__ float prior_weight(float norm, int N, int j) {
+  return (1.f / fmaxf(norm, 1e-6f)) * (1.f + logf(1.f + (float)(N - 1 - j)));
+}
+
 __global__ __launch_bounds__(256) void k_sel_zsum(const float* __restrict__ key_norm,
                                                   int64_t norm_stride,
                                                   const int32_t* __restrict__ seq_lens,
@@ -125,13 +133,24 @@ __global__ __launch_bounds__(256) void k_sel_zsum(const float* __restrict__ key_
   const int b = seq_ids[i];
   const int N = seq_lens[b];
   const float* a = key_norm + ((size_t)b * Hkv + g) * norm_stride;
+  const int j0 = chunk * kZChunk + 4 * (int)threadIdx.x;
+  float4 v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int j = j0 + 1024 * k;
+    v[k] = (j + 3 < N) ? *reinterpret_cast<const float4*>(a + j) : make_float4(1.f, 1.f, 1.f, 1.f);
+  }
   float acc = 0.f;
-  const int j0 = chunk * kZChunk;
-  const int j1 = min(j0 + kZChunk, N);
-  for (int j = j0 + (int)threadIdx.x; j < j1; j += 256) {
-    const float phi_key = 1.f / fmaxf(a[j], 1e-6f);
-    const float phi_pos = 1.f + logf(1.f + (float)(N - 1 - j));
-    acc += phi_key * phi_pos;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int j = j0 + 1024 * k;
+    if (j + 3 < N) {
+      acc += prior_weight(v[k].x, N, j) + prior_weight(v[k].y, N, j + 1) +
+             prior_weight(v[k].z, N, j + 2) + prior_weight(v[k].w, N, j + 3);
+    } else {
+      for (int q = 0; q < 4; ++q)
+        if (j + q < N) acc += prior_weight(a[j + q], N, j + q);
+    }
   }
   acc = block_sum<256>(acc, red);
   if (threadIdx.x == 0) zpart[blockIdx.x] = acc;
@@ -155,9 +174,42 @@ struct ScoreArgs {
   float lam, a_soft, a_cross;
 };
 
+// Fused score s(g, j) of one position for every KV head, written to LDS row idx.
+template <int GT>
+__device__ __forceinline__ void score_scalar(const ScoreArgs& a, const float* zs,
+                                             const float* lses, float* s_t, int W, int b,
+                                             int N, int j, int idx, bool dbg) {
+  const int G = GT > 0 ? GT : a.G;
+  const bool in = j >= 0 && j < N;
+  const float phi_pos = in ? 1.f + logf(1.f + (float)(N - 1 - j)) : 0.f;
+  for (int g = 0; g < a.Hkv; ++g) {
+    float s = -1.f;
+    if (in) {
+      float f = 0.f;
+      for (int hh = 0; hh < G; ++hh) {
+        const int h = g * G + hh;
+        f += expf(a.logits[((size_t)b * a.Hq + h) * a.logits_stride + j] - lses[h]);
+      }
+      f *= 1.f / (float)G;
+      const float nrm = a.key_norm[((size_t)b * a.Hkv + g) * a.norm_stride + j];
+      const float r = (1.f / fmaxf(nrm, 1e-6f)) * phi_pos / zs[g];
+      s = (1.f - a.lam) * f + a.lam * r;
+      if (dbg) a.dbg[((size_t)b * a.Hkv + g) * a.logits_stride + j] = s;
+    }
+    s_t[g * W + idx] = s;
+  }
+}
+
+// One block per (row, tile of TILE positions): every KV head of the tile plus an R-wide
+// halo on each side (soft-NMS reads neighbours, exclusivity reads all heads of a
+// position), then the refined keys of the tile's candidates.
+template <int GT, int PPT>
 __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
+  constexpr int TILE = 256 * PPT;
+  constexpr int GU = GT > 0 ? GT : kMaxG;  // unroll bound; runtime G when GT == 0
+  const int G = GT > 0 ? GT : a.G;
   extern __shared__ float lds[];
-  const int W = kScoreTile + 2 * a.R;
+  const int W = TILE + 2 * a.R;
   float* s_t = lds;                         // [Hkv][W]
   float* zs = lds + a.Hkv * W;              // [Hkv]
   float* lses = zs + a.Hkv;                 // [Hq]
@@ -166,7 +218,7 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
   const int tile = blockIdx.x % a.ntile;
   const int b = a.seq_ids[i];
   const int N = a.seq_lens[b];
-  const int t0 = tile * kScoreTile;
+  const int t0 = tile * TILE;
   if (t0 >= N) return;  // block-uniform
   const int lo = a.n_sink;
   const int hi = max(lo, N - a.n_recent);
@@ -180,59 +232,104 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
   for (int h = tid; h < a.Hq; h += 256) lses[h] = a.lse[(size_t)b * a.Hq + h];
   __syncthreads();
 
-  const float invG = 1.f / (float)a.G;
-  for (int idx = tid; idx < W; idx += 256) {
-    const int j = t0 - a.R + idx;
-    const bool in = j >= 0 && j < N;
-    const float phi_pos = in ? 1.f + logf(1.f + (float)(N - 1 - j)) : 0.f;
+  // Main positions: thread tid owns j = t0 + PPT*tid .. +PPT-1.
+  const int jm = t0 + PPT * tid;
+  if (PPT == 4 && jm + 3 < N) {
+    float phi[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) phi[q] = 1.f + logf(1.f + (float)(N - 1 - (jm + q)));
     for (int g = 0; g < a.Hkv; ++g) {
-      float s = -1.f;
-      if (in) {
-        float f = 0.f;
-        for (int hh = 0; hh < a.G; ++hh) {
-          const int h = g * a.G + hh;
-          f += expf(a.logits[((size_t)b * a.Hq + h) * a.logits_stride + j] - lses[h]);
-        }
-        f *= invG;
-        const float nrm = a.key_norm[((size_t)b * a.Hkv + g) * a.norm_stride + j];
-        const float r = (1.f / fmaxf(nrm, 1e-6f)) * phi_pos / zs[g];
-        s = (1.f - a.lam) * f + a.lam * r;
-        if (a.dbg && idx >= a.R && idx < a.R + kScoreTile)
-          a.dbg[((size_t)b * a.Hkv + g) * a.logits_stride + j] = s;
+      float4 zv[GU];
+#pragma unroll
+      for (int hh = 0; hh < GU; ++hh)
+        if (hh < G)
+          zv[hh] = *reinterpret_cast<const float4*>(
+              a.logits + ((size_t)b * a.Hq + g * G + hh) * a.logits_stride + jm);
+      const float4 nv = *reinterpret_cast<const float4*>(
+          a.key_norm + ((size_t)b * a.Hkv + g) * a.norm_stride + jm);
+      float f[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hh = 0; hh < GU; ++hh) {
+        if (hh >= G) break;
+        const float l = lses[g * G + hh];
+        f[0] += expf(zv[hh].x - l);
+        f[1] += expf(zv[hh].y - l);
+        f[2] += expf(zv[hh].z - l);
+        f[3] += expf(zv[hh].w - l);
       }
-      s_t[g * W + idx] = s;
+      const float nr[4] = {nv.x, nv.y, nv.z, nv.w};
+      float s[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float r = (1.f / fmaxf(nr[q], 1e-6f)) * phi[q] / zs[g];
+        s[q] = (1.f - a.lam) * (f[q] * (1.f / (float)G)) + a.lam * r;
+        s_t[g * W + a.R + PPT * tid + q] = s[q];
+      }
+      if (a.dbg)
+        *reinterpret_cast<float4*>(a.dbg + ((size_t)b * a.Hkv + g) * a.logits_stride + jm) =
+            make_float4(s[0], s[1], s[2], s[3]);
     }
+  } else {
+#pragma unroll
+    for (int q = 0; q < PPT; ++q)
+      score_scalar<GT>(a, zs, lses, s_t, W, b, N, jm + q, a.R + PPT * tid + q, a.dbg != nullptr);
+  }
+  // Halo: R positions left of the tile and R right of it.
+  for (int k = tid; k < 2 * a.R; k += 256) {
+    const int left = k < a.R;
+    const int j = left ? t0 - a.R + k : t0 + TILE + (k - a.R);
+    const int idx = left ? k : a.R + TILE + (k - a.R);
+    score_scalar<GT>(a, zs, lses, s_t, W, b, N, j, idx, false);
   }
   __syncthreads();
 
-  const int j = t0 + tid;
-  if (j < lo || j >= hi) return;
-  const int c = a.R + tid;
-  int own = 0;
-  float best = s_t[c];
-  for (int g = 1; g < a.Hkv; ++g) {
-    const float v = s_t[g * W + c];
-    if (v > best) {
-      best = v;
-      own = g;
-    }
-  }
   const float ws = 1.f - a.a_soft, wc = 1.f - a.a_cross;
-  const int dlo = max(lo, j - a.R) - j;    // <= 0
-  const int dhi = min(hi - 1, j + a.R) - j;  // >= 0
-  for (int g = 0; g < a.Hkv; ++g) {
-    const float* row = s_t + g * W + c;
-    const float sj = row[0];
-    bool dom = false;
-    for (int d = dlo; d <= dhi; ++d) dom |= (d != 0) && (row[d] > sj);
-    float sp = sj;
-    if (dom) sp *= ws;
-    if (a.Hkv > 1 && g != own) sp *= wc;
-    a.keys[((size_t)i * a.Hkv + g) * a.kstride + (j - lo)] = f2u(sp) & 0x7fffffffu;
+#pragma unroll
+  for (int q = 0; q < PPT; ++q) {
+    const int j = jm + q;
+    if (j < lo || j >= hi) continue;
+    const int c = a.R + PPT * tid + q;
+    int own = 0;
+    float best = s_t[c];
+    for (int g = 1; g < a.Hkv; ++g) {
+      const float v = s_t[g * W + c];
+      if (v > best) {
+        best = v;
+        own = g;
+      }
+    }
+    const int dlo = max(lo, j - a.R) - j;      // <= 0
+    const int dhi = min(hi - 1, j + a.R) - j;  // >= 0
+    for (int g = 0; g < a.Hkv; ++g) {
+      const float* row = s_t + g * W + c;
+      const float sj = row[0];
+      bool dom = false;
+      for (int d = dlo; d <= dhi; ++d) dom |= (d != 0) && (row[d] > sj);
+      float sp = sj;
+      if (dom) sp *= ws;
+      if (a.Hkv > 1 && g != own) sp *= wc;
+      a.keys[((size_t)i * a.Hkv + g) * a.kstride + (j - lo)] = f2u(sp) & 0x7fffffffu;
+    }
   }
 }
 
 // ------------------------------------------------------------------------------- top-K
+// Radix selection of the K_eff-th largest refined key per (row, KV head), one 1024-thread
+// block each:
+//   1. 11-bit histogram passes over the keys in global memory, each restricted to the
+//      digits fixed so far, until the bin holding the K_eff-th key has at most kCandCap
+//      keys (usually after one pass);
+//   2. that bin's keys and candidate indices are compacted into LDS;
+//   3. the remaining bits are resolved with LDS-resident histogram passes, giving the
+//      exact threshold T and the number of keys equal to T still to take; the last of
+//      those ties (lowest positions first) is found by the same selection on the
+//      complemented candidate index;
+//   4. one ordered pass writes every candidate above T and the ties up to that index,
+//      ascending, with a block-wide prefix sum per chunk.
+constexpr int kTopkThreads = 1024;
+constexpr int kHistBins = 2048;
+constexpr int kCandCap = kCandCapBytes / 8;  // key + index per candidate
+
 __device__ __forceinline__ void hist_add(uint32_t* hist, int bin, bool active) {
   // Aggregate lanes that share the first active lane's bin into one LDS atomic; the rest
   // add one by one.  Skewed key distributions put most lanes into a few bins.
@@ -277,6 +374,24 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uin
   return res;
 }
 
+// Bin of hist[0..2048) holding the krem-th largest counted element: thread t owns bins
+// 2047-2t and 2046-2t.  Writes (bin, count above the bin) to res[0..1].  All threads call.
+__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t krem, uint32_t* wsum,
+                                         uint32_t* res) {
+  const int t = threadIdx.x;
+  const uint32_t hh = hist[kHistBins - 1 - 2 * t], hl = hist[kHistBins - 2 - 2 * t];
+  uint32_t tot;
+  const uint32_t above = block_exscan(hh + hl, wsum, &tot);
+  if (above < krem && above + hh >= krem) {
+    res[0] = kHistBins - 1 - 2 * t;
+    res[1] = above;
+  } else if (above + hh < krem && above + hh + hl >= krem) {
+    res[0] = kHistBins - 2 - 2 * t;
+    res[1] = above + hh;
+  }
+  __syncthreads();
+}
+
 struct TopkArgs {
   const uint32_t* keys;
   int64_t kstride;
@@ -286,10 +401,26 @@ struct TopkArgs {
   int Hkv, K, n_sink, n_recent;
 };
 
+// Load keys[c .. c+8) (c a multiple of 8) into kv; entries past n read as 0 and are
+// marked invalid by the caller's bounds check.
+__device__ __forceinline__ void load8(const uint32_t* keys, int c, int n, uint32_t kv[8]) {
+  if (c + 8 <= n) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(keys + c);
+    const u32x4_t y = *reinterpret_cast<const u32x4_t*>(keys + c + 4);
+    kv[0] = x[0]; kv[1] = x[1]; kv[2] = x[2]; kv[3] = x[3];
+    kv[4] = y[0]; kv[5] = y[1]; kv[6] = y[2]; kv[7] = y[3];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) kv[q] = (c + q < n) ? keys[c + q] : 0u;
+  }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t ckey[kCandCap];
+  __shared__ uint32_t cidx[kCandCap];
   __shared__ uint32_t wsum[17];
-  __shared__ uint32_t bc[4];
+  __shared__ uint32_t res[4];
   const int tid = threadIdx.x;
   const int ig = blockIdx.x;
   const int g = ig % a.Hkv, i = ig / a.Hkv;
@@ -303,89 +434,156 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
   const uint32_t* keys = a.keys + (size_t)ig * a.kstride;
   for (int k = keff + tid; k < a.K; k += kTopkThreads) out[k] = -1;
   if (keff == 0) return;
+  if (keff == nC) {  // every candidate is taken
+    for (int k = tid; k < nC; k += kTopkThreads) out[k] = lo + k;
+    return;
+  }
+  constexpr int STEP = 8 * kTopkThreads;
 
-  uint32_t thr = 0, need_eq;
-  if (keff == nC) {
-    need_eq = 0xffffffffu;  // every candidate is taken: threshold 0 with unlimited ties
-  } else {
-    uint32_t prefix = 0, pmask = 0, krem = (uint32_t)keff;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      for (int k = tid; k < 256; k += kTopkThreads) hist[k] = 0;
-      __syncthreads();
-      for (int base = 0; base < nC; base += kTopkThreads) {
-        const int c = base + tid;
-        const uint32_t key = c < nC ? keys[c] : 0u;
-        const bool act = c < nC && (key & pmask) == prefix;
-        hist_add(hist, (key >> shift) & 255u, act);
+  // 1. global histogram passes
+  uint32_t prefix = 0, krem = (uint32_t)keff, cnt = 0;
+  int done = 0;  // resolved top bits
+  while (true) {
+    const int nb = min(11, 32 - done);
+    const int sh = 32 - done - nb;
+    for (int k = tid; k < kHistBins; k += kTopkThreads) hist[k] = 0;
+    __syncthreads();
+    for (int base = 0; base < nC; base += STEP) {
+      const int c = base + 8 * tid;
+      uint32_t kv[8];
+      load8(keys, c, nC, kv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool match = c + q < nC && (done == 0 || (kv[q] >> (32 - done)) == prefix);
+        hist_add(hist, (kv[q] >> sh) & ((1u << nb) - 1u), match);
       }
-      __syncthreads();
-      if (tid < 64) {
-        // lane l owns bins 4l .. 4l+3; suffix sums from the top bin down
-        uint32_t h4[4], s = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          h4[q] = hist[4 * tid + q];
-          s += h4[q];
-        }
-        // inclusive suffix scan over lanes (sum of lanes >= tid)
-        uint32_t suf = s;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_down(suf, o);
-          if (tid + o < 64) suf += y;
-        }
-        uint32_t above = suf - s;  // keys in bins of higher lanes
-#pragma unroll
-        for (int q = 3; q >= 0; --q) {
-          if (above < krem && above + h4[q] >= krem) {
-            bc[0] = 4 * tid + q;
-            bc[1] = above;
-          }
-          above += h4[q];
-        }
-      }
-      __syncthreads();
-      const uint32_t d = bc[0];
-      krem -= bc[1];
-      prefix |= d << shift;
-      pmask |= 255u << shift;
-      __syncthreads();
     }
-    thr = prefix;
-    need_eq = krem;
+    __syncthreads();
+    find_bin(hist, krem, wsum, res);
+    const uint32_t d = res[0];
+    krem -= res[1];
+    cnt = hist[d];
+    prefix = (prefix << nb) | d;
+    done += nb;
+    __syncthreads();
+    if (cnt <= (uint32_t)kCandCap || done == 32) break;
   }
 
-  // Ordered compaction: keys > thr, plus the first need_eq keys == thr by position.
+  uint32_t T, need_eq, c_last = 0xffffffffu;
+  bool by_index = false;
+  if (done == 32) {
+    T = prefix;
+    need_eq = krem;
+  } else {
+    // 2. compact the boundary bin into LDS (unordered)
+    if (tid == 0) res[2] = 0;
+    __syncthreads();
+    for (int base = 0; base < nC; base += STEP) {
+      const int c = base + 8 * tid;
+      uint32_t kv[8];
+      load8(keys, c, nC, kv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool match = c + q < nC && (kv[q] >> (32 - done)) == prefix;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(match);
+        const int lane = tid & 63;
+        uint32_t slot0 = 0;
+        if (m && lane == __builtin_ctzll(m)) slot0 = atomicAdd(&res[2], (uint32_t)__builtin_popcountll(m));
+        slot0 = __shfl(slot0, m ? __builtin_ctzll(m) : 0);
+        if (match) {
+          const uint32_t slot = slot0 + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+          ckey[slot] = kv[q];
+          cidx[slot] = (uint32_t)(c + q);
+        }
+      }
+    }
+    __syncthreads();
+    const int n = (int)res[2];
+    // 3. LDS passes over the remaining bits
+    while (done < 32) {
+      const int nb = min(11, 32 - done);
+      const int sh = 32 - done - nb;
+      for (int k = tid; k < kHistBins; k += kTopkThreads) hist[k] = 0;
+      __syncthreads();
+      for (int base = 0; base < n; base += kTopkThreads) {
+        const int e = base + tid;
+        const uint32_t key = e < n ? ckey[e] : 0u;
+        const bool match = e < n && (key >> (32 - done)) == prefix;
+        hist_add(hist, (key >> sh) & ((1u << nb) - 1u), match);
+      }
+      __syncthreads();
+      find_bin(hist, krem, wsum, res);
+      krem -= res[1];
+      prefix = (prefix << nb) | res[0];
+      done += nb;
+      __syncthreads();
+    }
+    T = prefix;
+    need_eq = krem;
+    // ties at T: the need_eq-th smallest candidate index is the last one taken
+    {
+      uint32_t uprefix = 0, urem = need_eq;
+      int udone = 0;
+      while (udone < 32) {
+        const int nb = min(11, 32 - udone);
+        const int sh = 32 - udone - nb;
+        for (int k = tid; k < kHistBins; k += kTopkThreads) hist[k] = 0;
+        __syncthreads();
+        for (int base = 0; base < n; base += kTopkThreads) {
+          const int e = base + tid;
+          const bool tie = e < n && ckey[e] == T;
+          const uint32_t u = tie ? ~cidx[e] : 0u;
+          const bool match = tie && (udone == 0 || (u >> (32 - udone)) == uprefix);
+          hist_add(hist, (u >> sh) & ((1u << nb) - 1u), match);
+        }
+        __syncthreads();
+        find_bin(hist, urem, wsum, res);
+        urem -= res[1];
+        uprefix = (uprefix << nb) | res[0];
+        udone += nb;
+        __syncthreads();
+      }
+      c_last = ~uprefix;
+      by_index = true;
+    }
+  }
+
+  // 4. ordered output
   uint32_t taken = 0, eq_seen = 0;
-  for (int base = 0; base < nC && taken < (uint32_t)keff; base += 4 * kTopkThreads) {
-    const int c0 = base + 4 * tid;
-    uint32_t kv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) kv[q] = (c0 + q < nC) ? keys[c0 + q] : 0u;
-    uint32_t neq = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) neq += (c0 + q < nC && kv[q] == thr) ? 1u : 0u;
-    uint32_t eq_tot;
-    uint32_t eq_before = eq_seen + block_exscan(neq, wsum, &eq_tot);
-    bool take[4];
+  for (int base = 0; base < nC && taken < (uint32_t)keff; base += STEP) {
+    const int c = base + 8 * tid;
+    uint32_t kv[8];
+    load8(keys, c, nC, kv);
+    bool take[8];
     uint32_t nsel = 0;
+    if (by_index) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool valid = c0 + q < nC;
-      const bool gt = valid && kv[q] > thr;
-      const bool eq = valid && kv[q] == thr;
-      take[q] = gt || (eq && eq_before < need_eq);
-      if (eq) ++eq_before;
-      nsel += take[q] ? 1u : 0u;
+      for (int q = 0; q < 8; ++q) {
+        take[q] = c + q < nC && (kv[q] > T || (kv[q] == T && (uint32_t)(c + q) <= c_last));
+        nsel += take[q] ? 1u : 0u;
+      }
+    } else {
+      uint32_t neq = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) neq += (c + q < nC && kv[q] == T) ? 1u : 0u;
+      uint32_t eq_tot;
+      uint32_t eq_before = eq_seen + block_exscan(neq, wsum, &eq_tot);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool valid = c + q < nC;
+        const bool eq = valid && kv[q] == T;
+        take[q] = (valid && kv[q] > T) || (eq && eq_before < need_eq);
+        if (eq) ++eq_before;
+        nsel += take[q] ? 1u : 0u;
+      }
+      eq_seen += eq_tot;
     }
     uint32_t sel_tot;
     uint32_t at = taken + block_exscan(nsel, wsum, &sel_tot);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (take[q] && at < (uint32_t)keff) out[at++] = lo + c0 + q;
+    for (int q = 0; q < 8; ++q)
+      if (take[q] && at < (uint32_t)keff) out[at++] = lo + c + q;
     taken += sel_tot;
-    eq_seen += eq_tot;
   }
 }
 
@@ -416,10 +614,27 @@ SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len) {
   return L;
 }
 
-size_t score_lds_bytes(int num_kv_heads, int num_q_heads, int nms_radius) {
-  return sizeof(float) * ((size_t)num_kv_heads * (kScoreTile + 2 * (size_t)nms_radius) +
+size_t score_lds_bytes(int num_kv_heads, int num_q_heads, int nms_radius, int tile) {
+  return sizeof(float) * ((size_t)num_kv_heads * (tile + 2 * (size_t)nms_radius) +
                           num_kv_heads + num_q_heads);
 }
+
+namespace {
+
+template <int PPT>
+void launch_score_g(const ScoreArgs& a, int n_seqs, size_t lds, hipStream_t st) {
+  const dim3 grid(n_seqs * a.ntile), block(256);
+  switch (a.G) {
+    case 1: hipLaunchKernelGGL((k_sel_score<1, PPT>), grid, block, lds, st, a); break;
+    case 2: hipLaunchKernelGGL((k_sel_score<2, PPT>), grid, block, lds, st, a); break;
+    case 4: hipLaunchKernelGGL((k_sel_score<4, PPT>), grid, block, lds, st, a); break;
+    case 8: hipLaunchKernelGGL((k_sel_score<8, PPT>), grid, block, lds, st, a); break;
+    case 16: hipLaunchKernelGGL((k_sel_score<16, PPT>), grid, block, lds, st, a); break;
+    default: hipLaunchKernelGGL((k_sel_score<0, PPT>), grid, block, lds, st, a); break;
+  }
+}
+
+}  // namespace
 
 hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm, const float* logits,
                          int64_t logits_stride, const float* lse, const float* key_norm,
@@ -449,15 +664,21 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm, const
   a.Hkv = Hkv;
   a.G = Hq / Hkv;
   a.nchunk = L.nchunk;
-  a.ntile = (max_seq_len + kScoreTile - 1) / kScoreTile;
   a.n_sink = prm.n_sink;
   a.n_recent = prm.n_recent;
   a.R = prm.nms_radius;
   a.lam = prm.lambda;
   a.a_soft = prm.alpha_soft;
   a.a_cross = prm.alpha_cross;
-  const size_t lds = score_lds_bytes(Hkv, Hq, prm.nms_radius);
-  hipLaunchKernelGGL(k_sel_score, dim3(n_seqs * a.ntile), dim3(256), lds, st, a);
+  // Wide tiles when their LDS fits, narrow ones otherwise.
+  const size_t wide = score_lds_bytes(Hkv, Hq, prm.nms_radius, 1024);
+  if (wide <= kScoreLdsLimit) {
+    a.ntile = (max_seq_len + 1023) / 1024;
+    launch_score_g<4>(a, n_seqs, wide, st);
+  } else {
+    a.ntile = (max_seq_len + 255) / 256;
+    launch_score_g<1>(a, n_seqs, score_lds_bytes(Hkv, Hq, prm.nms_radius, 256), st);
+  }
   TopkArgs t;
   t.keys = keys;
   t.kstride = L.kstride;

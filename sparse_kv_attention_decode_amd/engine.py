@@ -169,7 +169,6 @@ class Engine:
         self.layers.append(lb)
         return lb
 
-    # ------------------------------------------------------------------------ one step
     # ------------------------------------------------------------ algorithmic traffic
     def fast_bytes(self, s: int) -> int:
         """Bytes a fast attention call of step s must move: the packed rows and the recent
@@ -190,23 +189,66 @@ class Engine:
                    + 8 * w.num_q_heads * w.head_dim for b in ids)
 
     # ------------------------------------------------------------------------ one step
-    def step(self, s: int, dense_only: bool = False, timer: Optional[list] = None) -> None:
+    def _bind(self) -> None:
+        """Cache the ctypes entry points and the raw device pointers step() passes, so a
+        step costs one foreign call per kernel launch and no tensor indexing."""
+        import ctypes
+        self._lib = L.load()
+        self._shp = ctypes.byref(self.shape)
+        self._prm = ctypes.byref(self.params)
+        B = self.w.batch
+        self._rowb = B * 4                       # one [B] int32 row of the step tables
+        self._seq_len_p = self.seq_len_d.data_ptr()
+        self._rstart_p = self.rstart_d.data_ptr()
+        self._slow_p = self.slow_ids_d.data_ptr()
+        self._fast_p = self.fast_ids_d.data_ptr()
+        self._all_p = self.all_ids_d.data_ptr()
+        self._h1 = self.stream1.cuda_stream
+        self._h2 = self.stream2.cuda_stream
+        self._ws = {k: (t.data_ptr(), t.numel()) for k, t in
+                    (("slow", self.ws_slow), ("fast", self.ws_fast), ("sel", self.ws_sel))}
+        self._dbg_p = self.dbg_buf.data_ptr() if self.dbg_buf is not None else None
+        for lb in self.layers:
+            lb.ptr = {k: getattr(lb, a).data_ptr() for k, a in (
+                ("k", "k_cache"), ("v", "v_cache"), ("bt", "block_table"), ("q", "q_all"),
+                ("norm", "key_norm"), ("z", "logits"), ("lse", "lse"), ("sel", "sel_idx"),
+                ("pk", "packed_k"), ("pv", "packed_v"), ("pp", "packed_pos"),
+                ("pl", "packed_len"), ("out", "out"))}
+            lb.q_step = lb.q_all[0].numel() * lb.q_all.element_size()
+        self._bound_layers = len(self.layers)
+
+    @staticmethod
+    def _ok(name: str, rc: int) -> None:
+        if rc != L.SFI_OK:
+            raise L.SfiError(name, rc, L.status_str(rc))
+
+    def step(self, s: int, dense_only: bool = False, timer: Optional[list] = None,
+             time_every: int = 1) -> None:
         """Issue decode step s of every layer (no host synchronisation).
 
         dense_only runs the Full-KV baseline: dense attention for every sequence, no
-        Selector, no logits.  When `timer` is a list, every attention call is bracketed by
-        two events on stream 1 and (kind, start, end, algorithmic bytes) is appended.
+        Selector, no logits.  When `timer` is a list, the attention calls of every
+        `time_every`-th layer are bracketed by two events on stream 1 and
+        (kind, start, end, algorithmic bytes) is appended.
         """
-        w, shp = self.w, self.shape
-        slow_ids = self.plan.slow_ids[s]
-        fast_ids = self.plan.fast_ids[s]
-        n_slow, n_fast = len(slow_ids), len(fast_ids)
-        seq_len = self.seq_len_d[s]
-        rstart = self.rstart_d[s]
+        if getattr(self, "_bound_layers", -1) != len(self.layers):
+            self._bind()
+        w, lib, shp, prm = self.w, self._lib, self._shp, self._prm
+        n_slow = len(self.plan.slow_ids[s])
+        n_fast = len(self.plan.fast_ids[s])
+        seq_len = self._seq_len_p + s * self._rowb
+        rstart = self._rstart_p + s * self._rowb
+        slow_ids = self._slow_p + s * self._rowb
+        fast_ids = self._fast_p + s * self._rowb
         s1, s2 = self.stream1, self.stream2
+        h1, h2 = self._h1, self._h2
+        ws_slow, ws_slow_n = self._ws["slow"]
+        ws_fast, ws_fast_n = self._ws["fast"]
+        ws_sel, ws_sel_n = self._ws["sel"]
+        ok = self._ok
 
-        def timed(kind, nbytes, fn):
-            if timer is None:
+        def timed(li, kind, nbytes, fn):
+            if timer is None or li % time_every:
                 fn()
                 return
             e0 = torch.cuda.Event(enable_timing=True)
@@ -217,40 +259,38 @@ class Engine:
             timer.append((kind, e0, e1, nbytes))
 
         fb = self.fast_bytes(s) if (timer is not None and n_fast) else 0
-        db = self.dense_bytes(s, range(w.batch) if dense_only else slow_ids) \
+        db = self.dense_bytes(s, range(w.batch) if dense_only else self.plan.slow_ids[s]) \
             if timer is not None else 0
-        for lb in self.layers:
-            q = lb.q_all[s]
+        for li, lb in enumerate(self.layers):
+            P = lb.ptr
+            q = P["q"] + s * lb.q_step
             if dense_only:
-                timed("dense", db, lambda: L.sfi_slow_attn(
-                    shp, q, lb.k_cache, lb.v_cache, lb.block_table, seq_len, self.all_ids_d,
-                    w.batch, self.max_len, lb.out, None, 0, lb.lse, self.ws_slow, stream=s1))
+                timed(li, "dense", db, lambda: ok("sfi_slow_attn", lib.sfi_slow_attn(
+                    shp, q, P["k"], P["v"], P["bt"], seq_len, self._all_p, w.batch,
+                    self.max_len, P["out"], None, 0, P["lse"], ws_slow, ws_slow_n, h1)))
                 continue
             if lb.pack_pending:
                 s1.wait_event(lb.ev_pack)
                 lb.pack_pending = False
             if n_fast:
-                timed("fast", fb, lambda: L.sfi_fast_attn(
-                    shp, q, lb.packed_k, lb.packed_v, lb.packed_len, self.packed_cap,
-                    lb.k_cache, lb.v_cache, lb.block_table, rstart, seq_len,
-                    self.fast_ids_d[s], n_fast, self.max_recent, lb.out, None, self.ws_fast,
-                    stream=s1))
+                timed(li, "fast", fb, lambda: ok("sfi_fast_attn", lib.sfi_fast_attn(
+                    shp, q, P["pk"], P["pv"], P["pl"], self.packed_cap, P["k"], P["v"],
+                    P["bt"], rstart, seq_len, fast_ids, n_fast, self.max_recent, P["out"],
+                    None, ws_fast, ws_fast_n, h1)))
             if n_slow:
-                ids = self.slow_ids_d[s]
-                timed("slow", db, lambda: L.sfi_slow_attn(
-                    shp, q, lb.k_cache, lb.v_cache, lb.block_table, seq_len, ids, n_slow,
-                    self.max_len, lb.out, lb.logits, self.stride, lb.lse, self.ws_slow,
-                    stream=s1))
+                timed(li, "slow", db, lambda: ok("sfi_slow_attn", lib.sfi_slow_attn(
+                    shp, q, P["k"], P["v"], P["bt"], seq_len, slow_ids, n_slow, self.max_len,
+                    P["out"], P["z"], self.stride, P["lse"], ws_slow, ws_slow_n, h1)))
                 if s2 is not s1:
                     lb.ev_attn.record(s1)
                     s2.wait_event(lb.ev_attn)
-                dbg = self.dbg_buf if self.dbg else None
-                L.sfi_select(shp, self.params, lb.logits, self.stride, lb.lse, lb.key_norm,
-                             self.stride, seq_len, ids, n_slow, self.max_len, lb.sel_idx, dbg,
-                             self.ws_sel, stream=s2)
-                L.sfi_pack(shp, self.params, lb.k_cache, lb.v_cache, lb.block_table,
-                           lb.sel_idx, ids, n_slow, lb.packed_k, lb.packed_v, lb.packed_pos,
-                           lb.packed_len, self.packed_cap, stream=s2)
+                ok("sfi_select", lib.sfi_select(
+                    shp, prm, P["z"], self.stride, P["lse"], P["norm"], self.stride, seq_len,
+                    slow_ids, n_slow, self.max_len, P["sel"], self._dbg_p, ws_sel, ws_sel_n,
+                    h2))
+                ok("sfi_pack", lib.sfi_pack(
+                    shp, prm, P["k"], P["v"], P["bt"], P["sel"], slow_ids, n_slow, P["pk"],
+                    P["pv"], P["pp"], P["pl"], self.packed_cap, h2))
                 if s2 is not s1:
                     lb.ev_pack.record(s2)
                     lb.pack_pending = True

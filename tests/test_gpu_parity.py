@@ -363,3 +363,43 @@ def test_full_size_sampled(name):
         o, _ = O.fast_attention(q[1], K, V, pos, O.recent_start_at(N, w.n_sink, w.n_recent),
                                 w.seq_len(1))
         check_out(out1[b], o, f"{name} fast b={b}")
+
+
+# ------------------------------------------------------------- Top-K selection paths
+def _select_direct(shape, params, logits, lse, key_norm, N, stride):
+    B = shape.batch
+    seq_lens = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    ids = torch.arange(B, dtype=torch.int32, device="cuda")
+    sel = torch.full((B, shape.num_kv_heads, params.top_k), -7, dtype=torch.int32, device="cuda")
+    dbg = torch.zeros(B, shape.num_kv_heads, stride, dtype=torch.float32, device="cuda")
+    ws = L.workspace(L.sfi_select_ws(shape, params, B, N), "cuda")
+    L.sfi_select(shape, params, logits, stride, lse, key_norm, stride, seq_lens, ids, B, N, sel,
+                 dbg, ws)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), host64(dbg)
+
+
+def test_topk_concentrated_scores_need_several_passes():
+    """Prior-only scores (lambda = 1) with equal key norms vary by a few percent over 128K
+    positions, so the bin of the K-th key holds far more keys than the LDS candidate list
+    takes and the selection needs further passes over global memory."""
+    import math
+    Hq, Hkv, D, N, K = 8, 2, 128, 131072 + 100, 19456
+    stride = (N + 63) // 64 * 64
+    shape = L.make_shape(1, Hq, Hkv, D, (N + 15) // 16, "bf16")
+    params = L.make_params(4, 1024, K, 4, 1.0, 0.5, 0.5)
+    logits = torch.zeros(1, Hq, stride, device="cuda")
+    lse = torch.full((1, Hq), math.log(N), device="cuda")
+    key_norm = torch.full((1, Hkv, stride), 2.0, device="cuda")
+    sel, dbg = _select_direct(shape, params, logits, lse, key_norm, N, stride)
+    ref = O.select_from_scores(dbg[0, :, :N], N, 4, 1024, K, 4, 0.5, 0.5)
+    np.testing.assert_array_equal(sel[0], ref)
+
+
+def test_topk_heavy_exact_ties():
+    """alpha_soft = alpha_cross = 1 zeroes every dominated or non-owned score, so the K-th
+    key is 0 and thousands of candidates tie with it: the lowest positions must win."""
+    w = get("qwen3_0p6b_8k").replace(alpha_soft=1.0, alpha_cross=1.0, steps=4,
+                                     name="heavy_ties_8k")
+    d, eng, lb = _setup(w, dbg=True)
+    _select_and_check(w, d, eng, lb, 0)
