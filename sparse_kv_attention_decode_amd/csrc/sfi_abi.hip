@@ -176,8 +176,7 @@ int sfi_select(const sfi_shape* shape, const sfi_select_params* params, const fl
   if (!aligned16(logits) || !aligned16(key_norm) || (dbg_scores && !aligned16(dbg_scores)))
     return SFI_E_ALIGN;
   if (params->nms_radius > 1024) return SFI_E_UNSUPPORTED;
-  if (sfi::score_lds_bytes(shape->num_kv_heads, shape->num_q_heads, params->nms_radius, 256) >
-      sfi::kScoreLdsLimit)
+  if (sfi::score_tile(shape->num_kv_heads, shape->num_q_heads, params->nms_radius) == 0)
     return SFI_E_UNSUPPORTED;
   const size_t need = sfi_select_ws(shape, params, n_seqs, max_seq_len);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SFI_E_WORKSPACE;

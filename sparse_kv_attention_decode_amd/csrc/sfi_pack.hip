@@ -51,9 +51,23 @@ __global__ __launch_bounds__(64) void k_pack(PackArgs a) {
     const int page = a.bt[(size_t)b * a.max_pages + pos / kPage];
     const size_t src = (((size_t)page * a.Hkv + g) * kPage + pos % kPage) * a.row_bytes +
                        quarter * 16;
-    for (int o = 0; o < a.row_bytes; o += 64) {
-      *reinterpret_cast<u32x4_t*>(dk + o) = *reinterpret_cast<const u32x4_t*>(a.kc + src + o);
-      *reinterpret_cast<u32x4_t*>(dv + o) = *reinterpret_cast<const u32x4_t*>(a.vc + src + o);
+    // All loads of the row first, then all stores (rows are at most 512 bytes).
+    constexpr int kMaxSteps = 8;
+    const int steps = a.row_bytes / 64;
+    u32x4_t kv[kMaxSteps], vv[kMaxSteps];
+#pragma unroll
+    for (int k = 0; k < kMaxSteps; ++k) {
+      if (k < steps) {
+        kv[k] = *reinterpret_cast<const u32x4_t*>(a.kc + src + 64 * k);
+        vv[k] = *reinterpret_cast<const u32x4_t*>(a.vc + src + 64 * k);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxSteps; ++k) {
+      if (k < steps) {
+        *reinterpret_cast<u32x4_t*>(dk + 64 * k) = kv[k];
+        *reinterpret_cast<u32x4_t*>(dv + 64 * k) = vv[k];
+      }
     }
   } else {
     const u32x4_t zero = {0u, 0u, 0u, 0u};

@@ -17,11 +17,11 @@
 //
 // Kernels:
 //   k_sel_zsum   Z_g partial sums over chunks of 4096 positions.
-//   k_sel_score  one block per 1024-position tile (256 when LDS is short) with an
-//                R-position halo, all KV heads at once (NMS couples neighbours,
-//                exclusivity couples heads): s into LDS, then the refined score s' as an
-//                order-preserving uint32 key (s' >= 0, so its IEEE bits already order
-//                like the value).
+//   k_sel_score  one block per tile of up to 256 positions with an R-position halo, all
+//                KV heads at once (NMS couples neighbours, exclusivity couples heads):
+//                logits and norms staged in LDS, s computed there, then the refined score
+//                s' as an order-preserving uint32 key (s' >= 0, so its IEEE bits already
+//                order like the value).
 //   k_sel_topk   one 1024-thread block per (b, g): radix select of the K-th largest key
 //                (an 11-bit histogram pass over global memory, then LDS-resident passes
 //                over the boundary bin), then one ordered pass that writes every key
@@ -169,50 +169,34 @@ struct ScoreArgs {
   uint32_t* keys;
   int64_t kstride;
   float* dbg;
-  int Hq, Hkv, G, nchunk, ntile;
+  int Hq, Hkv, G, nchunk, ntile, tile;
   int n_sink, n_recent, R;
   float lam, a_soft, a_cross;
 };
 
-// Fused score s(g, j) of one position for every KV head, written to LDS row idx.
-template <int GT>
-__device__ __forceinline__ void score_scalar(const ScoreArgs& a, const float* zs,
-                                             const float* lses, float* s_t, int W, int b,
-                                             int N, int j, int idx, bool dbg) {
-  const int G = GT > 0 ? GT : a.G;
-  const bool in = j >= 0 && j < N;
-  const float phi_pos = in ? 1.f + logf(1.f + (float)(N - 1 - j)) : 0.f;
-  for (int g = 0; g < a.Hkv; ++g) {
-    float s = -1.f;
-    if (in) {
-      float f = 0.f;
-      for (int hh = 0; hh < G; ++hh) {
-        const int h = g * G + hh;
-        f += expf(a.logits[((size_t)b * a.Hq + h) * a.logits_stride + j] - lses[h]);
-      }
-      f *= 1.f / (float)G;
-      const float nrm = a.key_norm[((size_t)b * a.Hkv + g) * a.norm_stride + j];
-      const float r = (1.f / fmaxf(nrm, 1e-6f)) * phi_pos / zs[g];
-      s = (1.f - a.lam) * f + a.lam * r;
-      if (dbg) a.dbg[((size_t)b * a.Hkv + g) * a.logits_stride + j] = s;
-    }
-    s_t[g * W + idx] = s;
-  }
-}
+// Row width of the staged tile: the halo on each side is padded to a multiple of four
+// so the tile body keeps 16-byte alignment in LDS.
+__host__ __device__ inline int score_pad(int R) { return (R + 3) & ~3; }
 
-// One block per (row, tile of TILE positions): every KV head of the tile plus an R-wide
-// halo on each side (soft-NMS reads neighbours, exclusivity reads all heads of a
-// position), then the refined keys of the tile's candidates.
-template <int GT, int PPT>
+// One block per (row, tile of `tile` positions).  Stage the logits of every query head
+// and the key norms of every KV head over the tile and an R-wide halo on each side into
+// LDS, with all global loads issued before any arithmetic; then the fused score s of
+// every KV head at every staged position; then, for the tile's candidates, the soft-NMS
+// dominance (neighbours within R, same head) and ownership (all heads at the position)
+// and the refined key.
+template <int GT>
 __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
-  constexpr int TILE = 256 * PPT;
-  constexpr int GU = GT > 0 ? GT : kMaxG;  // unroll bound; runtime G when GT == 0
+  extern __shared__ float4 lds4[];  // float4 keeps the staged rows 16-byte aligned
+  float* lds = reinterpret_cast<float*>(lds4);
   const int G = GT > 0 ? GT : a.G;
-  extern __shared__ float lds[];
-  const int W = TILE + 2 * a.R;
-  float* s_t = lds;                         // [Hkv][W]
-  float* zs = lds + a.Hkv * W;              // [Hkv]
-  float* lses = zs + a.Hkv;                 // [Hq]
+  const int TILE = a.tile;
+  const int P = score_pad(a.R);
+  const int W = TILE + 2 * P;
+  float* zt = lds;                    // [Hq][W]   logits
+  float* nt = zt + a.Hq * W;          // [Hkv][W]  key norms
+  float* s_t = nt + a.Hkv * W;        // [Hkv][W]  fused scores
+  float* zs = s_t + a.Hkv * W;        // [Hkv]     prior normalisers
+  float* lses = zs + a.Hkv;           // [Hq]
   const int tid = threadIdx.x;
   const int i = blockIdx.x / a.ntile;
   const int tile = blockIdx.x % a.ntile;
@@ -223,6 +207,37 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
   const int lo = a.n_sink;
   const int hi = max(lo, N - a.n_recent);
 
+  // Stage the tile body (float4) and the halo (scalars) of logits and norms.
+  const int q4 = TILE / 4;
+  const int rows = a.Hq + a.Hkv;
+  for (int e = tid; e < rows * q4; e += 256) {
+    const int row = e / q4, c4 = e % q4;
+    const int j = t0 + 4 * c4;
+    const float* src = row < a.Hq
+                           ? a.logits + ((size_t)b * a.Hq + row) * a.logits_stride + j
+                           : a.key_norm + ((size_t)b * a.Hkv + (row - a.Hq)) * a.norm_stride + j;
+    float4 v;
+    if (j + 3 < N) {
+      v = *reinterpret_cast<const float4*>(src);
+    } else {
+      v.x = j < N ? src[0] : 0.f;
+      v.y = j + 1 < N ? src[1] : 0.f;
+      v.z = j + 2 < N ? src[2] : 0.f;
+      v.w = j + 3 < N ? src[3] : 0.f;
+    }
+    *reinterpret_cast<float4*>(zt + row * W + P + 4 * c4) = v;
+  }
+  for (int e = tid; e < rows * 2 * a.R; e += 256) {
+    const int row = e / (2 * a.R), k = e % (2 * a.R);
+    const bool left = k < a.R;
+    const int j = left ? t0 - a.R + k : t0 + TILE + (k - a.R);
+    const int col = left ? P - a.R + k : P + TILE + (k - a.R);
+    float v = 0.f;
+    if (j >= 0 && j < N)
+      v = row < a.Hq ? a.logits[((size_t)b * a.Hq + row) * a.logits_stride + j]
+                     : a.key_norm[((size_t)b * a.Hkv + (row - a.Hq)) * a.norm_stride + j];
+    zt[row * W + col] = v;
+  }
   for (int g = tid; g < a.Hkv; g += 256) {
     const float* zp = a.zpart + ((size_t)i * a.Hkv + g) * a.nchunk;
     float z = 0.f;
@@ -232,67 +247,43 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
   for (int h = tid; h < a.Hq; h += 256) lses[h] = a.lse[(size_t)b * a.Hq + h];
   __syncthreads();
 
-  // Main positions: thread tid owns j = t0 + PPT*tid .. +PPT-1.
-  const int jm = t0 + PPT * tid;
-  if (PPT == 4 && jm + 3 < N) {
-    float phi[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) phi[q] = 1.f + logf(1.f + (float)(N - 1 - (jm + q)));
+  // Fused scores over the tile and its halo.
+  const float invG = 1.f / (float)G;
+  for (int col = P - a.R + tid; col < P + TILE + a.R; col += 256) {
+    const int j = t0 - P + col;
+    const bool in = j >= 0 && j < N;
+    const float phi_pos = in ? 1.f + logf(1.f + (float)(N - 1 - j)) : 0.f;
+    const bool body = col >= P && col < P + TILE;
     for (int g = 0; g < a.Hkv; ++g) {
-      float4 zv[GU];
+      float s = -1.f;
+      if (in) {
+        float f = 0.f;
+        if (GT > 0) {
 #pragma unroll
-      for (int hh = 0; hh < GU; ++hh)
-        if (hh < G)
-          zv[hh] = *reinterpret_cast<const float4*>(
-              a.logits + ((size_t)b * a.Hq + g * G + hh) * a.logits_stride + jm);
-      const float4 nv = *reinterpret_cast<const float4*>(
-          a.key_norm + ((size_t)b * a.Hkv + g) * a.norm_stride + jm);
-      float f[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int hh = 0; hh < GU; ++hh) {
-        if (hh >= G) break;
-        const float l = lses[g * G + hh];
-        f[0] += expf(zv[hh].x - l);
-        f[1] += expf(zv[hh].y - l);
-        f[2] += expf(zv[hh].z - l);
-        f[3] += expf(zv[hh].w - l);
+          for (int hh = 0; hh < (GT > 0 ? GT : 1); ++hh)
+            f += expf(zt[(g * G + hh) * W + col] - lses[g * G + hh]);
+        } else {
+          for (int hh = 0; hh < G; ++hh) f += expf(zt[(g * G + hh) * W + col] - lses[g * G + hh]);
+        }
+        f *= invG;
+        const float r = (1.f / fmaxf(nt[g * W + col], 1e-6f)) * phi_pos / zs[g];
+        s = (1.f - a.lam) * f + a.lam * r;
+        if (a.dbg && body) a.dbg[((size_t)b * a.Hkv + g) * a.logits_stride + j] = s;
       }
-      const float nr[4] = {nv.x, nv.y, nv.z, nv.w};
-      float s[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float r = (1.f / fmaxf(nr[q], 1e-6f)) * phi[q] / zs[g];
-        s[q] = (1.f - a.lam) * (f[q] * (1.f / (float)G)) + a.lam * r;
-        s_t[g * W + a.R + PPT * tid + q] = s[q];
-      }
-      if (a.dbg)
-        *reinterpret_cast<float4*>(a.dbg + ((size_t)b * a.Hkv + g) * a.logits_stride + jm) =
-            make_float4(s[0], s[1], s[2], s[3]);
+      s_t[g * W + col] = s;
     }
-  } else {
-#pragma unroll
-    for (int q = 0; q < PPT; ++q)
-      score_scalar<GT>(a, zs, lses, s_t, W, b, N, jm + q, a.R + PPT * tid + q, a.dbg != nullptr);
-  }
-  // Halo: R positions left of the tile and R right of it.
-  for (int k = tid; k < 2 * a.R; k += 256) {
-    const int left = k < a.R;
-    const int j = left ? t0 - a.R + k : t0 + TILE + (k - a.R);
-    const int idx = left ? k : a.R + TILE + (k - a.R);
-    score_scalar<GT>(a, zs, lses, s_t, W, b, N, j, idx, false);
   }
   __syncthreads();
 
+  // Refinement decisions and keys for the tile's candidates.
   const float ws = 1.f - a.a_soft, wc = 1.f - a.a_cross;
-#pragma unroll
-  for (int q = 0; q < PPT; ++q) {
-    const int j = jm + q;
+  for (int col = P + tid; col < P + TILE; col += 256) {
+    const int j = t0 - P + col;
     if (j < lo || j >= hi) continue;
-    const int c = a.R + PPT * tid + q;
     int own = 0;
-    float best = s_t[c];
+    float best = s_t[col];
     for (int g = 1; g < a.Hkv; ++g) {
-      const float v = s_t[g * W + c];
+      const float v = s_t[g * W + col];
       if (v > best) {
         best = v;
         own = g;
@@ -301,7 +292,7 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
     const int dlo = max(lo, j - a.R) - j;      // <= 0
     const int dhi = min(hi - 1, j + a.R) - j;  // >= 0
     for (int g = 0; g < a.Hkv; ++g) {
-      const float* row = s_t + g * W + c;
+      const float* row = s_t + g * W + col;
       const float sj = row[0];
       bool dom = false;
       for (int d = dlo; d <= dhi; ++d) dom |= (d != 0) && (row[d] > sj);
@@ -326,6 +317,8 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
 //      complemented candidate index;
 //   4. one ordered pass writes every candidate above T and the ties up to that index,
 //      ascending, with a block-wide prefix sum per chunk.
+// Every pass over global keys reads 16 keys per thread per chunk with the next chunk in
+// flight.
 constexpr int kTopkThreads = 1024;
 constexpr int kHistBins = 2048;
 constexpr int kCandCap = kCandCapBytes / 8;  // key + index per candidate
@@ -401,17 +394,40 @@ struct TopkArgs {
   int Hkv, K, n_sink, n_recent;
 };
 
-// Load keys[c .. c+8) (c a multiple of 8) into kv; entries past n read as 0 and are
-// marked invalid by the caller's bounds check.
-__device__ __forceinline__ void load8(const uint32_t* keys, int c, int n, uint32_t kv[8]) {
-  if (c + 8 <= n) {
-    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(keys + c);
-    const u32x4_t y = *reinterpret_cast<const u32x4_t*>(keys + c + 4);
-    kv[0] = x[0]; kv[1] = x[1]; kv[2] = x[2]; kv[3] = x[3];
-    kv[4] = y[0]; kv[5] = y[1]; kv[6] = y[2]; kv[7] = y[3];
-  } else {
+constexpr int kKeysPerThread = 16;
+constexpr int kPassStep = kKeysPerThread * kTopkThreads;
+
+// keys[c .. c+16) as four 16-byte loads.  The read is clamped into the row
+// [0, kstride) (kstride is a multiple of 64), so it is issued unconditionally; entries at
+// or past the candidate count are masked by the caller through their index.
+__device__ __forceinline__ void load16(const uint32_t* keys, int64_t kstride, int c,
+                                       uint32_t kv[kKeysPerThread]) {
+  const int cl = (int)min((int64_t)c, kstride - kKeysPerThread);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) kv[q] = (c + q < n) ? keys[c + q] : 0u;
+  for (int w = 0; w < 4; ++w) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(keys + cl + 4 * w);
+    kv[4 * w] = x[0];
+    kv[4 * w + 1] = x[1];
+    kv[4 * w + 2] = x[2];
+    kv[4 * w + 3] = x[3];
+  }
+}
+
+// Visit keys [0, n) in chunks of 16 per thread; the next chunk is requested before the
+// current one is processed (two register buffers, unrolled so they swap roles without
+// copies).  f(c, kv) sees the keys at candidate indices c .. c+15 and is called by every
+// thread the same number of times (it may contain block barriers).
+template <typename F>
+__device__ __forceinline__ void pass16(const uint32_t* keys, int64_t kstride, int n, F&& f) {
+  const int off = kKeysPerThread * (int)threadIdx.x;
+  uint32_t A[kKeysPerThread], B[kKeysPerThread];
+  load16(keys, kstride, off, A);
+  for (int base = 0; base < n; base += 2 * kPassStep) {
+    load16(keys, kstride, base + kPassStep + off, B);
+    f(base + off, A);
+    if (base + kPassStep >= n) break;
+    load16(keys, kstride, base + 2 * kPassStep + off, A);
+    f(base + kPassStep + off, B);
   }
 }
 
@@ -438,8 +454,6 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
     for (int k = tid; k < nC; k += kTopkThreads) out[k] = lo + k;
     return;
   }
-  constexpr int STEP = 8 * kTopkThreads;
-
   // 1. global histogram passes
   uint32_t prefix = 0, krem = (uint32_t)keff, cnt = 0;
   int done = 0;  // resolved top bits
@@ -448,16 +462,13 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
     const int sh = 32 - done - nb;
     for (int k = tid; k < kHistBins; k += kTopkThreads) hist[k] = 0;
     __syncthreads();
-    for (int base = 0; base < nC; base += STEP) {
-      const int c = base + 8 * tid;
-      uint32_t kv[8];
-      load8(keys, c, nC, kv);
+    pass16(keys, a.kstride, nC, [&](int c, const uint32_t* kv) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kKeysPerThread; ++q) {
         const bool match = c + q < nC && (done == 0 || (kv[q] >> (32 - done)) == prefix);
         hist_add(hist, (kv[q] >> sh) & ((1u << nb) - 1u), match);
       }
-    }
+    });
     __syncthreads();
     find_bin(hist, krem, wsum, res);
     const uint32_t d = res[0];
@@ -478,12 +489,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
     // 2. compact the boundary bin into LDS (unordered)
     if (tid == 0) res[2] = 0;
     __syncthreads();
-    for (int base = 0; base < nC; base += STEP) {
-      const int c = base + 8 * tid;
-      uint32_t kv[8];
-      load8(keys, c, nC, kv);
+    pass16(keys, a.kstride, nC, [&](int c, const uint32_t* kv) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kKeysPerThread; ++q) {
         const bool match = c + q < nC && (kv[q] >> (32 - done)) == prefix;
         const uint64_t m = __builtin_amdgcn_ballot_w64(match);
         const int lane = tid & 63;
@@ -496,7 +504,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
           cidx[slot] = (uint32_t)(c + q);
         }
       }
-    }
+    });
     __syncthreads();
     const int n = (int)res[2];
     // 3. LDS passes over the remaining bits
@@ -550,26 +558,23 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
 
   // 4. ordered output
   uint32_t taken = 0, eq_seen = 0;
-  for (int base = 0; base < nC && taken < (uint32_t)keff; base += STEP) {
-    const int c = base + 8 * tid;
-    uint32_t kv[8];
-    load8(keys, c, nC, kv);
-    bool take[8];
+  pass16(keys, a.kstride, nC, [&](int c, const uint32_t* kv) {
+    bool take[kKeysPerThread];
     uint32_t nsel = 0;
     if (by_index) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kKeysPerThread; ++q) {
         take[q] = c + q < nC && (kv[q] > T || (kv[q] == T && (uint32_t)(c + q) <= c_last));
         nsel += take[q] ? 1u : 0u;
       }
     } else {
       uint32_t neq = 0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) neq += (c + q < nC && kv[q] == T) ? 1u : 0u;
+      for (int q = 0; q < kKeysPerThread; ++q) neq += (c + q < nC && kv[q] == T) ? 1u : 0u;
       uint32_t eq_tot;
       uint32_t eq_before = eq_seen + block_exscan(neq, wsum, &eq_tot);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kKeysPerThread; ++q) {
         const bool valid = c + q < nC;
         const bool eq = valid && kv[q] == T;
         take[q] = (valid && kv[q] > T) || (eq && eq_before < need_eq);
@@ -581,10 +586,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
     uint32_t sel_tot;
     uint32_t at = taken + block_exscan(nsel, wsum, &sel_tot);
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < kKeysPerThread; ++q)
       if (take[q] && at < (uint32_t)keff) out[at++] = lo + c + q;
     taken += sel_tot;
-  }
+  });
 }
 
 }  // namespace
@@ -615,22 +620,29 @@ SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len) {
 }
 
 size_t score_lds_bytes(int num_kv_heads, int num_q_heads, int nms_radius, int tile) {
-  return sizeof(float) * ((size_t)num_kv_heads * (tile + 2 * (size_t)nms_radius) +
-                          num_kv_heads + num_q_heads);
+  const size_t W = (size_t)tile + 2 * (size_t)score_pad(nms_radius);
+  return sizeof(float) * ((size_t)(num_q_heads + 2 * num_kv_heads) * W + num_kv_heads +
+                          num_q_heads);
+}
+
+int score_tile(int num_kv_heads, int num_q_heads, int nms_radius) {
+  for (int tile = 256; tile >= 64; tile /= 2)
+    if (score_lds_bytes(num_kv_heads, num_q_heads, nms_radius, tile) <= kScoreLdsLimit)
+      return tile;
+  return 0;
 }
 
 namespace {
 
-template <int PPT>
-void launch_score_g(const ScoreArgs& a, int n_seqs, size_t lds, hipStream_t st) {
+void launch_score(const ScoreArgs& a, int n_seqs, size_t lds, hipStream_t st) {
   const dim3 grid(n_seqs * a.ntile), block(256);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((k_sel_score<1, PPT>), grid, block, lds, st, a); break;
-    case 2: hipLaunchKernelGGL((k_sel_score<2, PPT>), grid, block, lds, st, a); break;
-    case 4: hipLaunchKernelGGL((k_sel_score<4, PPT>), grid, block, lds, st, a); break;
-    case 8: hipLaunchKernelGGL((k_sel_score<8, PPT>), grid, block, lds, st, a); break;
-    case 16: hipLaunchKernelGGL((k_sel_score<16, PPT>), grid, block, lds, st, a); break;
-    default: hipLaunchKernelGGL((k_sel_score<0, PPT>), grid, block, lds, st, a); break;
+    case 1: hipLaunchKernelGGL((k_sel_score<1>), grid, block, lds, st, a); break;
+    case 2: hipLaunchKernelGGL((k_sel_score<2>), grid, block, lds, st, a); break;
+    case 4: hipLaunchKernelGGL((k_sel_score<4>), grid, block, lds, st, a); break;
+    case 8: hipLaunchKernelGGL((k_sel_score<8>), grid, block, lds, st, a); break;
+    case 16: hipLaunchKernelGGL((k_sel_score<16>), grid, block, lds, st, a); break;
+    default: hipLaunchKernelGGL((k_sel_score<0>), grid, block, lds, st, a); break;
   }
 }
 
@@ -670,15 +682,9 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm, const
   a.lam = prm.lambda;
   a.a_soft = prm.alpha_soft;
   a.a_cross = prm.alpha_cross;
-  // Wide tiles when their LDS fits, narrow ones otherwise.
-  const size_t wide = score_lds_bytes(Hkv, Hq, prm.nms_radius, 1024);
-  if (wide <= kScoreLdsLimit) {
-    a.ntile = (max_seq_len + 1023) / 1024;
-    launch_score_g<4>(a, n_seqs, wide, st);
-  } else {
-    a.ntile = (max_seq_len + 255) / 256;
-    launch_score_g<1>(a, n_seqs, score_lds_bytes(Hkv, Hq, prm.nms_radius, 256), st);
-  }
+  a.tile = score_tile(Hkv, Hq, prm.nms_radius);
+  a.ntile = (max_seq_len + a.tile - 1) / a.tile;
+  launch_score(a, n_seqs, score_lds_bytes(Hkv, Hq, prm.nms_radius, a.tile), st);
   TopkArgs t;
   t.keys = keys;
   t.kstride = L.kstride;
