@@ -148,6 +148,7 @@ int sfi_slow_attn(const sfi_shape* shape, const float* q, const void* k_cache,
  *             position), ascending, then -1 up to top_k.
  * logits/lse come from sfi_slow_attn of the same step.  When dbg_scores is not NULL it
  * receives s as f32 [batch, Hkv, logits_stride] for j < N_b.
+ * max_seq_len <= 4194304 (SFI_E_UNSUPPORTED beyond).
  * ws: sfi_select_ws(shape, params, n_seqs, max_seq_len) bytes.
  */
 int sfi_select(const sfi_shape* shape, const sfi_select_params* params, const float* logits,

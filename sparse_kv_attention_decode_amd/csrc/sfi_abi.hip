@@ -89,7 +89,7 @@ size_t sfi_fast_attn_ws(const sfi_shape* shape, int32_t n_seqs, int32_t packed_c
 size_t sfi_select_ws(const sfi_shape* shape, const sfi_select_params* params, int32_t n_seqs,
                      int32_t max_seq_len) {
   if (check_shape(shape) != SFI_OK || check_params(params) != SFI_OK ||
-      check_rows(shape, n_seqs, max_seq_len) != SFI_OK)
+      check_rows(shape, n_seqs, max_seq_len) != SFI_OK || max_seq_len > sfi::kSelectMaxLen)
     return 0;
   return sfi::select_layout(*shape, n_seqs, max_seq_len).total;
 }
@@ -175,7 +175,7 @@ int sfi_select(const sfi_shape* shape, const sfi_select_params* params, const fl
   if (logits_stride % 4 != 0 || norm_stride % 4 != 0) return SFI_E_ALIGN;
   if (!aligned16(logits) || !aligned16(key_norm) || (dbg_scores && !aligned16(dbg_scores)))
     return SFI_E_ALIGN;
-  if (params->nms_radius > 1024) return SFI_E_UNSUPPORTED;
+  if (params->nms_radius > 1024 || max_seq_len > sfi::kSelectMaxLen) return SFI_E_UNSUPPORTED;
   if (sfi::score_tile(shape->num_kv_heads, shape->num_q_heads, params->nms_radius) == 0)
     return SFI_E_UNSUPPORTED;
   const size_t need = sfi_select_ws(shape, params, n_seqs, max_seq_len);

@@ -22,10 +22,9 @@
 //                logits and norms staged in LDS, s computed there, then the refined score
 //                s' as an order-preserving uint32 key (s' >= 0, so its IEEE bits already
 //                order like the value).
-//   k_sel_topk   one 1024-thread block per (b, g): radix select of the K-th largest key
-//                (an 11-bit histogram pass over global memory, then LDS-resident passes
-//                over the boundary bin), then one ordered pass that writes every key
-//                above the threshold and the lowest-position ties.
+//   k_topk_*     radix select of the K-th largest key spread over slices of 4096
+//                candidates (histogram, boundary-bin gather, a one-block select on the
+//                gathered bin in LDS, ordered parallel write); see the top-K section.
 #include "sfi_device.h"
 #include "sfi_internal.h"
 
@@ -37,6 +36,8 @@ namespace {
 
 constexpr int kZChunk = 4096;
 constexpr int kCandCapBytes = 48 * 1024;
+constexpr int kTopkHistWords = 2048;  // global radix histogram per (row, KV head)
+constexpr int kTopkStateWords = 8;
 
 template <int BLOCK>
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -125,10 +126,17 @@ __global__ __launch_bounds__(256) void k_sel_zsum(const float* __restrict__ key_
                                                   int64_t norm_stride,
                                                   const int32_t* __restrict__ seq_lens,
                                                   const int32_t* __restrict__ seq_ids, int Hkv,
-                                                  int nchunk, float* __restrict__ zpart) {
+                                                  int nchunk, float* __restrict__ zpart,
+                                                  uint32_t* __restrict__ topk_hist,
+                                                  uint32_t* __restrict__ topk_state) {
   __shared__ float red[8];
   const int chunk = blockIdx.x % nchunk;
   const int ig = blockIdx.x / nchunk;
+  if (chunk == 0) {  // clear the top-K histogram and state of this (row, head)
+    uint32_t* h = topk_hist + (size_t)ig * kTopkHistWords;
+    for (int k = threadIdx.x; k < kTopkHistWords; k += 256) h[k] = 0;
+    if (threadIdx.x < kTopkStateWords) topk_state[(size_t)ig * kTopkStateWords + threadIdx.x] = 0;
+  }
   const int g = ig % Hkv, i = ig / Hkv;
   const int b = seq_ids[i];
   const int N = seq_lens[b];
@@ -305,23 +313,38 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
 }
 
 // ------------------------------------------------------------------------------- top-K
-// Radix selection of the K_eff-th largest refined key per (row, KV head), one 1024-thread
-// block each:
-//   1. 11-bit histogram passes over the keys in global memory, each restricted to the
-//      digits fixed so far, until the bin holding the K_eff-th key has at most kCandCap
-//      keys (usually after one pass);
-//   2. that bin's keys and candidate indices are compacted into LDS;
-//   3. the remaining bits are resolved with LDS-resident histogram passes, giving the
-//      exact threshold T and the number of keys equal to T still to take; the last of
-//      those ties (lowest positions first) is found by the same selection on the
-//      complemented candidate index;
-//   4. one ordered pass writes every candidate above T and the ties up to that index,
-//      ascending, with a block-wide prefix sum per chunk.
-// Every pass over global keys reads 16 keys per thread per chunk with the next chunk in
-// flight.
+// Radix selection of the K_eff-th largest refined key per (row, KV head), spread over the
+// chip in slices of 4096 candidates:
+//   k_topk_hist    per slice: LDS histogram of the top 11 key bits, flushed into a global
+//                  2048-bin histogram of the (row, head);
+//   k_topk_gather  per slice: locate the bin holding the K_eff-th key, count the slice's
+//                  keys above that bin and append the keys inside it, with their
+//                  candidate indices, to a short candidate list;
+//   k_topk_final   per (row, head), 1024 threads: resolve the remaining 21 bits on the
+//                  candidate list in LDS, giving the exact threshold T and the number of
+//                  keys equal to T still to take; the last of those ties (lowest
+//                  positions first) is found by the same selection on the complemented
+//                  candidate index; then the output offset of every slice.  If the bin
+//                  holds more keys than the list takes, a single-block path selects from
+//                  the keys in global memory instead and writes the result itself;
+//   k_topk_write   per slice: every key above T and the taken ties, ascending.
 constexpr int kTopkThreads = 1024;
-constexpr int kHistBins = 2048;
+constexpr int kSliceThreads = 256;
+constexpr int kKeysPerThread = 16;
+constexpr int kSlice = kSliceThreads * kKeysPerThread;  // candidates per slice
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+static_assert(kHistBins == kTopkHistWords, "global histogram size");
 constexpr int kCandCap = kCandCapBytes / 8;  // key + index per candidate
+constexpr int kMaxSlices = 1024;
+
+// Per-(row, head) state words.
+constexpr int kStCount = 0;  // candidates appended by k_topk_gather
+constexpr int kStMode = 1;   // kModeWrite: k_topk_write emits; kModeDone: already written
+constexpr int kStT = 2;      // threshold key
+constexpr int kStCLast = 3;  // last tie taken (candidate index)
+constexpr int kStWords = kTopkStateWords;
+constexpr uint32_t kModeWrite = 0, kModeDone = 1;
 
 __device__ __forceinline__ void hist_add(uint32_t* hist, int bin, bool active) {
   // Aggregate lanes that share the first active lane's bin into one LDS atomic; the rest
@@ -338,8 +361,11 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, int bin, bool active) {
   if (active) atomicAdd(&hist[bin], 1u);
 }
 
-// Exclusive prefix of v over the block (1024 threads); returns the block total in *tot.
+// Exclusive prefix of v over a block of BLOCK threads; the block total goes to *tot.
+// wsum holds BLOCK / 64 + 1 words.
+template <int BLOCK>
 __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uint32_t* tot) {
+  constexpr int NWV = BLOCK / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -350,52 +376,49 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uin
   if (lane == 63) wsum[wv] = x;
   __syncthreads();
   if (tid < 64) {
-    uint32_t w = tid < kTopkThreads / 64 ? wsum[tid] : 0u;
+    const uint32_t w = tid < NWV ? wsum[tid] : 0u;
     uint32_t s = w;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t y = __shfl_up(s, o);
       if (tid >= o) s += y;
     }
-    if (tid < kTopkThreads / 64) wsum[tid] = s - w;  // exclusive
-    if (tid == kTopkThreads / 64 - 1) wsum[16] = s;
+    if (tid < NWV) wsum[tid] = s - w;  // exclusive
+    if (tid == NWV - 1) wsum[NWV] = s;
   }
   __syncthreads();
   const uint32_t res = wsum[wv] + x - v;
-  *tot = wsum[16];
+  *tot = wsum[NWV];
   __syncthreads();
   return res;
 }
 
-// Bin of hist[0..2048) holding the krem-th largest counted element: thread t owns bins
-// 2047-2t and 2046-2t.  Writes (bin, count above the bin) to res[0..1].  All threads call.
+// Bin of hist[0..2048) holding the krem-th largest counted element; thread t owns the
+// 2048 / BLOCK bins just below 2048 - t * (2048 / BLOCK).  Writes (bin, count above the
+// bin) to res[0..1].  All threads call.
+template <int BLOCK>
 __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t krem, uint32_t* wsum,
                                          uint32_t* res) {
-  const int t = threadIdx.x;
-  const uint32_t hh = hist[kHistBins - 1 - 2 * t], hl = hist[kHistBins - 2 - 2 * t];
+  constexpr int BPT = kHistBins / BLOCK;
+  const int top = kHistBins - 1 - BPT * (int)threadIdx.x;
+  uint32_t h[BPT], sum = 0;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    h[k] = hist[top - k];
+    sum += h[k];
+  }
   uint32_t tot;
-  const uint32_t above = block_exscan(hh + hl, wsum, &tot);
-  if (above < krem && above + hh >= krem) {
-    res[0] = kHistBins - 1 - 2 * t;
-    res[1] = above;
-  } else if (above + hh < krem && above + hh + hl >= krem) {
-    res[0] = kHistBins - 2 - 2 * t;
-    res[1] = above + hh;
+  uint32_t above = block_exscan<BLOCK>(sum, wsum, &tot);
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    if (above < krem && above + h[k] >= krem) {
+      res[0] = top - k;
+      res[1] = above;
+    }
+    above += h[k];
   }
   __syncthreads();
 }
-
-struct TopkArgs {
-  const uint32_t* keys;
-  int64_t kstride;
-  const int32_t* seq_lens;
-  const int32_t* seq_ids;
-  int32_t* sel;
-  int Hkv, K, n_sink, n_recent;
-};
-
-constexpr int kKeysPerThread = 16;
-constexpr int kPassStep = kKeysPerThread * kTopkThreads;
 
 // keys[c .. c+16) as four 16-byte loads.  The read is clamped into the row
 // [0, kstride) (kstride is a multiple of 64), so it is issued unconditionally; entries at
@@ -413,56 +436,192 @@ __device__ __forceinline__ void load16(const uint32_t* keys, int64_t kstride, in
   }
 }
 
-// Visit keys [0, n) in chunks of 16 per thread; the next chunk is requested before the
-// current one is processed (two register buffers, unrolled so they swap roles without
-// copies).  f(c, kv) sees the keys at candidate indices c .. c+15 and is called by every
-// thread the same number of times (it may contain block barriers).
+// Visit keys [0, n) in chunks of 16 per thread (1024 threads); the next chunk is
+// requested before the current one is processed (two register buffers, unrolled so they
+// swap roles without copies).  f(c, kv) sees the keys at candidate indices c .. c+15 and
+// is called by every thread the same number of times (it may contain block barriers).
 template <typename F>
 __device__ __forceinline__ void pass16(const uint32_t* keys, int64_t kstride, int n, F&& f) {
+  constexpr int STEP = kKeysPerThread * kTopkThreads;
   const int off = kKeysPerThread * (int)threadIdx.x;
   uint32_t A[kKeysPerThread], B[kKeysPerThread];
   load16(keys, kstride, off, A);
-  for (int base = 0; base < n; base += 2 * kPassStep) {
-    load16(keys, kstride, base + kPassStep + off, B);
+  for (int base = 0; base < n; base += 2 * STEP) {
+    load16(keys, kstride, base + STEP + off, B);
     f(base + off, A);
-    if (base + kPassStep >= n) break;
-    load16(keys, kstride, base + 2 * kPassStep + off, A);
-    f(base + kPassStep + off, B);
+    if (base + STEP >= n) break;
+    load16(keys, kstride, base + 2 * STEP + off, A);
+    f(base + STEP + off, B);
   }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
+struct TopkArgs {
+  const uint32_t* keys;
+  int64_t kstride;
+  const int32_t* seq_lens;
+  const int32_t* seq_ids;
+  int32_t* sel;
+  uint32_t* hist;         // [n_seqs * Hkv][2048]
+  uint32_t* state;        // [n_seqs * Hkv][kStWords]
+  uint32_t* slice_above;  // [n_seqs * Hkv][nslice]
+  uint32_t* slice_off;    // [n_seqs * Hkv][nslice]
+  uint32_t* cand_key;     // [n_seqs * Hkv][kCandCap]
+  uint32_t* cand_idx;     // [n_seqs * Hkv][kCandCap]
+  int Hkv, K, n_sink, n_recent, nslice;
+};
+
+struct TopkRow {
+  int b, lo, nC, keff;
+};
+
+__device__ __forceinline__ TopkRow topk_row(const TopkArgs& a, int i) {
+  TopkRow r;
+  r.b = a.seq_ids[i];
+  const int N = a.seq_lens[r.b];
+  r.lo = a.n_sink;
+  const int hi = max(r.lo, N - a.n_recent);
+  r.nC = hi - r.lo;
+  r.keff = min(a.K, r.nC);
+  return r;
+}
+
+__global__ __launch_bounds__(kSliceThreads) void k_topk_hist(TopkArgs a) {
   __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t ckey[kCandCap];
-  __shared__ uint32_t cidx[kCandCap];
-  __shared__ uint32_t wsum[17];
+  const int tid = threadIdx.x;
+  const int sl = blockIdx.x % a.nslice;
+  const int ig = blockIdx.x / a.nslice;
+  const TopkRow row = topk_row(a, ig / a.Hkv);
+  const int c0 = sl * kSlice;
+  if (row.keff == 0 || row.keff == row.nC || c0 >= row.nC) return;  // block-uniform
+  for (int k = tid; k < kHistBins; k += kSliceThreads) hist[k] = 0;
+  __syncthreads();
+  const int c = c0 + kKeysPerThread * tid;
+  uint32_t kv[kKeysPerThread];
+  load16(a.keys + (size_t)ig * a.kstride, a.kstride, c, kv);
+#pragma unroll
+  for (int q = 0; q < kKeysPerThread; ++q)
+    hist_add(hist, kv[q] >> (32 - kHistBits), c + q < row.nC);
+  __syncthreads();
+  uint32_t* gh = a.hist + (size_t)ig * kHistBins;
+  for (int k = tid; k < kHistBins; k += kSliceThreads) {
+    const uint32_t h = hist[k];
+    if (h) atomicAdd(&gh[k], h);
+  }
+}
+
+__global__ __launch_bounds__(kSliceThreads) void k_topk_gather(TopkArgs a) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t wsum[kSliceThreads / 64 + 1];
   __shared__ uint32_t res[4];
   const int tid = threadIdx.x;
-  const int ig = blockIdx.x;
-  const int g = ig % a.Hkv, i = ig / a.Hkv;
-  const int b = a.seq_ids[i];
-  const int N = a.seq_lens[b];
-  const int lo = a.n_sink;
-  const int hi = max(lo, N - a.n_recent);
-  const int nC = hi - lo;
-  const int keff = min(a.K, nC);
-  int32_t* out = a.sel + ((size_t)b * a.Hkv + g) * a.K;
-  const uint32_t* keys = a.keys + (size_t)ig * a.kstride;
-  for (int k = keff + tid; k < a.K; k += kTopkThreads) out[k] = -1;
-  if (keff == 0) return;
-  if (keff == nC) {  // every candidate is taken
-    for (int k = tid; k < nC; k += kTopkThreads) out[k] = lo + k;
-    return;
+  const int sl = blockIdx.x % a.nslice;
+  const int ig = blockIdx.x / a.nslice;
+  const TopkRow row = topk_row(a, ig / a.Hkv);
+  const int c0 = sl * kSlice;
+  if (row.keff == 0 || row.keff == row.nC || c0 >= row.nC) return;  // block-uniform
+  const uint32_t* gh = a.hist + (size_t)ig * kHistBins;
+  for (int k = tid; k < kHistBins; k += kSliceThreads) hist[k] = gh[k];
+  __syncthreads();
+  find_bin<kSliceThreads>(hist, (uint32_t)row.keff, wsum, res);
+  const uint32_t d = res[0];
+  const bool list_ok = hist[d] <= (uint32_t)kCandCap;
+  const int c = c0 + kKeysPerThread * tid;
+  uint32_t kv[kKeysPerThread];
+  load16(a.keys + (size_t)ig * a.kstride, a.kstride, c, kv);
+  uint32_t n_above = 0, n_in = 0;
+#pragma unroll
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    const bool valid = c + q < row.nC;
+    const uint32_t bin = kv[q] >> (32 - kHistBits);
+    n_above += (valid && bin > d) ? 1u : 0u;
+    n_in += (valid && bin == d) ? 1u : 0u;
   }
-  // 1. global histogram passes
-  uint32_t prefix = 0, krem = (uint32_t)keff, cnt = 0;
-  int done = 0;  // resolved top bits
-  while (true) {
-    const int nb = min(11, 32 - done);
+  // One scan for both counts (each at most 4096 per block): above in the high half.
+  uint32_t tot;
+  const uint32_t pre = block_exscan<kSliceThreads>((n_above << 16) | n_in, wsum, &tot);
+  if (tid == 0) a.slice_above[(size_t)ig * a.nslice + sl] = tot >> 16;
+  if (list_ok) {
+    if (tid == 0) res[2] = atomicAdd(&a.state[(size_t)ig * kStWords + kStCount], tot & 0xffffu);
+    __syncthreads();
+    uint32_t slot = res[2] + (pre & 0xffffu);
+    uint32_t* ck = a.cand_key + (size_t)ig * kCandCap;
+    uint32_t* ci = a.cand_idx + (size_t)ig * kCandCap;
+#pragma unroll
+    for (int q = 0; q < kKeysPerThread; ++q) {
+      if (c + q < row.nC && (kv[q] >> (32 - kHistBits)) == d && slot < (uint32_t)kCandCap) {
+        ck[slot] = kv[q];
+        ci[slot] = (uint32_t)(c + q);
+        ++slot;
+      }
+    }
+  }
+}
+
+// Radix selection on the candidate list in LDS: resolves the key bits below `done` and
+// then the last tie by candidate index.  Returns T, need_eq and c_last.
+__device__ void select_in_lds(const uint32_t* ckey, const uint32_t* cidx, int n, uint32_t prefix,
+                              int done, uint32_t krem, uint32_t* hist, uint32_t* wsum,
+                              uint32_t* res, uint32_t& T, uint32_t& c_last) {
+  const int tid = threadIdx.x;
+  while (done < 32) {
+    const int nb = min(kHistBits, 32 - done);
     const int sh = 32 - done - nb;
     for (int k = tid; k < kHistBins; k += kTopkThreads) hist[k] = 0;
     __syncthreads();
-    pass16(keys, a.kstride, nC, [&](int c, const uint32_t* kv) {
+    for (int base = 0; base < n; base += kTopkThreads) {
+      const int e = base + tid;
+      const uint32_t key = e < n ? ckey[e] : 0u;
+      const bool match = e < n && (key >> (32 - done)) == prefix;
+      hist_add(hist, (key >> sh) & ((1u << nb) - 1u), match);
+    }
+    __syncthreads();
+    find_bin<kTopkThreads>(hist, krem, wsum, res);
+    krem -= res[1];
+    prefix = (prefix << nb) | res[0];
+    done += nb;
+    __syncthreads();
+  }
+  T = prefix;
+  // ties at T: the krem-th smallest candidate index is the last one taken
+  uint32_t uprefix = 0, urem = krem;
+  int udone = 0;
+  while (udone < 32) {
+    const int nb = min(kHistBits, 32 - udone);
+    const int sh = 32 - udone - nb;
+    for (int k = tid; k < kHistBins; k += kTopkThreads) hist[k] = 0;
+    __syncthreads();
+    for (int base = 0; base < n; base += kTopkThreads) {
+      const int e = base + tid;
+      const bool tie = e < n && ckey[e] == T;
+      const uint32_t u = tie ? ~cidx[e] : 0u;
+      const bool match = tie && (udone == 0 || (u >> (32 - udone)) == uprefix);
+      hist_add(hist, (u >> sh) & ((1u << nb) - 1u), match);
+    }
+    __syncthreads();
+    find_bin<kTopkThreads>(hist, urem, wsum, res);
+    urem -= res[1];
+    uprefix = (uprefix << nb) | res[0];
+    udone += nb;
+    __syncthreads();
+  }
+  c_last = ~uprefix;
+}
+
+// Whole selection of one (row, head) by one block from the keys in global memory; the
+// path for a boundary bin larger than the candidate list (massive ties, very flat
+// scores).  Writes out[0 .. keff).
+__device__ void topk_single_block(const uint32_t* keys, int64_t kstride, int nC, int keff,
+                                  int lo, int32_t* out, uint32_t* hist, uint32_t* ckey,
+                                  uint32_t* cidx, uint32_t* wsum, uint32_t* res) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, krem = (uint32_t)keff, cnt = 0;
+  int done = 0;
+  while (true) {
+    const int nb = min(kHistBits, 32 - done);
+    const int sh = 32 - done - nb;
+    for (int k = tid; k < kHistBins; k += kTopkThreads) hist[k] = 0;
+    __syncthreads();
+    pass16(keys, kstride, nC, [&](int c, const uint32_t* kv) {
 #pragma unroll
       for (int q = 0; q < kKeysPerThread; ++q) {
         const bool match = c + q < nC && (done == 0 || (kv[q] >> (32 - done)) == prefix);
@@ -470,7 +629,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
       }
     });
     __syncthreads();
-    find_bin(hist, krem, wsum, res);
+    find_bin<kTopkThreads>(hist, krem, wsum, res);
     const uint32_t d = res[0];
     krem -= res[1];
     cnt = hist[d];
@@ -479,17 +638,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
     __syncthreads();
     if (cnt <= (uint32_t)kCandCap || done == 32) break;
   }
-
-  uint32_t T, need_eq, c_last = 0xffffffffu;
+  uint32_t T, need_eq = krem, c_last = 0xffffffffu;
   bool by_index = false;
   if (done == 32) {
     T = prefix;
-    need_eq = krem;
   } else {
-    // 2. compact the boundary bin into LDS (unordered)
     if (tid == 0) res[2] = 0;
     __syncthreads();
-    pass16(keys, a.kstride, nC, [&](int c, const uint32_t* kv) {
+    pass16(keys, kstride, nC, [&](int c, const uint32_t* kv) {
 #pragma unroll
       for (int q = 0; q < kKeysPerThread; ++q) {
         const bool match = c + q < nC && (kv[q] >> (32 - done)) == prefix;
@@ -506,59 +662,11 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
       }
     });
     __syncthreads();
-    const int n = (int)res[2];
-    // 3. LDS passes over the remaining bits
-    while (done < 32) {
-      const int nb = min(11, 32 - done);
-      const int sh = 32 - done - nb;
-      for (int k = tid; k < kHistBins; k += kTopkThreads) hist[k] = 0;
-      __syncthreads();
-      for (int base = 0; base < n; base += kTopkThreads) {
-        const int e = base + tid;
-        const uint32_t key = e < n ? ckey[e] : 0u;
-        const bool match = e < n && (key >> (32 - done)) == prefix;
-        hist_add(hist, (key >> sh) & ((1u << nb) - 1u), match);
-      }
-      __syncthreads();
-      find_bin(hist, krem, wsum, res);
-      krem -= res[1];
-      prefix = (prefix << nb) | res[0];
-      done += nb;
-      __syncthreads();
-    }
-    T = prefix;
-    need_eq = krem;
-    // ties at T: the need_eq-th smallest candidate index is the last one taken
-    {
-      uint32_t uprefix = 0, urem = need_eq;
-      int udone = 0;
-      while (udone < 32) {
-        const int nb = min(11, 32 - udone);
-        const int sh = 32 - udone - nb;
-        for (int k = tid; k < kHistBins; k += kTopkThreads) hist[k] = 0;
-        __syncthreads();
-        for (int base = 0; base < n; base += kTopkThreads) {
-          const int e = base + tid;
-          const bool tie = e < n && ckey[e] == T;
-          const uint32_t u = tie ? ~cidx[e] : 0u;
-          const bool match = tie && (udone == 0 || (u >> (32 - udone)) == uprefix);
-          hist_add(hist, (u >> sh) & ((1u << nb) - 1u), match);
-        }
-        __syncthreads();
-        find_bin(hist, urem, wsum, res);
-        urem -= res[1];
-        uprefix = (uprefix << nb) | res[0];
-        udone += nb;
-        __syncthreads();
-      }
-      c_last = ~uprefix;
-      by_index = true;
-    }
+    select_in_lds(ckey, cidx, (int)res[2], prefix, done, krem, hist, wsum, res, T, c_last);
+    by_index = true;
   }
-
-  // 4. ordered output
   uint32_t taken = 0, eq_seen = 0;
-  pass16(keys, a.kstride, nC, [&](int c, const uint32_t* kv) {
+  pass16(keys, kstride, nC, [&](int c, const uint32_t* kv) {
     bool take[kKeysPerThread];
     uint32_t nsel = 0;
     if (by_index) {
@@ -572,7 +680,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
 #pragma unroll
       for (int q = 0; q < kKeysPerThread; ++q) neq += (c + q < nC && kv[q] == T) ? 1u : 0u;
       uint32_t eq_tot;
-      uint32_t eq_before = eq_seen + block_exscan(neq, wsum, &eq_tot);
+      uint32_t eq_before = eq_seen + block_exscan<kTopkThreads>(neq, wsum, &eq_tot);
 #pragma unroll
       for (int q = 0; q < kKeysPerThread; ++q) {
         const bool valid = c + q < nC;
@@ -584,12 +692,106 @@ __global__ __launch_bounds__(kTopkThreads) void k_sel_topk(TopkArgs a) {
       eq_seen += eq_tot;
     }
     uint32_t sel_tot;
-    uint32_t at = taken + block_exscan(nsel, wsum, &sel_tot);
+    uint32_t at = taken + block_exscan<kTopkThreads>(nsel, wsum, &sel_tot);
 #pragma unroll
     for (int q = 0; q < kKeysPerThread; ++q)
       if (take[q] && at < (uint32_t)keff) out[at++] = lo + c + q;
     taken += sel_tot;
   });
+}
+
+__global__ __launch_bounds__(kTopkThreads) void k_topk_final(TopkArgs a) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t ckey[kCandCap];
+  __shared__ uint32_t cidx[kCandCap];
+  __shared__ uint32_t cnt_sl[kMaxSlices];
+  __shared__ uint32_t wsum[kTopkThreads / 64 + 1];
+  __shared__ uint32_t res[4];
+  const int tid = threadIdx.x;
+  const int ig = blockIdx.x;
+  const TopkRow row = topk_row(a, ig / a.Hkv);
+  const int g = ig % a.Hkv;
+  int32_t* out = a.sel + ((size_t)row.b * a.Hkv + g) * a.K;
+  uint32_t* st = a.state + (size_t)ig * kStWords;
+  for (int k = row.keff + tid; k < a.K; k += kTopkThreads) out[k] = -1;
+  if (row.keff == 0 || row.keff == row.nC) {  // nothing to rank: none or every candidate
+    for (int k = tid; k < row.keff; k += kTopkThreads) out[k] = row.lo + k;
+    if (tid == 0) st[kStMode] = kModeDone;
+    return;
+  }
+  const uint32_t* gh = a.hist + (size_t)ig * kHistBins;
+  for (int k = tid; k < kHistBins; k += kTopkThreads) hist[k] = gh[k];
+  __syncthreads();
+  find_bin<kTopkThreads>(hist, (uint32_t)row.keff, wsum, res);
+  const uint32_t d = res[0];
+  const uint32_t krem = (uint32_t)row.keff - res[1];
+  const uint32_t cnt = hist[d];
+  __syncthreads();
+  const uint32_t* keys = a.keys + (size_t)ig * a.kstride;
+  if (cnt > (uint32_t)kCandCap) {
+    topk_single_block(keys, a.kstride, row.nC, row.keff, row.lo, out, hist, ckey, cidx, wsum,
+                      res);
+    if (tid == 0) st[kStMode] = kModeDone;
+    return;
+  }
+  const int n = (int)cnt;
+  const uint32_t* gk = a.cand_key + (size_t)ig * kCandCap;
+  const uint32_t* gi = a.cand_idx + (size_t)ig * kCandCap;
+  for (int e = tid; e < n; e += kTopkThreads) {
+    ckey[e] = gk[e];
+    cidx[e] = gi[e];
+  }
+  __syncthreads();
+  uint32_t T, c_last;
+  select_in_lds(ckey, cidx, n, d, kHistBits, krem, hist, wsum, res, T, c_last);
+  // Selected count of every slice: keys above the bin plus the taken candidates.
+  const int nsl = (row.nC + kSlice - 1) / kSlice;
+  const uint32_t* above = a.slice_above + (size_t)ig * a.nslice;
+  for (int k = tid; k < nsl; k += kTopkThreads) cnt_sl[k] = above[k];
+  __syncthreads();
+  for (int e = tid; e < n; e += kTopkThreads) {
+    const uint32_t key = ckey[e], idx = cidx[e];
+    if (key > T || (key == T && idx <= c_last)) atomicAdd(&cnt_sl[idx / kSlice], 1u);
+  }
+  __syncthreads();
+  uint32_t tot;
+  const uint32_t off = block_exscan<kTopkThreads>(tid < nsl ? cnt_sl[tid] : 0u, wsum, &tot);
+  if (tid < nsl) a.slice_off[(size_t)ig * a.nslice + tid] = off;
+  if (tid == 0) {
+    st[kStT] = T;
+    st[kStCLast] = c_last;
+    st[kStMode] = kModeWrite;
+  }
+}
+
+__global__ __launch_bounds__(kSliceThreads) void k_topk_write(TopkArgs a) {
+  __shared__ uint32_t wsum[kSliceThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  const int sl = blockIdx.x % a.nslice;
+  const int ig = blockIdx.x / a.nslice;
+  const TopkRow row = topk_row(a, ig / a.Hkv);
+  const int c0 = sl * kSlice;
+  if (row.keff == 0 || row.keff == row.nC || c0 >= row.nC) return;  // block-uniform
+  const uint32_t* st = a.state + (size_t)ig * kStWords;
+  if (st[kStMode] != kModeWrite) return;
+  const uint32_t T = st[kStT], c_last = st[kStCLast];
+  const int c = c0 + kKeysPerThread * tid;
+  uint32_t kv[kKeysPerThread];
+  load16(a.keys + (size_t)ig * a.kstride, a.kstride, c, kv);
+  bool take[kKeysPerThread];
+  uint32_t nsel = 0;
+#pragma unroll
+  for (int q = 0; q < kKeysPerThread; ++q) {
+    take[q] = c + q < row.nC && (kv[q] > T || (kv[q] == T && (uint32_t)(c + q) <= c_last));
+    nsel += take[q] ? 1u : 0u;
+  }
+  uint32_t tot;
+  uint32_t at = a.slice_off[(size_t)ig * a.nslice + sl] +
+                block_exscan<kSliceThreads>(nsel, wsum, &tot);
+  int32_t* out = a.sel + ((size_t)row.b * a.Hkv + ig % a.Hkv) * a.K;
+#pragma unroll
+  for (int q = 0; q < kKeysPerThread; ++q)
+    if (take[q] && at < (uint32_t)row.keff) out[at++] = row.lo + c + q;
 }
 
 }  // namespace
@@ -611,11 +813,23 @@ SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len) {
   SelectLayout L;
   L.nchunk = (max_seq_len + kZChunk - 1) / kZChunk;
   L.kstride = ((int64_t)max_seq_len + 63) / 64 * 64;
+  L.nslice = (max_seq_len + kSlice - 1) / kSlice;
   const size_t units = (size_t)n_seqs * s.num_kv_heads;
-  L.zpart_off = 0;
-  const size_t zbytes = ((units * L.nchunk * sizeof(float) + 255) / 256) * 256;
-  L.keys_off = zbytes;
-  L.total = zbytes + units * (size_t)L.kstride * sizeof(uint32_t);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  L.zpart_off = take(units * L.nchunk * sizeof(float));
+  L.keys_off = take(units * (size_t)L.kstride * sizeof(uint32_t));
+  L.hist_off = take(units * kHistBins * sizeof(uint32_t));
+  L.state_off = take(units * kStWords * sizeof(uint32_t));
+  L.above_off = take(units * L.nslice * sizeof(uint32_t));
+  L.sloff_off = take(units * L.nslice * sizeof(uint32_t));
+  L.ckey_off = take(units * kCandCap * sizeof(uint32_t));
+  L.cidx_off = take(units * kCandCap * sizeof(uint32_t));
+  L.total = off;
   return L;
 }
 
@@ -659,7 +873,9 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm, const
   uint32_t* keys = reinterpret_cast<uint32_t*>(w + L.keys_off);
   const int Hkv = s.num_kv_heads, Hq = s.num_q_heads;
   hipLaunchKernelGGL(k_sel_zsum, dim3(n_seqs * Hkv * L.nchunk), dim3(256), 0, st, key_norm,
-                     norm_stride, seq_lens, seq_ids, Hkv, L.nchunk, zpart);
+                     norm_stride, seq_lens, seq_ids, Hkv, L.nchunk, zpart,
+                     reinterpret_cast<uint32_t*>(w + L.hist_off),
+                     reinterpret_cast<uint32_t*>(w + L.state_off));
   ScoreArgs a;
   a.logits = logits;
   a.logits_stride = logits_stride;
@@ -691,11 +907,22 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm, const
   t.seq_lens = seq_lens;
   t.seq_ids = seq_ids;
   t.sel = sel_idx;
+  t.hist = reinterpret_cast<uint32_t*>(w + L.hist_off);
+  t.state = reinterpret_cast<uint32_t*>(w + L.state_off);
+  t.slice_above = reinterpret_cast<uint32_t*>(w + L.above_off);
+  t.slice_off = reinterpret_cast<uint32_t*>(w + L.sloff_off);
+  t.cand_key = reinterpret_cast<uint32_t*>(w + L.ckey_off);
+  t.cand_idx = reinterpret_cast<uint32_t*>(w + L.cidx_off);
   t.Hkv = Hkv;
   t.K = prm.top_k;
   t.n_sink = prm.n_sink;
   t.n_recent = prm.n_recent;
-  hipLaunchKernelGGL(k_sel_topk, dim3(n_seqs * Hkv), dim3(kTopkThreads), 0, st, t);
+  t.nslice = L.nslice;
+  const dim3 slices(n_seqs * Hkv * L.nslice);
+  hipLaunchKernelGGL(k_topk_hist, slices, dim3(kSliceThreads), 0, st, t);
+  hipLaunchKernelGGL(k_topk_gather, slices, dim3(kSliceThreads), 0, st, t);
+  hipLaunchKernelGGL(k_topk_final, dim3(n_seqs * Hkv), dim3(kTopkThreads), 0, st, t);
+  hipLaunchKernelGGL(k_topk_write, slices, dim3(kSliceThreads), 0, st, t);
   return hipGetLastError();
 }
 
