@@ -496,8 +496,6 @@ __global__ __launch_bounds__(64) void k_attn_partial_f32(AttnParams p) {
 }
 
 // One block per (listed row, query head): log-sum-exp merge of the split partials.
-// Split weights exp(m_s - M) are staged in LDS; thread (grp, col) accumulates float4
-// column `col` of o over the splits s = grp (mod groups), then the groups are summed.
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm,
                                                     const float* __restrict__ pl,
                                                     const float* __restrict__ po, int nsplit,
@@ -505,9 +503,11 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm
                                                     const int32_t* __restrict__ seq_ids,
                                                     float* __restrict__ out,
                                                     float* __restrict__ lse) {
-  constexpr int kChunk = 1024;
-  __shared__ float wts[kChunk];
-  __shared__ float red[8];
+  // Thread (grp, col) folds splits grp, grp + ngrp, ... of column block col into a running
+  // (max, sum, weighted o); the loads of kUnroll splits are issued together.  The groups
+  // are then combined in LDS.
+  constexpr int kUnroll = 4;
+  __shared__ float gm[64], gl[64];
   __shared__ float4 acc4[256];
   const int tid = threadIdx.x;
   const int i = blockIdx.x / Hq;
@@ -515,58 +515,62 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm
   const int g = h / G, hh = h % G;
   const int b = seq_ids[i];
   const size_t base = ((size_t)i * Hkv + g) * nsplit;
-
-  float mx = -INFINITY;
-  for (int s = tid; s < nsplit; s += 256) mx = fmaxf(mx, pm[(base + s) * G + hh]);
-  mx = wave_max_xor(mx, kWave);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  __syncthreads();
-
   const int cols = D / 4;
   const int ngrp = 256 / cols;
   const int col = tid % cols, grp = tid / cols;
   const float4* po4 = reinterpret_cast<const float4*>(po);
+  float mt = -INFINITY, lt = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float L = 0.f;
-  for (int c0 = 0; c0 < nsplit; c0 += kChunk) {
-    const int n = min(kChunk, nsplit - c0);
-    for (int s = tid; s < n; s += 256) {
-      const size_t u = (base + c0 + s) * G + hh;
-      const float m = pm[u];
-      const float w = (m == -INFINITY) ? 0.f : __expf(m - Mu);
-      wts[s] = w;
-      L += w * pl[u];
+  for (int s0 = grp; s0 < nsplit; s0 += kUnroll * ngrp) {
+    float m[kUnroll], l[kUnroll];
+    float4 v[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int s = s0 + k * ngrp;
+      const size_t u = (base + min(s, nsplit - 1)) * G + hh;
+      m[k] = s < nsplit ? pm[u] : -INFINITY;
+      l[k] = pl[u];
+      v[k] = po4[u * cols + col];
     }
-    __syncthreads();
-    for (int s = grp; s < n; s += ngrp) {
-      const float w = wts[s];
-      const float4 v = po4[((base + c0 + s) * G + hh) * cols + col];
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      if (m[k] == -INFINITY) continue;  // empty split (or past the end): weight 0
+      const float mn = fmaxf(mt, m[k]);
+      const float co = __expf(mt - mn);  // 0 while mt is -inf
+      const float cn = __expf(m[k] - mn);
+      lt = lt * co + l[k] * cn;
+      acc.x = acc.x * co + v[k].x * cn;
+      acc.y = acc.y * co + v[k].y * cn;
+      acc.z = acc.z * co + v[k].z * cn;
+      acc.w = acc.w * co + v[k].w * cn;
+      mt = mn;
     }
-    __syncthreads();
   }
-  L = wave_sum_xor(L, kWave);
-  if ((tid & 63) == 0) red[4 + (tid >> 6)] = L;
+  if (col == 0) {
+    gm[grp] = mt;
+    gl[grp] = lt;
+  }
   acc4[tid] = acc;
   __syncthreads();
   if (grp == 0) {
-    const float Lt = (red[4] + red[5]) + (red[6] + red[7]);
-    for (int q = 1; q < ngrp; ++q) {
-      const float4 v = acc4[q * cols + col];
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+    float M = -INFINITY;
+    for (int q = 0; q < ngrp; ++q) M = fmaxf(M, gm[q]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float Lt = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < ngrp; ++q) {
+      if (gm[q] == -INFINITY) continue;
+      const float w = __expf(gm[q] - Mu);
+      const float4 x = acc4[q * cols + col];
+      Lt += w * gl[q];
+      o.x += w * x.x;
+      o.y += w * x.y;
+      o.z += w * x.z;
+      o.w += w * x.w;
     }
     const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
     reinterpret_cast<float4*>(out + ((size_t)b * Hq + h) * D)[col] =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
     if (col == 0 && lse) lse[(size_t)b * Hq + h] = Lt > 0.f ? Mu + logf(Lt) : -INFINITY;
   }
 }

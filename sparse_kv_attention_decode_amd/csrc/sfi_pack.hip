@@ -3,9 +3,12 @@
 // them sequentially instead of gathering scattered pages (zh "2.3 显存合并的内核",
 // nl "Memory-Coalesced Kernel", fr "2.C Kernels Mémoire-Coalescés").
 //
-// One wavefront per group of 16 packed rows: the four lanes l = 4 r .. 4 r + 3 copy row r
-// of K and V, 64 contiguous bytes per step.  Packed row i holds position packed_pos[i] = i for i < n_sink and
-// sel_idx[i - n_sink] after; rows without a position are zero-filled.
+// Each wavefront moves a run of consecutive packed rows.  The lanes first look up one row
+// each (selected position, then its page), then every load instruction covers whole rows
+// with consecutive lanes on consecutive 16-byte words: LPR = row bytes / 16 lanes per row,
+// 64 / LPR rows per instruction, eight instructions per wavefront for K and eight for V,
+// all issued before any store.  Packed row i holds position packed_pos[i] = i for
+// i < n_sink and sel_idx[i - n_sink] after; rows without a position are zero-filled.
 #include "sfi_device.h"
 #include "sfi_internal.h"
 
@@ -32,57 +35,61 @@ __device__ __forceinline__ int packed_source(const PackArgs& a, const int32_t* s
   return k < a.K ? selrow[k] : -1;
 }
 
-__global__ __launch_bounds__(64) void k_pack(PackArgs a) {
-  const int lane = threadIdx.x;
-  const int ngrp = a.cap / kPage;
-  const int grp = blockIdx.x % ngrp;
-  const int ig = blockIdx.x / ngrp;
+constexpr int kPackInstr = 8;   // load instructions per wavefront and tensor
+constexpr int kPackWaves = 4;   // wavefronts per block
+
+template <int LPR>
+__global__ __launch_bounds__(64 * kPackWaves) void k_pack(PackArgs a) {
+  constexpr int RPI = 64 / LPR;          // rows per load instruction
+  constexpr int RW = kPackInstr * RPI;   // rows per wavefront
+  constexpr int RB = kPackWaves * RW;    // rows per block
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nblk = (a.cap + RB - 1) / RB;
+  const int blk = blockIdx.x % nblk;
+  const int ig = blockIdx.x / nblk;
   const int g = ig % a.Hkv, i = ig / a.Hkv;
   const int b = a.seq_ids[i];
   const size_t bg = (size_t)b * a.Hkv + g;
   const int32_t* selrow = a.sel + bg * a.K;
-  const int row = grp * kPage + lane / 4;
-  const int quarter = lane % 4;
-  const int pos = packed_source(a, selrow, row);
-  // The four lanes of a row copy 64 contiguous bytes per step.
-  uint8_t* dk = a.pk + (bg * a.cap + row) * a.row_bytes + quarter * 16;
-  uint8_t* dv = a.pv + (bg * a.cap + row) * a.row_bytes + quarter * 16;
-  if (pos >= 0) {
-    const int page = a.bt[(size_t)b * a.max_pages + pos / kPage];
-    const size_t src = (((size_t)page * a.Hkv + g) * kPage + pos % kPage) * a.row_bytes +
-                       quarter * 16;
-    // All loads of the row first, then all stores (rows are at most 512 bytes).
-    constexpr int kMaxSteps = 8;
-    const int steps = a.row_bytes / 64;
-    u32x4_t kv[kMaxSteps], vv[kMaxSteps];
-#pragma unroll
-    for (int k = 0; k < kMaxSteps; ++k) {
-      if (k < steps) {
-        kv[k] = *reinterpret_cast<const u32x4_t*>(a.kc + src + 64 * k);
-        vv[k] = *reinterpret_cast<const u32x4_t*>(a.vc + src + 64 * k);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kMaxSteps; ++k) {
-      if (k < steps) {
-        *reinterpret_cast<u32x4_t*>(dk + 64 * k) = kv[k];
-        *reinterpret_cast<u32x4_t*>(dv + 64 * k) = vv[k];
-      }
-    }
-  } else {
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    for (int o = 0; o < a.row_bytes; o += 64) {
-      *reinterpret_cast<u32x4_t*>(dk + o) = zero;
-      *reinterpret_cast<u32x4_t*>(dv + o) = zero;
-    }
+  const int row0 = blk * RB + wv * RW;
+  if (row0 >= a.cap) return;  // wavefront-uniform; the kernel has no block barrier
+  // Lane r < RW resolves row row0 + r: its position and page.
+  const int my_row = row0 + lane;
+  const bool own = lane < RW && my_row < a.cap;
+  const int pos = own ? packed_source(a, selrow, my_row) : -1;
+  const int page = pos >= 0 ? a.bt[(size_t)b * a.max_pages + pos / kPage] : 0;
+  if (own) {
+    a.ppos[bg * a.cap + my_row] = pos;
+    // Valid rows form a prefix: the last valid row (or row 0 when none is valid) records
+    // the packed length.
+    const int next = my_row + 1 < a.cap ? packed_source(a, selrow, my_row + 1) : -1;
+    if (pos >= 0 && next < 0) a.plen[bg] = my_row + 1;
+    if (my_row == 0 && pos < 0) a.plen[bg] = 0;
   }
-  if (quarter == 0) {
-    a.ppos[bg * a.cap + row] = pos;
-    // Valid rows form a prefix: the last valid row (or group 0 when none is valid)
-    // records the packed length.
-    const int next = row + 1 < a.cap ? packed_source(a, selrow, row + 1) : -1;
-    if (pos >= 0 && next < 0) a.plen[bg] = row + 1;
-    if (row == 0 && pos < 0) a.plen[bg] = 0;
+  const int sub = lane % LPR, rsub = lane / LPR;
+  const size_t rb = (size_t)a.row_bytes;
+  u32x4_t kv[kPackInstr], vv[kPackInstr];
+  bool valid[kPackInstr];
+#pragma unroll
+  for (int j = 0; j < kPackInstr; ++j) {
+    const int r = j * RPI + rsub;
+    const int pr = __shfl(pos, r), pg = __shfl(page, r);
+    valid[j] = pr >= 0;
+    // Rows without a position read row 0 of page 0 (always present) and store zeros.
+    const size_t src = valid[j] ? (((size_t)pg * a.Hkv + g) * kPage + pr % kPage) * rb : 0;
+    kv[j] = *reinterpret_cast<const u32x4_t*>(a.kc + src + 16 * sub);
+    vv[j] = *reinterpret_cast<const u32x4_t*>(a.vc + src + 16 * sub);
+  }
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < kPackInstr; ++j) {
+    const int row = row0 + j * RPI + rsub;
+    if (row < a.cap) {
+      const size_t dst = (bg * a.cap + row) * rb + 16 * sub;
+      *reinterpret_cast<u32x4_t*>(a.pk + dst) = valid[j] ? kv[j] : zero;
+      *reinterpret_cast<u32x4_t*>(a.pv + dst) = valid[j] ? vv[j] : zero;
+    }
   }
 }
 
@@ -109,8 +116,16 @@ hipError_t launch_pack(const sfi_shape& s, const sfi_select_params& prm, const v
   a.n_sink = prm.n_sink;
   a.cap = packed_cap;
   a.row_bytes = s.head_dim * (s.dtype == SFI_BF16 ? 2 : 4);
-  const int blocks = n_seqs * s.num_kv_heads * (packed_cap / kPage);
-  hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(64), 0, stream, a);
+  const dim3 block(64 * kPackWaves);
+  auto grid = [&](int lpr) {
+    const int rb = kPackWaves * kPackInstr * (64 / lpr);
+    return dim3(n_seqs * s.num_kv_heads * ((packed_cap + rb - 1) / rb));
+  };
+  switch (a.row_bytes / 16) {
+    case 8: hipLaunchKernelGGL(k_pack<8>, grid(8), block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(k_pack<16>, grid(16), block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(k_pack<32>, grid(32), block, 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -563,6 +563,7 @@ __device__ void select_in_lds(const uint32_t* ckey, const uint32_t* cidx, int n,
                               int done, uint32_t krem, uint32_t* hist, uint32_t* wsum,
                               uint32_t* res, uint32_t& T, uint32_t& c_last) {
   const int tid = threadIdx.x;
+  uint32_t n_eq = 0;  // candidates equal to the prefix once all 32 bits are fixed
   while (done < 32) {
     const int nb = min(kHistBits, 32 - done);
     const int sh = 32 - done - nb;
@@ -577,11 +578,16 @@ __device__ void select_in_lds(const uint32_t* ckey, const uint32_t* cidx, int n,
     __syncthreads();
     find_bin<kTopkThreads>(hist, krem, wsum, res);
     krem -= res[1];
+    n_eq = hist[res[0]];
     prefix = (prefix << nb) | res[0];
     done += nb;
     __syncthreads();
   }
   T = prefix;
+  if (n_eq == krem) {  // every tie at T is taken
+    c_last = 0xffffffffu;
+    return;
+  }
   // ties at T: the krem-th smallest candidate index is the last one taken
   uint32_t uprefix = 0, urem = krem;
   int udone = 0;
