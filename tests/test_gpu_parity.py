@@ -217,7 +217,7 @@ def test_two_streams_bit_identical_to_one_stream():
 
 
 def test_fast_equals_dense_when_k_covers_candidates():
-    """spec invariant on the device: with K >= |C| every fast step equals the dense
+    """Invariant on the device: with K >= |C| every fast step equals the dense
     step (same positions, so equal up to fp32 rounding)."""
     w = get("qwen3_0p6b_8k").replace(steps=40, top_k=9000, context=2048)
     d, eng, lb = _setup(w)

@@ -319,7 +319,8 @@ def test_fast_two_segments_equal_single_pass():
 
 
 def test_fast_equals_dense_when_k_covers_candidates():
-    """spec invariant: with K >= |C| every fast step equals dense attention."""
+    """With K >= |C| every fast step equals dense attention: sink, selected memory and
+    recent segment then cover the whole history."""
     Hq, Hkv, D, ctx, S = 4, 2, 8, 60, 25
     r = np.random.default_rng(17)
     K = r.standard_normal((Hkv, ctx + S, D)) * 2
