@@ -9,9 +9,11 @@ tables) are resident in HBM before the timed region; the timed region issues exa
 
 Printed: one JSON line.  `value` is layer decode steps per second (steps x layers /
 seconds).  `roofline` covers the dominant call, the fast-step attention: algorithmic bytes
-(packed rows + recent window of K and V, q in, o out) over the time between HIP events
-recorded around each call on the stream it runs on.  `cpu_baseline` is the fp64 oracle on
-a bounded sample of the same workload on the host cores.
+(packed rows + recent window of K and V, q in, o out) over its average duration, from HIP
+events recorded on the stream it runs on around every fast-step graph replay (all layers'
+calls back to back; per call = replay time / layers), or around every n-th layer's call
+when graphs are off.  `cpu_baseline` is the fp64 oracle on a bounded sample of the same
+workload on the host cores.
 """
 from __future__ import annotations
 
@@ -42,12 +44,18 @@ def _parse():
     ap.add_argument("--time-every", type=int, default=9,
                     help="bracket the attention calls of every n-th layer with HIP events "
                          "(0: none)")
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="issue fast steps call by call instead of replaying the captured "
+                         "fast-step graph")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue the Selector and pack on the attention stream")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a device copy of known size (for counter calibration)")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="HBM traffic per fast call measured with counters (optional)")
+    ap.add_argument("--traffic-json",
+                    default=os.path.join(ROOT, "profiles",
+                                         "fast_attn_traffic_qwen3_4b_128k_36l.json"),
+                    help="HBM traffic per fast call measured with counters; used only when "
+                         "its workload and attention-kernel source hash match this run")
     return ap.parse_args()
 
 
@@ -140,6 +148,8 @@ def main():
         if layer % 6 == 5 or layer == w.layers - 1:
             print(f"[bench] layer {layer + 1}/{w.layers} resident "
                   f"({time.perf_counter() - t_setup:.1f} s)", file=sys.stderr, flush=True)
+    if not args.no_graphs:
+        eng.enable_graphs()
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
     S = w.steps
@@ -171,13 +181,14 @@ def main():
     slow_ms = [t for t, sl in zip(step_ms, slow_step) if sl]
 
     def agg(kind):
-        ts = [(e0.elapsed_time(e1), nb) for kd, e0, e1, nb in timer if kd == kind]
+        ts = [(e0.elapsed_time(e1), nb, nc) for kd, e0, e1, nb, nc in timer if kd == kind]
         if not ts:
             return None
-        tot_ms = sum(t for t, _ in ts)
-        tot_b = sum(b for _, b in ts)
-        return {"calls": len(ts), "avg_us": 1e3 * tot_ms / len(ts),
-                "gbs": tot_b / (tot_ms * 1e-3) / 1e9, "avg_bytes": tot_b / len(ts)}
+        tot_ms = sum(t for t, _, _ in ts)
+        tot_b = sum(b for _, b, _ in ts)
+        calls = sum(c for _, _, c in ts)
+        return {"calls": calls, "avg_us": 1e3 * tot_ms / calls,
+                "gbs": tot_b / (tot_ms * 1e-3) / 1e9, "avg_bytes": tot_b / calls}
 
     fast = agg("fast")
     slow = agg("slow")
@@ -196,7 +207,7 @@ def main():
             dt.append((e0, e1))
         torch.cuda.synchronize()
         dms = [a.elapsed_time(b) for a, b in dt]
-        dk = [(e0.elapsed_time(e1), nb) for _, e0, e1, nb in dense_timer]
+        dk = [(e0.elapsed_time(e1), nb) for _, e0, e1, nb, _ in dense_timer]
         dense = {"step_ms": sum(dms) / len(dms),
                  "gbs": sum(b for _, b in dk) / (sum(t for t, _ in dk) * 1e-3) / 1e9}
 
@@ -205,10 +216,14 @@ def main():
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
+            import hashlib
             tj = json.load(open(args.traffic_json))
-            if tj.get("workload") == w.name:
+            src = os.path.join(ROOT, "sparse_kv_attention_decode_amd", "csrc", "sfi_attn.hip")
+            digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+            # counters taken on another kernel or workload do not describe this run
+            if tj.get("workload") == w.name and tj.get("kernel_source_sha256") == digest:
                 traffic = tj.get("bytes_per_call")
-        except Exception:
+        except (OSError, ValueError):
             traffic = None
     roof = None
     if fast:
@@ -239,7 +254,8 @@ def main():
                    "context": w.context, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "top_k": w.top_k, "n_recent": w.n_recent,
-                   "streams": 1 if args.one_stream else 2},
+                   "streams": 1 if args.one_stream else 2,
+                   "fast_step_graph": eng.graph is not None},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {

@@ -92,6 +92,11 @@ __device__ __forceinline__ void split3(float x, float& hi, float& mid, float& lo
   lo = trunc_bf16(r1 - mid);
 }
 
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 template <int D, bool WRITE_Z>
 __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
   constexpr int NC = D / 32;   // 32-dim steps of the logit product
@@ -113,10 +118,40 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
   const int g = ig % p.Hkv;
   const int i = ig / p.Hkv;
   const int b = uniform(p.seq_ids[i]);
-  const int N = uniform(p.seq_lens[b]);
   const int r = lane & 15;
   const int qd = lane >> 4;
   const size_t pidx = (size_t)ig * p.nsplit + split;
+  const int lane_off = r * D + 8 * qd;
+
+  const bool packed = p.fast && split < p.nsplit_a;
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  if (packed) {
+    const size_t off = ((size_t)b * p.Hkv + g) * (size_t)p.packed_cap * D;
+    kbase = reinterpret_cast<const uint16_t*>(p.packed_k) + off;
+    vbase = reinterpret_cast<const uint16_t*>(p.packed_v) + off;
+  } else {
+    kbase = reinterpret_cast<const uint16_t*>(p.k_cache);
+    vbase = reinterpret_cast<const uint16_t*>(p.v_cache);
+  }
+  auto load_rows = [&](size_t off, u32x4_t* kk, u32x4_t* vv) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kk[c] = *reinterpret_cast<const u32x4_t*>(kbase + off + 32 * c);
+      vv[c] = *reinterpret_cast<const u32x4_t*>(vbase + off + 32 * c);
+    }
+  };
+  // A packed tile's address depends only on the row, the KV head and the tile index, so
+  // a packed split requests its wave's first two tiles before the split's extent is known
+  // (indices clamped to the buffer's capacity); their latency overlaps the set-up below.
+  u32x4_t ka[NC], va[NC], kb[NC], vb[NC];
+  if (packed) {
+    const int last = p.packed_cap / kPage - 1;
+    const int t0w = split * p.tps + wave;
+    load_rows((size_t)min(t0w, last) * (kPage * D) + lane_off, ka, va);
+    load_rows((size_t)min(t0w + NW, last) * (kPage * D) + lane_off, kb, vb);
+  }
+  const int N = uniform(p.seq_lens[b]);
 
   const SplitRange sr = split_range(p, b, g, split, N);
   if (sr.t0 >= sr.t1) {  // workgroup-uniform
@@ -127,45 +162,30 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
   const int wt0 = sr.t0 + wave;
   // Physical pages of the split, staged once in LDS: the per-tile lookups then wait on
   // the LDS counter only and never on the in-flight K/V loads.
-  if (!sr.packed) {
+  if (!packed) {
     const int32_t* btg = p.block_table + (size_t)b * p.max_pages + sr.t0;
     for (int k = threadIdx.x; k < sr.t1 - sr.t0; k += 256) sm_page[k] = btg[k];
   }
   __syncthreads();
 
-  const uint16_t* kbase;
-  const uint16_t* vbase;
-  if (sr.packed) {
-    const size_t off = ((size_t)b * p.Hkv + g) * (size_t)p.packed_cap * D;
-    kbase = reinterpret_cast<const uint16_t*>(p.packed_k) + off;
-    vbase = reinterpret_cast<const uint16_t*>(p.packed_v) + off;
-  } else {
-    kbase = reinterpret_cast<const uint16_t*>(p.k_cache);
-    vbase = reinterpret_cast<const uint16_t*>(p.v_cache);
-  }
-  const int lane_off = r * D + 8 * qd;
   float* zrow = (WRITE_Z && r < p.G)
                     ? p.logits + ((size_t)b * p.Hq + (size_t)g * p.G + r) * p.logits_stride
                     : nullptr;
 
   auto tile_offset = [&](int t) -> size_t {
-    if (sr.packed) return (size_t)t * kPage * D;
+    if (packed) return (size_t)t * kPage * D;
     const int page = uniform(sm_page[t - sr.t0]);
     return ((size_t)page * p.Hkv + g) * (size_t)(kPage * D);
   };
   auto load_tile = [&](int t, u32x4_t* kk, u32x4_t* vv) {
-    const size_t off = tile_offset(t) + lane_off;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kk[c] = *reinterpret_cast<const u32x4_t*>(kbase + off + 32 * c);
-      vv[c] = *reinterpret_cast<const u32x4_t*>(vbase + off + 32 * c);
-    }
+    load_rows(tile_offset(t) + lane_off, kk, vv);
   };
 
-  // The wave's first tile is requested before the query is prepared, so its latency
-  // overlaps the prologue.
-  u32x4_t ka[NC], va[NC], kb[NC], vb[NC];
-  if (wt0 < sr.t1) load_tile(wt0, ka, va);
+  // Paged splits request their wave's first two tiles now, before the query is prepared.
+  if (!packed && wt0 < sr.t1) {
+    load_tile(wt0, ka, va);
+    load_tile(min(wt0 + NW, sr.t1 - 1), kb, vb);
+  }
 
   // Query operand, in LDS: lane (qd, r) of every wave reads head r, dims 32c + 8qd .. +8,
   // pre-scaled by 1/sqrt(D) and split into three bf16 terms.  Wave 0 prepares it.
@@ -224,8 +244,9 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
   // The request is unconditional (the last tile is re-read at the end of the run) so the
   // number of loads in flight, and with it the wait before tile t's products, does not
   // depend on a branch.
-  auto step = [&](int t, u32x4_t* kr, u32x4_t* vr, u32x4_t* kpf, u32x4_t* vpf) {
-    load_tile(min(t + NW, sr.t1 - 1), kpf, vpf);
+  auto step = [&](auto prefetch, int t, u32x4_t* kr, u32x4_t* vr, u32x4_t* kpf,
+                  u32x4_t* vpf) {
+    if constexpr (decltype(prefetch)::value) load_tile(min(t + NW, sr.t1 - 1), kpf, vpf);
     // Read the query operand from LDS every tile (an opaque lane index keeps the reads
     // inside the loop, so the 48 registers they need are not held across it).
     int ql_idx = lane;
@@ -316,10 +337,15 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
       O[tt] = mfma16(vt[tt], ph2, O[tt]);
     }
   };
-  for (int t = wt0; t < sr.t1; t += 2 * NW) {
-    step(t, ka, va, kb, vb);
-    if (t + NW >= sr.t1) break;
-    step(t + NW, kb, vb, ka, va);
+  // The first tile's successor is already in flight; every later step requests the
+  // wave's tile after next.
+  if (wt0 < sr.t1) {
+    step(Flag<false>{}, wt0, ka, va, kb, vb);
+    for (int t = wt0 + NW; t < sr.t1; t += 2 * NW) {
+      step(Flag<true>{}, t, kb, vb, ka, va);
+      if (t + NW >= sr.t1) break;
+      step(Flag<true>{}, t + NW, ka, va, kb, vb);
+    }
   }
 
   // Merge the four waves of the workgroup: common max, rescaled sums, one partial.
@@ -506,7 +532,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm
   // Thread (grp, col) folds splits grp, grp + ngrp, ... of column block col into a running
   // (max, sum, weighted o); the loads of kUnroll splits are issued together.  The groups
   // are then combined in LDS.
-  constexpr int kUnroll = 4;
+  constexpr int kUnroll = 8;
   __shared__ float gm[64], gl[64];
   __shared__ float4 acc4[256];
   const int tid = threadIdx.x;

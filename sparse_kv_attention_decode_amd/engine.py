@@ -16,6 +16,13 @@ for layer i's pack event.  Both streams have the default priority.
 All per-step tables (sequence lengths, recent-window starts, slow/fast row lists) are
 built on the host from the seeded flags and copied to the device once, so a step issues
 kernels only.
+
+Graphs (`enable_graphs`): a fast step of every row issues the same calls at every step,
+so it is captured once as a HIP graph over all layers.  The graph reads the step's
+inputs from fixed buffers (current lengths, recent starts and every layer's query); a
+step stages them with three device copies and replays the graph.  This removes the host
+cost of issuing one call per layer, which is larger than a fast call's GPU time.  The
+first fast step after a slow step stays call by call (see `step`).
 """
 from __future__ import annotations
 
@@ -148,6 +155,7 @@ class Engine:
         self.stream2 = torch.cuda.Stream(device=dev) if two_streams else self.stream1
         self.layers: List[LayerBuffers] = []
         self.dbg = dbg_scores
+        self.graph = None
         self.dbg_buf: Optional[torch.Tensor] = None
         if dbg_scores:
             self.dbg_buf = torch.zeros(B, w.num_kv_heads, self.stride, dtype=torch.float32,
@@ -217,6 +225,33 @@ class Engine:
             lb.q_step = lb.q_all[0].numel() * lb.q_all.element_size()
         self._bound_layers = len(self.layers)
 
+    def enable_graphs(self) -> None:
+        """Capture the all-rows fast step of every layer as one HIP graph on stream 1.
+        Call after the last add_layer."""
+        w, dev = self.w, self.device
+        self._bind()
+        lib, shp = self._lib, self._shp
+        B = w.batch
+        # every layer's query of every step, step-major, so one copy stages a step
+        self.q_table = torch.stack([lb.q_all for lb in self.layers], dim=1).contiguous()
+        self.q_cur = torch.zeros_like(self.q_table[0])          # [layers, B, Hq, D]
+        self.cur_len = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.cur_rstart = torch.zeros(B, dtype=torch.int32, device=dev)
+        ws_fast, ws_fast_n = self._ws["fast"]
+        q0, q_step = self.q_cur.data_ptr(), self.q_cur[0].numel() * 4
+        self.stream1.wait_stream(torch.cuda.current_stream(dev))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream1):
+            for li, lb in enumerate(self.layers):
+                P = lb.ptr
+                self._ok("sfi_fast_attn", lib.sfi_fast_attn(
+                    shp, q0 + li * q_step, P["pk"], P["pv"], P["pl"], self.packed_cap,
+                    P["k"], P["v"], P["bt"], self.cur_rstart.data_ptr(),
+                    self.cur_len.data_ptr(), self._all_p, B, self.max_recent, P["out"], None,
+                    ws_fast, ws_fast_n, self._h1))
+        self.graph = g
+        torch.cuda.synchronize()
+
     @staticmethod
     def _ok(name: str, rc: int) -> None:
         if rc != L.SFI_OK:
@@ -229,10 +264,19 @@ class Engine:
         dense_only runs the Full-KV baseline: dense attention for every sequence, no
         Selector, no logits.  When `timer` is a list, the attention calls of every
         `time_every`-th layer are bracketed by two events on stream 1 and
-        (kind, start, end, algorithmic bytes) is appended.
+        (kind, start, end, algorithmic bytes, calls) is appended; a graph replay is
+        bracketed as a whole (calls = layers).
         """
         if getattr(self, "_bound_layers", -1) != len(self.layers):
             self._bind()
+        # The graph waits for every layer's pending pack before its first call, so the
+        # first fast step after a slow step is issued call by call: its layer i then waits
+        # only for layer i's pack and overlaps the Selector work still queued on stream 2.
+        if self.graph is not None and not dense_only and \
+                len(self.plan.fast_ids[s]) == self.w.batch and \
+                not any(lb.pack_pending for lb in self.layers):
+            self._step_graph(s, timer)
+            return
         w, lib, shp, prm = self.w, self._lib, self._shp, self._prm
         n_slow = len(self.plan.slow_ids[s])
         n_fast = len(self.plan.fast_ids[s])
@@ -256,7 +300,7 @@ class Engine:
             e0.record(s1)
             fn()
             e1.record(s1)
-            timer.append((kind, e0, e1, nbytes))
+            timer.append((kind, e0, e1, nbytes, 1))
 
         fb = self.fast_bytes(s) if (timer is not None and n_fast) else 0
         db = self.dense_bytes(s, range(w.batch) if dense_only else self.plan.slow_ids[s]) \
@@ -294,6 +338,24 @@ class Engine:
                 if s2 is not s1:
                     lb.ev_pack.record(s2)
                     lb.pack_pending = True
+
+    def _step_graph(self, s: int, timer: Optional[list]) -> None:
+        """Fast step s of every row through the captured graph (no pack pending)."""
+        s1 = self.stream1
+        with torch.cuda.stream(s1):
+            self.q_cur.copy_(self.q_table[s], non_blocking=True)
+            self.cur_len.copy_(self.seq_len_d[s], non_blocking=True)
+            self.cur_rstart.copy_(self.rstart_d[s], non_blocking=True)
+            if timer is None:
+                self.graph.replay()
+            else:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(s1)
+                self.graph.replay()
+                e1.record(s1)
+                nl = len(self.layers)
+                timer.append(("fast", e0, e1, self.fast_bytes(s) * nl, nl))
 
     def join(self) -> None:
         """Make stream 1 wait for every outstanding Selector/pack."""

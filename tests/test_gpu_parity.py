@@ -216,6 +216,33 @@ def test_two_streams_bit_identical_to_one_stream():
         assert torch.equal(a, b)
 
 
+def test_fast_step_graph_bit_identical_to_eager():
+    """Fast steps replayed from the captured two-layer graph, with eager slow steps,
+    Selector and pack work and host synchronisations between the replays, give
+    bit-identical outputs to the same trajectory issued call by call."""
+    w = get("qwen3_0p6b_8k").replace(steps=48)
+    runs = []
+    for graphs in (False, True):
+        ds = [make_layer(w, layer, device="cuda") for layer in (0, 1)]
+        eng = Engine(w, ds[0]["flags"])
+        lbs = [eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
+               for d in ds]
+        if graphs:
+            eng.enable_graphs()
+        res = []
+        for s in range(w.steps):
+            eng.step(s)
+            eng.join()
+            torch.cuda.synchronize()
+            res.append(torch.stack([lb.out.clone() for lb in lbs]))
+        runs.append((res, eng.plan.mode[0].copy()))
+    (eager, mode), (graph, _) = runs
+    assert int((mode == 0).sum()) >= 10  # many replays, interleaved with slow steps
+    assert int(mode.sum()) >= 2
+    for s, (a, b) in enumerate(zip(eager, graph)):
+        assert torch.equal(a, b), s
+
+
 def test_fast_equals_dense_when_k_covers_candidates():
     """Invariant on the device: with K >= |C| every fast step equals the dense
     step (same positions, so equal up to fp32 rounding)."""
