@@ -71,7 +71,8 @@ SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len);
 // nms_radius on each side, the prior normalisers and the lse of every query head.
 size_t score_lds_bytes(int num_kv_heads, int num_q_heads, int nms_radius, int tile);
 constexpr size_t kScoreLdsLimit = 64 * 1024;
-// Widest scoring tile (256, 128 or 64 positions) whose LDS fits, or 0 if none does.
+// Scoring tile: 256 - 2 nms_radius positions (one position per thread with the halo)
+// when the radius is at most 96, else 64; 0 if its LDS does not fit.
 int score_tile(int num_kv_heads, int num_q_heads, int nms_radius);
 
 hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm,

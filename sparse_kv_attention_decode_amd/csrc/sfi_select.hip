@@ -17,11 +17,11 @@
 //
 // Kernels:
 //   k_sel_zsum   Z_g partial sums over chunks of 4096 positions.
-//   k_sel_score  one block per tile of up to 256 positions with an R-position halo, all
+//   k_sel_score  one block per tile of 256 - 2R positions plus an R-position halo, all
 //                KV heads at once (NMS couples neighbours, exclusivity couples heads):
-//                logits and norms staged in LDS, s computed there, then the refined score
-//                s' as an order-preserving uint32 key (s' >= 0, so its IEEE bits already
-//                order like the value).
+//                one thread per position computes s of every head into LDS, then the
+//                refined score s' as an order-preserving uint32 key (s' >= 0, so its IEEE
+//                bits already order like the value).
 //   k_topk_*     radix select of the K-th largest key spread over slices of 4096
 //                candidates (histogram, boundary-bin gather, a one-block select on the
 //                gathered bin in LDS, ordered parallel write); see the top-K section.
@@ -182,27 +182,21 @@ struct ScoreArgs {
   float lam, a_soft, a_cross;
 };
 
-// Row width of the staged tile: the halo on each side is padded to a multiple of four
-// so the tile body keeps 16-byte alignment in LDS.
-__host__ __device__ inline int score_pad(int R) { return (R + 3) & ~3; }
-
-// One block per (row, tile of `tile` positions).  Stage the logits of every query head
-// and the key norms of every KV head over the tile and an R-wide halo on each side into
-// LDS, with all global loads issued before any arithmetic; then the fused score s of
-// every KV head at every staged position; then, for the tile's candidates, the soft-NMS
-// dominance (neighbours within R, same head) and ownership (all heads at the position)
-// and the refined key.
+// One block per (row, tile of `tile` positions).  Every thread computes the fused score s
+// of every KV head at one position of the tile or of the R-wide halo on either side,
+// reading the logits of the position's query heads and the key norms straight from global
+// memory (consecutive threads, consecutive positions), and leaves s in LDS.  Then, for the
+// tile's candidates, the soft-NMS dominance (neighbours within R, same head), the
+// ownership (all heads at the position) and the refined key.  Only s is staged, so the
+// block needs little LDS and shares CUs well with attention running at the same time.
 template <int GT>
 __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
-  extern __shared__ float4 lds4[];  // float4 keeps the staged rows 16-byte aligned
-  float* lds = reinterpret_cast<float*>(lds4);
+  extern __shared__ float lds[];
   const int G = GT > 0 ? GT : a.G;
   const int TILE = a.tile;
-  const int P = score_pad(a.R);
-  const int W = TILE + 2 * P;
-  float* zt = lds;                    // [Hq][W]   logits
-  float* nt = zt + a.Hq * W;          // [Hkv][W]  key norms
-  float* s_t = nt + a.Hkv * W;        // [Hkv][W]  fused scores
+  const int R = a.R;
+  const int W = TILE + 2 * R;
+  float* s_t = lds;                   // [Hkv][W]  fused scores, column c = position t0 - R + c
   float* zs = s_t + a.Hkv * W;        // [Hkv]     prior normalisers
   float* lses = zs + a.Hkv;           // [Hq]
   const int tid = threadIdx.x;
@@ -215,78 +209,57 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
   const int lo = a.n_sink;
   const int hi = max(lo, N - a.n_recent);
 
-  // Stage the tile body (float4) and the halo (scalars) of logits and norms.
-  const int q4 = TILE / 4;
-  const int rows = a.Hq + a.Hkv;
-  for (int e = tid; e < rows * q4; e += 256) {
-    const int row = e / q4, c4 = e % q4;
-    const int j = t0 + 4 * c4;
-    const float* src = row < a.Hq
-                           ? a.logits + ((size_t)b * a.Hq + row) * a.logits_stride + j
-                           : a.key_norm + ((size_t)b * a.Hkv + (row - a.Hq)) * a.norm_stride + j;
-    float4 v;
-    if (j + 3 < N) {
-      v = *reinterpret_cast<const float4*>(src);
-    } else {
-      v.x = j < N ? src[0] : 0.f;
-      v.y = j + 1 < N ? src[1] : 0.f;
-      v.z = j + 2 < N ? src[2] : 0.f;
-      v.w = j + 3 < N ? src[3] : 0.f;
-    }
-    *reinterpret_cast<float4*>(zt + row * W + P + 4 * c4) = v;
-  }
-  for (int e = tid; e < rows * 2 * a.R; e += 256) {
-    const int row = e / (2 * a.R), k = e % (2 * a.R);
-    const bool left = k < a.R;
-    const int j = left ? t0 - a.R + k : t0 + TILE + (k - a.R);
-    const int col = left ? P - a.R + k : P + TILE + (k - a.R);
-    float v = 0.f;
-    if (j >= 0 && j < N)
-      v = row < a.Hq ? a.logits[((size_t)b * a.Hq + row) * a.logits_stride + j]
-                     : a.key_norm[((size_t)b * a.Hkv + (row - a.Hq)) * a.norm_stride + j];
-    zt[row * W + col] = v;
-  }
-  for (int g = tid; g < a.Hkv; g += 256) {
+  // Prior normalisers: eight lanes per KV head add every eighth chunk partial, then a
+  // fixed-order reduction over the eight lanes (the same sum in every block).
+  if (tid < 8 * a.Hkv) {
+    const int g = tid >> 3, part = tid & 7;
     const float* zp = a.zpart + ((size_t)i * a.Hkv + g) * a.nchunk;
     float z = 0.f;
-    for (int c = 0; c < a.nchunk; ++c) z += zp[c];
-    zs[g] = z;
+    for (int c = part; c < a.nchunk; c += 8) z += zp[c];
+    z += __shfl_xor(z, 1, 8);
+    z += __shfl_xor(z, 2, 8);
+    z += __shfl_xor(z, 4, 8);
+    if (part == 0) zs[g] = z;
   }
   for (int h = tid; h < a.Hq; h += 256) lses[h] = a.lse[(size_t)b * a.Hq + h];
   __syncthreads();
 
   // Fused scores over the tile and its halo.
   const float invG = 1.f / (float)G;
-  for (int col = P - a.R + tid; col < P + TILE + a.R; col += 256) {
-    const int j = t0 - P + col;
+  for (int col = tid; col < W; col += 256) {
+    const int j = t0 - R + col;
     const bool in = j >= 0 && j < N;
-    const float phi_pos = in ? 1.f + logf(1.f + (float)(N - 1 - j)) : 0.f;
-    const bool body = col >= P && col < P + TILE;
+    const int jc = in ? j : 0;
+    const float phi_pos = 1.f + logf(1.f + (float)(N - 1 - jc));
+    const bool body = col >= R && col < R + TILE;
+    const float* zrow = a.logits + (size_t)b * a.Hq * a.logits_stride + jc;
+    const float* nrow = a.key_norm + (size_t)b * a.Hkv * a.norm_stride + jc;
     for (int g = 0; g < a.Hkv; ++g) {
-      float s = -1.f;
-      if (in) {
-        float f = 0.f;
-        if (GT > 0) {
+      float f = 0.f;
+      if (GT > 0) {
+        float zv[GT > 0 ? GT : 1];
 #pragma unroll
-          for (int hh = 0; hh < (GT > 0 ? GT : 1); ++hh)
-            f += expf(zt[(g * G + hh) * W + col] - lses[g * G + hh]);
-        } else {
-          for (int hh = 0; hh < G; ++hh) f += expf(zt[(g * G + hh) * W + col] - lses[g * G + hh]);
-        }
-        f *= invG;
-        const float r = (1.f / fmaxf(nt[g * W + col], 1e-6f)) * phi_pos / zs[g];
-        s = (1.f - a.lam) * f + a.lam * r;
-        if (a.dbg && body) a.dbg[((size_t)b * a.Hkv + g) * a.logits_stride + j] = s;
+        for (int hh = 0; hh < (GT > 0 ? GT : 1); ++hh)
+          zv[hh] = zrow[(size_t)(g * G + hh) * a.logits_stride];
+#pragma unroll
+        for (int hh = 0; hh < (GT > 0 ? GT : 1); ++hh) f += expf(zv[hh] - lses[g * G + hh]);
+      } else {
+        for (int hh = 0; hh < G; ++hh)
+          f += expf(zrow[(size_t)(g * G + hh) * a.logits_stride] - lses[g * G + hh]);
       }
-      s_t[g * W + col] = s;
+      f *= invG;
+      const float r = (1.f / fmaxf(nrow[(size_t)g * a.norm_stride], 1e-6f)) * phi_pos / zs[g];
+      const float s = (1.f - a.lam) * f + a.lam * r;
+      if (in && a.dbg && body) a.dbg[((size_t)b * a.Hkv + g) * a.logits_stride + j] = s;
+      s_t[g * W + col] = in ? s : -1.f;
     }
   }
   __syncthreads();
 
   // Refinement decisions and keys for the tile's candidates.
   const float ws = 1.f - a.a_soft, wc = 1.f - a.a_cross;
-  for (int col = P + tid; col < P + TILE; col += 256) {
-    const int j = t0 - P + col;
+  for (int col = R + tid; col < R + TILE; col += 256) {
+    const int j = t0 - R + col;
     if (j < lo || j >= hi) continue;
     int own = 0;
     float best = s_t[col];
@@ -297,8 +270,8 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
         own = g;
       }
     }
-    const int dlo = max(lo, j - a.R) - j;      // <= 0
-    const int dhi = min(hi - 1, j + a.R) - j;  // >= 0
+    const int dlo = max(lo, j - R) - j;      // <= 0
+    const int dhi = min(hi - 1, j + R) - j;  // >= 0
     for (int g = 0; g < a.Hkv; ++g) {
       const float* row = s_t + g * W + col;
       const float sj = row[0];
@@ -320,7 +293,7 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
 //   k_topk_gather  per slice: locate the bin holding the K_eff-th key, count the slice's
 //                  keys above that bin and append the keys inside it, with their
 //                  candidate indices, to a short candidate list;
-//   k_topk_final   per (row, head), 1024 threads: resolve the remaining 21 bits on the
+//   k_topk_final   per (row, head), 512 threads: resolve the remaining 21 bits on the
 //                  candidate list in LDS, giving the exact threshold T and the number of
 //                  keys equal to T still to take; the last of those ties (lowest
 //                  positions first) is found by the same selection on the complemented
@@ -328,7 +301,7 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
 //                  holds more keys than the list takes, a single-block path selects from
 //                  the keys in global memory instead and writes the result itself;
 //   k_topk_write   per slice: every key above T and the taken ties, ascending.
-constexpr int kTopkThreads = 1024;
+constexpr int kTopkThreads = 512;   // one-block stages: fits beside attention on a CU
 constexpr int kSliceThreads = 256;
 constexpr int kKeysPerThread = 16;
 constexpr int kSlice = kSliceThreads * kKeysPerThread;  // candidates per slice
@@ -337,6 +310,7 @@ constexpr int kHistBins = 1 << kHistBits;
 static_assert(kHistBins == kTopkHistWords, "global histogram size");
 constexpr int kCandCap = kCandCapBytes / 8;  // key + index per candidate
 constexpr int kMaxSlices = 1024;
+static_assert(kMaxSlices % kTopkThreads == 0, "slices per thread");
 
 // Per-(row, head) state words.
 constexpr int kStCount = 0;  // candidates appended by k_topk_gather
@@ -436,7 +410,7 @@ __device__ __forceinline__ void load16(const uint32_t* keys, int64_t kstride, in
   }
 }
 
-// Visit keys [0, n) in chunks of 16 per thread (1024 threads); the next chunk is
+// Visit keys [0, n) in chunks of 16 per thread (kTopkThreads threads); the next chunk is
 // requested before the current one is processed (two register buffers, unrolled so they
 // swap roles without copies).  f(c, kv) sees the keys at candidate indices c .. c+15 and
 // is called by every thread the same number of times (it may contain block barriers).
@@ -760,9 +734,24 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_final(TopkArgs a) {
     if (key > T || (key == T && idx <= c_last)) atomicAdd(&cnt_sl[idx / kSlice], 1u);
   }
   __syncthreads();
+  // Output offset of every slice: exclusive scan, kSlicesPerThread consecutive slices per
+  // thread.
+  constexpr int kSlicesPerThread = kMaxSlices / kTopkThreads;
+  uint32_t v[kSlicesPerThread], sum = 0;
+#pragma unroll
+  for (int k = 0; k < kSlicesPerThread; ++k) {
+    const int sl = kSlicesPerThread * tid + k;
+    v[k] = sl < nsl ? cnt_sl[sl] : 0u;
+    sum += v[k];
+  }
   uint32_t tot;
-  const uint32_t off = block_exscan<kTopkThreads>(tid < nsl ? cnt_sl[tid] : 0u, wsum, &tot);
-  if (tid < nsl) a.slice_off[(size_t)ig * a.nslice + tid] = off;
+  uint32_t off = block_exscan<kTopkThreads>(sum, wsum, &tot);
+#pragma unroll
+  for (int k = 0; k < kSlicesPerThread; ++k) {
+    const int sl = kSlicesPerThread * tid + k;
+    if (sl < nsl) a.slice_off[(size_t)ig * a.nslice + sl] = off;
+    off += v[k];
+  }
   if (tid == 0) {
     st[kStT] = T;
     st[kStCLast] = c_last;
@@ -840,16 +829,15 @@ SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len) {
 }
 
 size_t score_lds_bytes(int num_kv_heads, int num_q_heads, int nms_radius, int tile) {
-  const size_t W = (size_t)tile + 2 * (size_t)score_pad(nms_radius);
-  return sizeof(float) * ((size_t)(num_q_heads + 2 * num_kv_heads) * W + num_kv_heads +
-                          num_q_heads);
+  const size_t W = (size_t)tile + 2 * (size_t)nms_radius;
+  return sizeof(float) * ((size_t)num_kv_heads * W + num_kv_heads + num_q_heads);
 }
 
 int score_tile(int num_kv_heads, int num_q_heads, int nms_radius) {
-  for (int tile = 256; tile >= 64; tile /= 2)
-    if (score_lds_bytes(num_kv_heads, num_q_heads, nms_radius, tile) <= kScoreLdsLimit)
-      return tile;
-  return 0;
+  // One position per thread when the halo allows it (256 - 2R), else 64 positions.
+  const int tile = nms_radius <= 96 ? 256 - 2 * nms_radius : 64;
+  return score_lds_bytes(num_kv_heads, num_q_heads, nms_radius, tile) <= kScoreLdsLimit ? tile
+                                                                                     : 0;
 }
 
 namespace {

@@ -9,9 +9,11 @@ buffer and the recent window.
 
 Overlap (es "3. Optimización del Sistema / Pipeline Asíncrono", zh "2.3 异步流水线"): the
 attention of every layer is issued on stream 1; the Selector and pack of layer i are
-issued on stream 2 after an event recorded behind layer i's slow attention, so they run
-while stream 1 continues with layer i+1.  Before layer i's next attention, stream 1 waits
-for layer i's pack event.  Both streams have the default priority.
+issued on a Selector stream after an event recorded behind layer i's slow attention, so
+they run while stream 1 continues with layer i+1.  There are two Selector streams, used by
+alternate layers, so that the short dependent kernels of two layers' Selectors overlap
+each other too.  Before layer i's next attention, stream 1 waits for layer i's pack event.
+All streams have the default priority.
 
 All per-step tables (sequence lengths, recent-window starts, slow/fast row lists) are
 built on the host from the seeded flags and copied to the device once, so a step issues
@@ -149,10 +151,19 @@ class Engine:
         self.ws_fast = L.workspace(
             max(L.sfi_fast_attn_ws(self.shape, n, self.packed_cap, self.max_recent)
                 for n in range(1, B + 1)), dev)
-        self.ws_sel = L.workspace(max(L.sfi_select_ws(self.shape, self.params, n, self.max_len)
-                                      for n in range(1, B + 1)), dev)
+        # Selector streams: the Selector and pack of consecutive layers alternate between
+        # them, so the dependent kernel chains of two layers run side by side.  Each stream
+        # has its own Selector workspace.  The debug score buffer is shared, so with it only
+        # one stream is used.
+        n_sel = 2 if (two_streams and not dbg_scores) else 1
+        sel_ws = max(L.sfi_select_ws(self.shape, self.params, n, self.max_len)
+                     for n in range(1, B + 1))
+        self.ws_sels = [L.workspace(sel_ws, dev) for _ in range(n_sel)]
+        self.ws_sel = self.ws_sels[0]
         self.stream1 = torch.cuda.Stream(device=dev)
-        self.stream2 = torch.cuda.Stream(device=dev) if two_streams else self.stream1
+        self.sel_streams = ([torch.cuda.Stream(device=dev) for _ in range(n_sel)]
+                            if two_streams else [self.stream1])
+        self.stream2 = self.sel_streams[0]
         self.layers: List[LayerBuffers] = []
         self.dbg = dbg_scores
         self.graph = None
@@ -212,9 +223,10 @@ class Engine:
         self._fast_p = self.fast_ids_d.data_ptr()
         self._all_p = self.all_ids_d.data_ptr()
         self._h1 = self.stream1.cuda_stream
-        self._h2 = self.stream2.cuda_stream
+        self._h2 = [st.cuda_stream for st in self.sel_streams]
+        self._ws_sel = [(t.data_ptr(), t.numel()) for t in self.ws_sels]
         self._ws = {k: (t.data_ptr(), t.numel()) for k, t in
-                    (("slow", self.ws_slow), ("fast", self.ws_fast), ("sel", self.ws_sel))}
+                    (("slow", self.ws_slow), ("fast", self.ws_fast))}
         self._dbg_p = self.dbg_buf.data_ptr() if self.dbg_buf is not None else None
         for lb in self.layers:
             lb.ptr = {k: getattr(lb, a).data_ptr() for k, a in (
@@ -284,11 +296,10 @@ class Engine:
         rstart = self._rstart_p + s * self._rowb
         slow_ids = self._slow_p + s * self._rowb
         fast_ids = self._fast_p + s * self._rowb
-        s1, s2 = self.stream1, self.stream2
-        h1, h2 = self._h1, self._h2
+        s1 = self.stream1
+        h1 = self._h1
         ws_slow, ws_slow_n = self._ws["slow"]
         ws_fast, ws_fast_n = self._ws["fast"]
-        ws_sel, ws_sel_n = self._ws["sel"]
         ok = self._ok
 
         def timed(li, kind, nbytes, fn):
@@ -325,6 +336,9 @@ class Engine:
                 timed(li, "slow", db, lambda: ok("sfi_slow_attn", lib.sfi_slow_attn(
                     shp, q, P["k"], P["v"], P["bt"], seq_len, slow_ids, n_slow, self.max_len,
                     P["out"], P["z"], self.stride, P["lse"], ws_slow, ws_slow_n, h1)))
+                k = li % len(self.sel_streams)
+                s2, h2 = self.sel_streams[k], self._h2[k]
+                ws_sel, ws_sel_n = self._ws_sel[k]
                 if s2 is not s1:
                     lb.ev_attn.record(s1)
                     s2.wait_event(lb.ev_attn)
