@@ -27,6 +27,7 @@ struct PackArgs {
   int32_t* ppos;
   int32_t* plen;
   int Hkv, max_pages, K, n_sink, cap, row_bytes;
+  int n_work;  // row blocks in all
 };
 
 __device__ __forceinline__ int packed_source(const PackArgs& a, const int32_t* selrow, int row) {
@@ -37,6 +38,9 @@ __device__ __forceinline__ int packed_source(const PackArgs& a, const int32_t* s
 
 constexpr int kPackInstr = 8;   // load instructions per wavefront and tensor
 constexpr int kPackWaves = 4;   // wavefronts per block
+// At most this many blocks (one per CU), each looping over row blocks: the copy keeps the
+// HBM busy while leaving room on every CU for the attention that runs at the same time.
+constexpr int kPackMaxBlocks = 256;
 
 template <int LPR>
 __global__ __launch_bounds__(64 * kPackWaves) void k_pack(PackArgs a) {
@@ -46,49 +50,52 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack(PackArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nblk = (a.cap + RB - 1) / RB;
-  const int blk = blockIdx.x % nblk;
-  const int ig = blockIdx.x / nblk;
-  const int g = ig % a.Hkv, i = ig / a.Hkv;
-  const int b = a.seq_ids[i];
-  const size_t bg = (size_t)b * a.Hkv + g;
-  const int32_t* selrow = a.sel + bg * a.K;
-  const int row0 = blk * RB + wv * RW;
-  if (row0 >= a.cap) return;  // wavefront-uniform; the kernel has no block barrier
-  // Lane r < RW resolves row row0 + r: its position and page.
-  const int my_row = row0 + lane;
-  const bool own = lane < RW && my_row < a.cap;
-  const int pos = own ? packed_source(a, selrow, my_row) : -1;
-  const int page = pos >= 0 ? a.bt[(size_t)b * a.max_pages + pos / kPage] : 0;
-  if (own) {
-    a.ppos[bg * a.cap + my_row] = pos;
-    // Valid rows form a prefix: the last valid row (or row 0 when none is valid) records
-    // the packed length.
-    const int next = my_row + 1 < a.cap ? packed_source(a, selrow, my_row + 1) : -1;
-    if (pos >= 0 && next < 0) a.plen[bg] = my_row + 1;
-    if (my_row == 0 && pos < 0) a.plen[bg] = 0;
-  }
-  const int sub = lane % LPR, rsub = lane / LPR;
-  const size_t rb = (size_t)a.row_bytes;
-  u32x4_t kv[kPackInstr], vv[kPackInstr];
-  bool valid[kPackInstr];
+  // Grid-stride over the row blocks: the grid is capped (see launch_pack).
+  for (int work = blockIdx.x; work < a.n_work; work += gridDim.x) {
+    const int blk = work % nblk;
+    const int ig = work / nblk;
+    const int g = ig % a.Hkv, i = ig / a.Hkv;
+    const int b = a.seq_ids[i];
+    const size_t bg = (size_t)b * a.Hkv + g;
+    const int32_t* selrow = a.sel + bg * a.K;
+    const int row0 = blk * RB + wv * RW;
+    if (row0 >= a.cap) continue;  // wavefront-uniform; the kernel has no block barrier
+    // Lane r < RW resolves row row0 + r: its position and page.
+    const int my_row = row0 + lane;
+    const bool own = lane < RW && my_row < a.cap;
+    const int pos = own ? packed_source(a, selrow, my_row) : -1;
+    const int page = pos >= 0 ? a.bt[(size_t)b * a.max_pages + pos / kPage] : 0;
+    if (own) {
+      a.ppos[bg * a.cap + my_row] = pos;
+      // Valid rows form a prefix: the last valid row (or row 0 when none is valid) records
+      // the packed length.
+      const int next = my_row + 1 < a.cap ? packed_source(a, selrow, my_row + 1) : -1;
+      if (pos >= 0 && next < 0) a.plen[bg] = my_row + 1;
+      if (my_row == 0 && pos < 0) a.plen[bg] = 0;
+    }
+    const int sub = lane % LPR, rsub = lane / LPR;
+    const size_t rb = (size_t)a.row_bytes;
+    u32x4_t kv[kPackInstr], vv[kPackInstr];
+    bool valid[kPackInstr];
 #pragma unroll
-  for (int j = 0; j < kPackInstr; ++j) {
-    const int r = j * RPI + rsub;
-    const int pr = __shfl(pos, r), pg = __shfl(page, r);
-    valid[j] = pr >= 0;
-    // Rows without a position read row 0 of page 0 (always present) and store zeros.
-    const size_t src = valid[j] ? (((size_t)pg * a.Hkv + g) * kPage + pr % kPage) * rb : 0;
-    kv[j] = *reinterpret_cast<const u32x4_t*>(a.kc + src + 16 * sub);
-    vv[j] = *reinterpret_cast<const u32x4_t*>(a.vc + src + 16 * sub);
-  }
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < kPackInstr; ++j) {
+      const int r = j * RPI + rsub;
+      const int pr = __shfl(pos, r), pg = __shfl(page, r);
+      valid[j] = pr >= 0;
+      // Rows without a position read row 0 of page 0 (always present) and store zeros.
+      const size_t src = valid[j] ? (((size_t)pg * a.Hkv + g) * kPage + pr % kPage) * rb : 0;
+      kv[j] = *reinterpret_cast<const u32x4_t*>(a.kc + src + 16 * sub);
+      vv[j] = *reinterpret_cast<const u32x4_t*>(a.vc + src + 16 * sub);
+    }
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int j = 0; j < kPackInstr; ++j) {
-    const int row = row0 + j * RPI + rsub;
-    if (row < a.cap) {
-      const size_t dst = (bg * a.cap + row) * rb + 16 * sub;
-      *reinterpret_cast<u32x4_t*>(a.pk + dst) = valid[j] ? kv[j] : zero;
-      *reinterpret_cast<u32x4_t*>(a.pv + dst) = valid[j] ? vv[j] : zero;
+    for (int j = 0; j < kPackInstr; ++j) {
+      const int row = row0 + j * RPI + rsub;
+      if (row < a.cap) {
+        const size_t dst = (bg * a.cap + row) * rb + 16 * sub;
+        *reinterpret_cast<u32x4_t*>(a.pk + dst) = valid[j] ? kv[j] : zero;
+        *reinterpret_cast<u32x4_t*>(a.pv + dst) = valid[j] ? vv[j] : zero;
+      }
     }
   }
 }
@@ -116,15 +123,15 @@ hipError_t launch_pack(const sfi_shape& s, const sfi_select_params& prm, const v
   a.n_sink = prm.n_sink;
   a.cap = packed_cap;
   a.row_bytes = s.head_dim * (s.dtype == SFI_BF16 ? 2 : 4);
+  const int lpr = a.row_bytes / 16;  // 8, 16 or 32 lanes per row
+  const int rb = kPackWaves * kPackInstr * (64 / lpr);
+  a.n_work = n_seqs * s.num_kv_heads * ((packed_cap + rb - 1) / rb);
+  const dim3 grid(a.n_work < kPackMaxBlocks ? a.n_work : kPackMaxBlocks);
   const dim3 block(64 * kPackWaves);
-  auto grid = [&](int lpr) {
-    const int rb = kPackWaves * kPackInstr * (64 / lpr);
-    return dim3(n_seqs * s.num_kv_heads * ((packed_cap + rb - 1) / rb));
-  };
-  switch (a.row_bytes / 16) {
-    case 8: hipLaunchKernelGGL(k_pack<8>, grid(8), block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL(k_pack<16>, grid(16), block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(k_pack<32>, grid(32), block, 0, stream, a); break;
+  switch (lpr) {
+    case 8: hipLaunchKernelGGL(k_pack<8>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(k_pack<16>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(k_pack<32>, grid, block, 0, stream, a); break;
   }
   return hipGetLastError();
 }
