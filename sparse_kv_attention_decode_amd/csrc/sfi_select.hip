@@ -178,6 +178,7 @@ struct ScoreArgs {
   int64_t kstride;
   float* dbg;
   int Hq, Hkv, G, nchunk, ntile, tile;
+  int n_work;  // rows x tiles
   int n_sink, n_recent, R;
   float lam, a_soft, a_cross;
 };
@@ -190,8 +191,7 @@ struct ScoreArgs {
 // ownership (all heads at the position) and the refined key.  Only s is staged, so the
 // block needs little LDS and shares CUs well with attention running at the same time.
 template <int GT>
-__global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
-  extern __shared__ float lds[];
+__device__ __forceinline__ void score_block(const ScoreArgs& a, int work, float* lds) {
   const int G = GT > 0 ? GT : a.G;
   const int TILE = a.tile;
   const int R = a.R;
@@ -200,8 +200,8 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
   float* zs = s_t + a.Hkv * W;        // [Hkv]     prior normalisers
   float* lses = zs + a.Hkv;           // [Hq]
   const int tid = threadIdx.x;
-  const int i = blockIdx.x / a.ntile;
-  const int tile = blockIdx.x % a.ntile;
+  const int i = work / a.ntile;
+  const int tile = work % a.ntile;
   const int b = a.seq_ids[i];
   const int N = a.seq_lens[b];
   const int t0 = tile * TILE;
@@ -282,6 +282,19 @@ __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
       if (a.Hkv > 1 && g != own) sp *= wc;
       a.keys[((size_t)i * a.Hkv + g) * a.kstride + (j - lo)] = f2u(sp) & 0x7fffffffu;
     }
+  }
+}
+
+// Grid-stride over (row, tile) blocks: the grid is capped at one block per CU so the
+// scoring leaves room for the attention that runs at the same time.
+constexpr int kScoreMaxBlocks = 256;
+
+template <int GT>
+__global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
+  extern __shared__ float lds[];
+  for (int work = blockIdx.x; work < a.n_work; work += gridDim.x) {
+    score_block<GT>(a, work, lds);
+    __syncthreads();  // the next block reuses the LDS
   }
 }
 
@@ -842,8 +855,9 @@ int score_tile(int num_kv_heads, int num_q_heads, int nms_radius) {
 
 namespace {
 
-void launch_score(const ScoreArgs& a, int n_seqs, size_t lds, hipStream_t st) {
-  const dim3 grid(n_seqs * a.ntile), block(256);
+void launch_score(ScoreArgs a, int n_seqs, size_t lds, hipStream_t st) {
+  a.n_work = n_seqs * a.ntile;
+  const dim3 grid(a.n_work < kScoreMaxBlocks ? a.n_work : kScoreMaxBlocks), block(256);
   switch (a.G) {
     case 1: hipLaunchKernelGGL((k_sel_score<1>), grid, block, lds, st, a); break;
     case 2: hipLaunchKernelGGL((k_sel_score<2>), grid, block, lds, st, a); break;
