@@ -128,6 +128,13 @@ def test_select_validation():
     assert _select(s, _params(nms_radius=5000)) == L.SFI_E_UNSUPPORTED
     assert _select(s, p, wsb=10) == L.SFI_E_WORKSPACE
     assert _select(s, p, n=0) == L.SFI_OK
+    # the top-K takes at most 1024 slices of 4096 candidates
+    big = _shape(max_pages_per_seq=(1 << 22) // 16 + 8)
+    stride = (1 << 22) + 64
+    assert L.sfi_select_ws(big, p, 1, 1 << 22) > 0
+    assert L.sfi_select_ws(big, p, 1, (1 << 22) + 1) == 0
+    assert _select(big, p, maxlen=(1 << 22) + 1, lstride=stride, nstride=stride) == \
+        L.SFI_E_UNSUPPORTED
 
 
 def _pack(shape, params, **over):
