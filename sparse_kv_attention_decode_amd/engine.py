@@ -19,12 +19,11 @@ All per-step tables (sequence lengths, recent-window starts, slow/fast row lists
 built on the host from the seeded flags and copied to the device once, so a step issues
 kernels only.
 
-Graphs (`enable_graphs`): a fast step of every row issues the same calls at every step,
-so it is captured once as a HIP graph over all layers.  The graph reads the step's
-inputs from fixed buffers (current lengths, recent starts and every layer's query); a
-step stages them with three device copies and replays the graph.  This removes the host
-cost of issuing one call per layer, which is larger than a fast call's GPU time.  The
-first fast step after a slow step stays call by call (see `step`).
+Graphs (`enable_graphs`): every step whose rows are all fast is captured as one HIP graph
+holding that step's calls for every layer, with the step's own query, length and
+recent-start pointers, so a replay is the kernels alone.  This removes the host cost of
+issuing one call per layer, which is larger than a fast call's GPU time.  The first fast
+step after a slow step stays call by call (see `step`).
 """
 from __future__ import annotations
 
@@ -89,6 +88,10 @@ def make_plan(flags: np.ndarray, context: int, budget: int, n_sink: int, n_recen
         plan.slow_ids.append(np.nonzero(mode[:, s])[0].astype(np.int32))
         plan.fast_ids.append(np.nonzero(mode[:, s] == 0)[0].astype(np.int32))
     return plan
+
+
+# Fewest layers for which a fast step is replayed from a graph (see Engine.enable_graphs).
+kGraphMinLayers = 8
 
 
 class LayerBuffers:
@@ -167,6 +170,7 @@ class Engine:
         self.layers: List[LayerBuffers] = []
         self.dbg = dbg_scores
         self.graph = None
+        self.graphs = {}
         self.dbg_buf: Optional[torch.Tensor] = None
         if dbg_scores:
             self.dbg_buf = torch.zeros(B, w.num_kv_heads, self.stride, dtype=torch.float32,
@@ -237,31 +241,43 @@ class Engine:
             lb.q_step = lb.q_all[0].numel() * lb.q_all.element_size()
         self._bound_layers = len(self.layers)
 
-    def enable_graphs(self) -> None:
-        """Capture the all-rows fast step of every layer as one HIP graph on stream 1.
-        Call after the last add_layer."""
+    def enable_graphs(self, min_layers: int = kGraphMinLayers) -> None:
+        """Capture, for every step whose rows are all fast, that step's calls of every
+        layer as one HIP graph on stream 1 (the step's queries, lengths and recent starts
+        are at fixed places in the per-step tables, so each graph holds its own pointers
+        and a replay needs no staging).  Call after the last add_layer.
+
+        A graph launch costs more host and device time than issuing a few calls directly
+        (measured: about 33 us per replay of a one-layer step against 12 us for its two
+        kernels issued back to back), so below `min_layers` layers nothing is captured and
+        steps stay call by call."""
         w, dev = self.w, self.device
+        if len(self.layers) < min_layers:
+            self.graphs, self.graph = {}, None
+            return
         self._bind()
         lib, shp = self._lib, self._shp
         B = w.batch
-        # every layer's query of every step, step-major, so one copy stages a step
-        self.q_table = torch.stack([lb.q_all for lb in self.layers], dim=1).contiguous()
-        self.q_cur = torch.zeros_like(self.q_table[0])          # [layers, B, Hq, D]
-        self.cur_len = torch.zeros(B, dtype=torch.int32, device=dev)
-        self.cur_rstart = torch.zeros(B, dtype=torch.int32, device=dev)
         ws_fast, ws_fast_n = self._ws["fast"]
-        q0, q_step = self.q_cur.data_ptr(), self.q_cur[0].numel() * 4
         self.stream1.wait_stream(torch.cuda.current_stream(dev))
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=self.stream1):
-            for li, lb in enumerate(self.layers):
-                P = lb.ptr
-                self._ok("sfi_fast_attn", lib.sfi_fast_attn(
-                    shp, q0 + li * q_step, P["pk"], P["pv"], P["pl"], self.packed_cap,
-                    P["k"], P["v"], P["bt"], self.cur_rstart.data_ptr(),
-                    self.cur_len.data_ptr(), self._all_p, B, self.max_recent, P["out"], None,
-                    ws_fast, ws_fast_n, self._h1))
-        self.graph = g
+        self.graphs = {}
+        pool = None
+        for s in range(w.steps):
+            if len(self.plan.fast_ids[s]) != B:
+                continue
+            seq_len = self._seq_len_p + s * self._rowb
+            rstart = self._rstart_p + s * self._rowb
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream1, pool=pool):
+                for lb in self.layers:
+                    P = lb.ptr
+                    self._ok("sfi_fast_attn", lib.sfi_fast_attn(
+                        shp, P["q"] + s * lb.q_step, P["pk"], P["pv"], P["pl"],
+                        self.packed_cap, P["k"], P["v"], P["bt"], rstart, seq_len, self._all_p,
+                        B, self.max_recent, P["out"], None, ws_fast, ws_fast_n, self._h1))
+            pool = g.pool()
+            self.graphs[s] = g
+        self.graph = self.graphs or None
         torch.cuda.synchronize()
 
     @staticmethod
@@ -284,8 +300,7 @@ class Engine:
         # The graph waits for every layer's pending pack before its first call, so the
         # first fast step after a slow step is issued call by call: its layer i then waits
         # only for layer i's pack and overlaps the Selector work still queued on stream 2.
-        if self.graph is not None and not dense_only and \
-                len(self.plan.fast_ids[s]) == self.w.batch and \
+        if self.graph is not None and not dense_only and s in self.graphs and \
                 not any(lb.pack_pending for lb in self.layers):
             self._step_graph(s, timer)
             return
@@ -354,19 +369,17 @@ class Engine:
                     lb.pack_pending = True
 
     def _step_graph(self, s: int, timer: Optional[list]) -> None:
-        """Fast step s of every row through the captured graph (no pack pending)."""
+        """Fast step s of every row through its captured graph (no pack pending)."""
         s1 = self.stream1
+        g = self.graphs[s]
         with torch.cuda.stream(s1):
-            self.q_cur.copy_(self.q_table[s], non_blocking=True)
-            self.cur_len.copy_(self.seq_len_d[s], non_blocking=True)
-            self.cur_rstart.copy_(self.rstart_d[s], non_blocking=True)
             if timer is None:
-                self.graph.replay()
+                g.replay()
             else:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(s1)
-                self.graph.replay()
+                g.replay()
                 e1.record(s1)
                 nl = len(self.layers)
                 timer.append(("fast", e0, e1, self.fast_bytes(s) * nl, nl))

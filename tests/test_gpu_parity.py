@@ -232,7 +232,8 @@ def test_fast_step_graph_bit_identical_to_eager(batch):
         lbs = [eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
                for d in ds]
         if graphs:
-            eng.enable_graphs()
+            eng.enable_graphs(min_layers=1)
+            assert eng.graphs
         res = []
         for s in range(w.steps):
             eng.step(s)
