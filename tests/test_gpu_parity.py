@@ -436,3 +436,26 @@ def test_topk_heavy_exact_ties():
                                      name="heavy_ties_8k")
     d, eng, lb = _setup(w, dbg=True)
     _select_and_check(w, d, eng, lb, 0)
+
+
+@pytest.mark.parametrize("levels", [16, 4])
+def test_topk_ties_across_slices(levels):
+    """Score levels 22% apart (each its own 11-bit bin), interleaved over 70000 positions
+    (18 slices of 4096 candidates); the K-th key sits inside a level, so only part of its
+    exactly tied positions is taken, lowest positions first.  With 16 levels (about 4400
+    positions each) the level fits the candidate list; with 4 (about 17500 each) it does
+    not and the one-block path over global memory selects."""
+    Hq, Hkv, D, N, K = 4, 2, 128, 70000, 30000
+    stride = (N + 63) // 64 * 64
+    shape = L.make_shape(1, Hq, Hkv, D, (N + 15) // 16, "bf16")
+    params = L.make_params(4, 64, K, 4, 0.0, 0.0, 0.0)  # lambda = 0: s = f; no refinement
+    j = torch.arange(stride, device="cuda")
+    level = (j * 7919) % levels  # levels interleaved over positions, not in runs
+    logits = (-0.2 * level.float()).expand(1, Hq, stride).contiguous()
+    lse = torch.zeros(1, Hq, device="cuda")
+    key_norm = torch.ones(1, Hkv, stride, device="cuda")
+    sel, dbg = _select_direct(shape, params, logits, lse, key_norm, N, stride)
+    s = dbg[0, :, :N]
+    assert len(np.unique(s[0, 4:N - 64])) == levels
+    ref = O.select_from_scores(s, N, 4, 64, K, 4, 0.0, 0.0)
+    np.testing.assert_array_equal(sel[0], ref)
