@@ -622,25 +622,27 @@ hipError_t launch_partial(const AttnParams& p, int dtype, hipStream_t stream) {
 
 }  // namespace
 
-// Tiles per split for about `target` workgroups per call, with at least kMinTps tiles per
-// workgroup.  Fast calls aim at two workgroups per CU (256 CUs), which fills the chip in
+// Tiles per split for about `target` workgroups per call.  Fast calls aim at two workgroups per CU (256 CUs), which fills the chip in
 // one wave of workgroups.  Slow calls aim at one per CU: the dense pass stays HBM-bound
 // (the same duration as with two), and half of every CU stays free for the Selector and
 // pack of the previous layer, which run at the same time on another stream.
+// Small calls are latency-bound, so the floor is low: one tile per wavefront (four per
+// bf16 workgroup) or two tiles for the one-wavefront fp32 workgroup, and the many short
+// splits start at once.
 constexpr long kFastTargetSplits = 512;
 constexpr long kSlowTargetSplits = 256;
-constexpr int kMinTps = 8;
 constexpr int kMaxTps = kMaxTilesPerSplit;
 
-static int tiles_per_split(long total, long target) {
+static int tiles_per_split(const sfi_shape& s, long total, long target) {
+  const int min_tps = s.dtype == SFI_BF16 ? 4 : 2;
   long tps = (total + target - 1) / target;
-  return (int)(tps < kMinTps ? kMinTps : (tps > kMaxTps ? kMaxTps : tps));
+  return (int)(tps < min_tps ? min_tps : (tps > kMaxTps ? kMaxTps : tps));
 }
 
 SplitPlan plan_slow(const sfi_shape& s, int n_seqs, int max_seq_len) {
   SplitPlan sp;
   const int ntile = (max_seq_len + kPage - 1) / kPage;
-  const int tps = tiles_per_split((long)n_seqs * s.num_kv_heads * ntile, kSlowTargetSplits);
+  const int tps = tiles_per_split(s, (long)n_seqs * s.num_kv_heads * ntile, kSlowTargetSplits);
   sp.tps = tps;
   sp.nsplit = (ntile + tps - 1) / tps;
   sp.nsplit_a = 0;
@@ -651,7 +653,7 @@ SplitPlan plan_fast(const sfi_shape& s, int n_seqs, int packed_cap, int max_rece
   SplitPlan sp;
   const int ta = packed_cap / kPage;
   const int tb = (max_recent + kPage - 1) / kPage + 1;  // +1: the window need not start on a page
-  const int tps = tiles_per_split((long)n_seqs * s.num_kv_heads * (ta + tb), kFastTargetSplits);
+  const int tps = tiles_per_split(s, (long)n_seqs * s.num_kv_heads * (ta + tb), kFastTargetSplits);
   sp.tps = tps;
   sp.nsplit_a = (ta + tps - 1) / tps;
   sp.nsplit = sp.nsplit_a + (tb + tps - 1) / tps;
