@@ -120,7 +120,7 @@ class LayerBuffers:
 
 class Engine:
     def __init__(self, w, flags, device="cuda", two_streams: bool = True,
-                 dbg_scores: bool = False):
+                 dbg_scores: bool = False, sel_streams: int = 2):
         self.w = w
         self.device = torch.device(device)
         self.two_streams = two_streams
@@ -158,7 +158,7 @@ class Engine:
         # them, so the dependent kernel chains of two layers run side by side.  Each stream
         # has its own Selector workspace.  The debug score buffer is shared, so with it only
         # one stream is used.
-        n_sel = 2 if (two_streams and not dbg_scores) else 1
+        n_sel = max(1, sel_streams) if (two_streams and not dbg_scores) else 1
         sel_ws = max(L.sfi_select_ws(self.shape, self.params, n, self.max_len)
                      for n in range(1, B + 1))
         self.ws_sels = [L.workspace(sel_ws, dev) for _ in range(n_sel)]
@@ -171,6 +171,7 @@ class Engine:
         self.dbg = dbg_scores
         self.graph = None
         self.graphs = {}
+        self._calls = 0
         self.dbg_buf: Optional[torch.Tensor] = None
         if dbg_scores:
             self.dbg_buf = torch.zeros(B, w.num_kv_heads, self.stride, dtype=torch.float32,
@@ -290,8 +291,8 @@ class Engine:
         """Issue decode step s of every layer (no host synchronisation).
 
         dense_only runs the Full-KV baseline: dense attention for every sequence, no
-        Selector, no logits.  When `timer` is a list, the attention calls of every
-        `time_every`-th layer are bracketed by two events on stream 1 and
+        Selector, no logits.  When `timer` is a list, every `time_every`-th attention call
+        (counted over the engine's life) is bracketed by two events on stream 1 and
         (kind, start, end, algorithmic bytes, calls) is appended; a graph replay is
         bracketed as a whole (calls = layers).
         """
@@ -318,7 +319,10 @@ class Engine:
         ok = self._ok
 
         def timed(li, kind, nbytes, fn):
-            if timer is None or li % time_every:
+            # every time_every-th call of the engine's life is timed (a global count, so
+            # one-layer stacks are sampled as sparsely as deep ones)
+            self._calls += 1
+            if timer is None or (self._calls - 1) % time_every:
                 fn()
                 return
             e0 = torch.cuda.Event(enable_timing=True)
