@@ -202,14 +202,16 @@ def main():
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(eng.stream1)
-            eng.step(k % S, dense_only=True, timer=dense_timer)
+            eng.step(k % S, dense_only=True, timer=dense_timer,
+                     time_every=max(1, args.time_every))
             e1.record(eng.stream1)
             dt.append((e0, e1))
         torch.cuda.synchronize()
         dms = [a.elapsed_time(b) for a, b in dt]
         dk = [(e0.elapsed_time(e1), nb) for _, e0, e1, nb, _ in dense_timer]
         dense = {"step_ms": sum(dms) / len(dms),
-                 "gbs": sum(b for _, b in dk) / (sum(t for t, _ in dk) * 1e-3) / 1e9}
+                 "gbs": (sum(b for _, b in dk) / (sum(t for t, _ in dk) * 1e-3) / 1e9)
+                 if dk else None}
 
     ms_per_step = total_ms / steps
     value = steps * w.layers / (total_ms * 1e-3)
