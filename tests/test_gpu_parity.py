@@ -336,6 +336,47 @@ def test_ragged_batch_lengths():
         np.testing.assert_array_equal(lb.sel_idx[b].cpu().numpy(), ref_sel)
 
 
+def test_fast_and_pack_on_a_row_subset():
+    """Pack and fast attention serve only the rows listed in seq_ids (here rows 2 and 0 of
+    three, in that order, with their own lengths and recent starts); the other row's
+    outputs are left untouched."""
+    w = get("qwen3_0p6b_8k").replace(batch=3, context=2000, steps=4, name="row_subset")
+    d, eng, lb = _setup(w)
+    N0 = w.seq_len(0)
+    lens0 = torch.full((3,), N0, dtype=torch.int32, device="cuda")
+    L.sfi_slow_attn(eng.shape, d["q"][0], lb.k_cache, lb.v_cache, lb.block_table, lens0,
+                    eng.all_ids_d, 3, eng.max_len, lb.out, lb.logits, eng.stride, lb.lse,
+                    eng.ws_slow)
+    L.sfi_select(eng.shape, eng.params, lb.logits, eng.stride, lb.lse, lb.key_norm, eng.stride,
+                 lens0, eng.all_ids_d, 3, eng.max_len, lb.sel_idx, None, eng.ws_sel)
+    ids = torch.tensor([2, 0], dtype=torch.int32, device="cuda")
+    lb.packed_len.fill_(-5)
+    lb.packed_pos.fill_(-5)
+    L.sfi_pack(eng.shape, eng.params, lb.k_cache, lb.v_cache, lb.block_table, lb.sel_idx, ids,
+               2, lb.packed_k, lb.packed_v, lb.packed_pos, lb.packed_len, eng.packed_cap)
+    torch.cuda.synchronize()
+    assert bool((lb.packed_len[1] == -5).all()) and bool((lb.packed_pos[1] == -5).all())
+    # fast step of rows 2 and 0 at their own lengths
+    lens = torch.tensor([N0 + 3, N0, N0 + 2], dtype=torch.int32, device="cuda")
+    rs = O.recent_start_at(N0, w.n_sink, w.n_recent)
+    rstart = torch.full((3,), rs, dtype=torch.int32, device="cuda")
+    lb.out.fill_(123.0)
+    L.sfi_fast_attn(eng.shape, d["q"][1], lb.packed_k, lb.packed_v, lb.packed_len,
+                    eng.packed_cap, lb.k_cache, lb.v_cache, lb.block_table, rstart, lens, ids, 2,
+                    eng.max_recent, lb.out, None, eng.ws_fast)
+    torch.cuda.synchronize()
+    assert bool((lb.out[1] == 123.0).all())
+    out = host64(lb.out)
+    for b in (2, 0):
+        sel = lb.sel_idx[b].cpu().numpy()
+        pos = [O.packed_positions(sel[g], w.n_sink) for g in range(w.num_kv_heads)]
+        for g in range(w.num_kv_heads):
+            assert int(lb.packed_len[b, g]) == len(pos[g])
+        q, K, V = oracle_layer_arrays(d, b)
+        o, _ = O.fast_attention(q[1], K, V, pos, rs, int(lens[b]))
+        check_out(out[b], o, f"fast row {b}")
+
+
 # ------------------------------------------------------------ full-size sampled checks
 FULL = ["qwen3_4b_32k_b4", "qwen3_4b_128k_36l", "g16_64k_b8"]
 
