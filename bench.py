@@ -220,9 +220,13 @@ def main():
         try:
             import hashlib
             tj = json.load(open(args.traffic_json))
-            src = os.path.join(ROOT, "sparse_kv_attention_decode_amd", "csrc", "sfi_attn.hip")
-            digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-            # counters taken on another kernel or workload do not describe this run
+            pkg = os.path.join(ROOT, "sparse_kv_attention_decode_amd")
+            h = hashlib.sha256()
+            for f in (os.path.join(pkg, "csrc", "sfi_attn.hip"), os.path.join(pkg, "build.py")):
+                h.update(open(f, "rb").read())
+            digest = h.hexdigest()
+            # counters taken on another kernel (source or build flags) or workload do not
+            # describe this run
             if tj.get("workload") == w.name and tj.get("kernel_source_sha256") == digest:
                 traffic = tj.get("bytes_per_call")
         except (OSError, ValueError):

@@ -15,8 +15,12 @@ LIB = os.path.join(PKG, "libsfi.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 instructions are switched off for the device code: plain fp32 VALU only.
+# Matrix-core results are kept in ordinary VGPRs rather than accumulation registers: the
+# attention kernel reads most of its MFMA results with VALU instructions (the V transposes
+# and the logits), and the accumulation-register form cost a copy per value (32 per tile).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC,
          "-Wno-unused-result"]
 
