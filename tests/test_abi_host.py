@@ -204,3 +204,18 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load(str(tmp_path / "nope.so"))
     finally:
         importlib.reload(L)
+
+
+def test_topic_recall_counts_candidate_topics_only():
+    """The recall measurement: topics of the G query heads of a KV head, restricted to the
+    candidate range, found in that head's selection."""
+    import numpy as np
+    from sparse_kv_attention_decode_amd.recall import topic_recall
+    sel = np.array([[5, 9, 12, -1], [3, 4, -1, -1]])
+    topics = np.array([[5, 9, 2], [12, 30, 9],   # KV head 0 (query heads 0, 1)
+                       [3, 7, 50], [4, 7, 8]])   # KV head 1 (query heads 2, 3)
+    r = topic_recall(sel, topics, G=2, lo=4, hi=40)
+    # head 0: candidates {5, 9, 12, 30} (2 is below lo), selected {5, 9, 12} -> 3/4
+    # head 1: candidates {4, 7, 8} (3 below lo, 50 above hi), selected {4} -> 1/3
+    assert np.allclose(r, [0.75, 1 / 3])
+    assert np.isnan(topic_recall(sel[:1], np.array([[1, 2]]), G=1, lo=4, hi=40)[0])

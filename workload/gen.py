@@ -83,10 +83,12 @@ def span_starts(w: Workload, flags_row) -> list:
 
 
 def gen_queries(w: Workload, layer: int, K: torch.Tensor, flags: torch.Tensor,
-                device=None) -> torch.Tensor:
+                device=None, topics: Optional[list] = None) -> torch.Tensor:
     """Span-drift queries of one layer: [steps, B, Hq, D] fp32.
 
-    K is the layer's stored logical key tensor [B, Hkv, total_len, D].
+    K is the layer's stored logical key tensor [B, Hkv, total_len, D].  When `topics` is
+    a list, (b, s0, s1, positions [Hq, t]) is appended for every span: the topic positions
+    whose keys make up the span's query base (the support a selection should recover).
     """
     device = K.device if device is None else device
     gt = _gen(w, STREAM_TOPICS, layer, device)
@@ -111,6 +113,8 @@ def gen_queries(w: Workload, layer: int, K: torch.Tensor, flags: torch.Tensor,
                 pos = u.topk(t, dim=1).indices + lo                         # [Hq, t]
                 rows = K[b][kv_of_head[:, None], pos].to(torch.float32)   # [Hq, t, D]
                 base = rows.sum(dim=1)
+                if topics is not None:
+                    topics.append((b, s0, s1, pos.cpu()))
             noise = torch.randn(s1 - s0, Hq, D, generator=gn, device=device)
             q[s0:s1, b] = base[None] + w.query_noise * noise
     return q
@@ -146,14 +150,16 @@ def paginate(w: Workload, X: torch.Tensor, block_table: torch.Tensor,
 
 def make_layer(w: Workload, layer: int, device="cpu", keep_logical: bool = True):
     """All inputs of one layer.  Returns a dict with K/V (logical, optional), the paged
-    caches, the block table and the queries [steps, B, Hq, D]."""
+    caches, the block table, the queries [steps, B, Hq, D] and the spans' topic positions
+    (see gen_queries)."""
     K, V = gen_layer_kv(w, layer, device)
     flags = gen_flags(w, device)
-    q = gen_queries(w, layer, K, flags)
+    topics: list = []
+    q = gen_queries(w, layer, K, flags, topics=topics)
     bt = gen_block_table(w, layer, device)
     kc = paginate(w, K, bt)
     vc = paginate(w, V, bt)
-    out = dict(q=q, flags=flags, block_table=bt, k_cache=kc, v_cache=vc)
+    out = dict(q=q, flags=flags, block_table=bt, k_cache=kc, v_cache=vc, topics=topics)
     if keep_logical:
         out["K"], out["V"] = K, V
     else:
