@@ -19,7 +19,8 @@ Where the pages leave a step open, the plainest reading is taken; each reading i
 in the docstring of the function that applies it.
 
 Parity status of each function:
-  attention, merge_segments, evidence, fuse, topk, pack, fast_attention, schedule:
+  attention, merge_segments, evidence, window_evidence, window_queries, fuse, topk, pack,
+  fast_attention, schedule:
       pinned by tests (closed forms, library routines, brute force).
   key_norms: pinned (library norm).
   prior: invariants pinned (normalisation, positivity, monotonicity); the functional form
@@ -117,6 +118,35 @@ def evidence(p: np.ndarray, num_kv_heads: int) -> np.ndarray:
     Hq, N = p.shape
     G = Hq // num_kv_heads
     return p.reshape(num_kv_heads, G, N).mean(axis=1)
+
+
+def window_queries(q_steps: np.ndarray, s: int, window: int) -> np.ndarray:
+    """The queries of the slow step's window at decode step s: slot k holds the query of
+    step max(0, s - k), k < window.
+
+    The pages call the Selector's evidence the attention observed in the slow step's window
+    (es "Metodología / El Selector", zh "2.2 输入") without sizing the window.  Reading:
+    the window is the current decode query and the window - 1 decode queries before it;
+    before the first decode step there are none, so the first query fills the missing
+    slots.  q_steps [S, Hq, D] -> [window, Hq, D]."""
+    q_steps = np.asarray(q_steps, F64)
+    return np.stack([q_steps[max(0, s - k)] for k in range(window)])
+
+
+def window_evidence(P: np.ndarray, num_kv_heads: int) -> np.ndarray:
+    """Evidence f per KV head pooled over a window of queries (es "Metodología / El
+    Selector": the attention distribution observed in the slow step's window).  Reading:
+    every query of the window and every query head of the group weighs the same, so f of
+    KV head g is the mean over the window slots k and the G heads of g of the softmax
+    probabilities; each of them attends to all N positions of the current history (no
+    causal mask between the slots).  P [window, Hq, N] -> f [Hkv, N]."""
+    P = np.asarray(P, F64)
+    W, Hq, N = P.shape
+    G = Hq // num_kv_heads
+    f = np.zeros((num_kv_heads, N), F64)
+    for g in range(num_kv_heads):
+        f[g] = P[:, g * G:(g + 1) * G, :].sum(axis=(0, 1)) / (W * G)
+    return f
 
 
 def key_norms(K: np.ndarray) -> np.ndarray:
@@ -252,7 +282,22 @@ def select(p: np.ndarray, norms: np.ndarray, N: int, num_kv_heads: int, n_sink: 
            lam: float) -> Selection:
     """The whole Selector of one slow step: evidence, prior, fusion, refinement, Top-K.
     p [Hq, N] slow-step softmax probabilities; norms [Hkv, N] cached key norms."""
-    f = evidence(p, num_kv_heads)
+    return select_from_evidence(evidence(p, num_kv_heads), norms, N, n_sink, n_recent, top_k,
+                                R, alpha_soft, alpha_cross, lam)
+
+
+def select_window(P: np.ndarray, norms: np.ndarray, N: int, num_kv_heads: int, n_sink: int,
+                  n_recent: int, top_k: int, R: int, alpha_soft: float, alpha_cross: float,
+                  lam: float) -> Selection:
+    """The Selector with evidence pooled over a window of queries, P [window, Hq, N]."""
+    return select_from_evidence(window_evidence(P, num_kv_heads), norms, N, n_sink, n_recent,
+                                top_k, R, alpha_soft, alpha_cross, lam)
+
+
+def select_from_evidence(f: np.ndarray, norms: np.ndarray, N: int, n_sink: int,
+                         n_recent: int, top_k: int, R: int, alpha_soft: float,
+                         alpha_cross: float, lam: float) -> Selection:
+    """Prior, fusion, refinement and Top-K on given evidence f [Hkv, N]."""
     r = prior(norms[:, :N])
     s = fuse(f, r, lam)
     lo, hi = candidates(N, n_sink, n_recent)

@@ -141,6 +141,68 @@ def test_evidence_is_distribution():
     np.testing.assert_allclose(O.evidence(p, 8), p, atol=0)
 
 
+def test_window_evidence_worked_example():
+    """Two slots, two query heads of one KV head, three positions, summed by hand:
+    f = (0.5+0.2+1+0, 0.25+0.3+0+0, 0.25+0.5+0+1) / 4."""
+    P = np.array([[[0.5, 0.25, 0.25], [0.2, 0.3, 0.5]],
+                  [[1.0, 0.0, 0.0], [0.0, 0.0, 1.0]]])
+    np.testing.assert_allclose(O.window_evidence(P, 1), [[0.425, 0.1375, 0.4375]], atol=1e-15)
+
+
+def test_window_evidence_reduces_to_single_query_evidence():
+    q, K, V = _rand_qkv(Hq=8, Hkv=2, n=40, seed=12)
+    _, _, _, p = O.attention(q, K, V)
+    # a window of one slot, and a window whose slots all hold the same query
+    np.testing.assert_allclose(O.window_evidence(p[None], 2), O.evidence(p, 2), atol=1e-16)
+    np.testing.assert_allclose(O.window_evidence(np.stack([p] * 3), 2), O.evidence(p, 2),
+                               atol=1e-16)
+
+
+def test_window_evidence_is_the_mean_of_per_slot_evidence():
+    """Linearity: pooling over the window equals averaging each slot's own evidence; the
+    result is a distribution and does not depend on the order of the slots."""
+    r = np.random.default_rng(13)
+    Q = r.standard_normal((4, 8, 8))
+    _, K, V = _rand_qkv(Hq=8, Hkv=2, n=33, seed=13)
+    P = np.stack([O.attention(Q[k], K, V)[3] for k in range(4)])
+    f = O.window_evidence(P, 2)
+    np.testing.assert_allclose(f, np.mean([O.evidence(P[k], 2) for k in range(4)], axis=0),
+                               atol=1e-15)
+    np.testing.assert_allclose(f.sum(axis=1), 1.0, atol=1e-14)
+    np.testing.assert_allclose(O.window_evidence(P[[2, 0, 3, 1]], 2), f, atol=1e-15)
+
+
+def test_window_queries_slots():
+    q = np.arange(5 * 2 * 3, dtype=float).reshape(5, 2, 3)
+    Wq = O.window_queries(q, 3, 3)
+    for k, step in enumerate((3, 2, 1)):
+        np.testing.assert_array_equal(Wq[k], q[step])
+    # at the first steps the missing slots repeat the first query
+    np.testing.assert_array_equal(O.window_queries(q, 0, 3), np.stack([q[0]] * 3))
+    np.testing.assert_array_equal(O.window_queries(q, 1, 3), np.stack([q[1], q[0], q[0]]))
+
+
+def test_window_selector_keeps_what_each_slot_attends_to():
+    """Slot 0 attends to position 10, slot 1 to position 30 (one KV head, no prior, no
+    refinement).  With K = 2 the current query alone keeps 10 and its next-largest
+    position; the window keeps 10 and 30."""
+    N = 48
+    P = np.full((2, 1, N), 0.1 / (N - 1))
+    P[0, 0, 10] = 0.9
+    P[1, 0, 30] = 0.9
+    P[0, 0, 20] = P[0, 0, 20] + 1e-3
+    P[0, 0] /= P[0, 0].sum()
+    norms = np.ones((1, N))
+    kw = dict(N=N, num_kv_heads=1, n_sink=2, n_recent=4, top_k=2, R=0, alpha_soft=0.0,
+              alpha_cross=0.0, lam=0.0)
+    np.testing.assert_array_equal(O.select(P[0], norms, **kw).sel, [[10, 20]])
+    np.testing.assert_array_equal(O.select_window(P, norms, **kw).sel, [[10, 30]])
+    # identical slots: the window changes nothing
+    same = np.stack([P[0]] * 2)
+    np.testing.assert_array_equal(O.select_window(same, norms, **kw).sel,
+                                  O.select(P[0], norms, **kw).sel)
+
+
 def test_key_norms_library():
     K = rng.standard_normal((3, 20, 16))
     np.testing.assert_allclose(O.key_norms(K), np.sqrt((K ** 2).sum(-1)), rtol=1e-14)
