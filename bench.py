@@ -49,6 +49,9 @@ def _parse():
                          "fast-step graph")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue the Selector and pack on the attention stream")
+    ap.add_argument("--evidence-window", type=int, default=None,
+                    help="decode queries pooled into the Selector's evidence at a slow step "
+                         "(default: the workload's, 1)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a device copy of known size (for counter calibration)")
     ap.add_argument("--traffic-json",
@@ -132,6 +135,8 @@ def main():
     from sparse_kv_attention_decode_amd.engine import Engine
 
     w = get(args.workload)
+    if args.evidence_window is not None:
+        w = w.replace(evidence_window=args.evidence_window)
     steps = args.steps if args.steps is not None else w.steps
     t_setup = time.perf_counter()
     d0 = None
@@ -261,7 +266,8 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "top_k": w.top_k, "n_recent": w.n_recent,
                    "streams": 1 if args.one_stream else 2,
-                   "fast_step_graph": eng.graph is not None},
+                   "fast_step_graph": eng.graph is not None,
+                   "evidence_window": w.evidence_window},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SFI_ABI_VERSION 1
+#define SFI_ABI_VERSION 2
 
 enum sfi_status {
   SFI_OK = 0,
@@ -103,6 +103,12 @@ size_t sfi_fast_attn_ws(const sfi_shape* shape, int32_t n_seqs, int32_t packed_c
 size_t sfi_select_ws(const sfi_shape* shape, const sfi_select_params* params,
                      int32_t n_seqs, int32_t max_seq_len);
 
+/* The same for the query-window calls (sfi_slow_attn_window, sfi_select_window). */
+size_t sfi_slow_attn_window_ws(const sfi_shape* shape, int32_t window, int32_t n_seqs,
+                               int32_t max_seq_len);
+size_t sfi_select_window_ws(const sfi_shape* shape, const sfi_select_params* params,
+                            int32_t window, int32_t n_seqs, int32_t max_seq_len);
+
 /* Round-up of n_sink + top_k to a multiple of 16: rows per (b, KV head) of the packed
  * buffers. */
 int32_t sfi_packed_cap(const sfi_select_params* params);
@@ -133,6 +139,27 @@ int sfi_slow_attn(const sfi_shape* shape, const float* q, const void* k_cache,
                   void* stream);
 
 /*
+ * sfi_slow_attn_window -- a slow step whose evidence comes from a window of `window`
+ * queries per head instead of the current query alone (the pages describe the evidence as
+ * the attention observed in the slow step's window: es "Metodología / El Selector",
+ * zh "2.2 输入").  Slot 0 is the current query; the other slots are earlier decode queries
+ * chosen by the caller.  Every slot attends to all N_b positions (no causal mask between
+ * the slots).  The window's queries of KV head g are extra rows of its group, so K and V
+ * are read once for all of them.
+ *   q_win   f32 [batch, Hkv, window, G, D]   slot k of query head g*G + i at [b][g][k][i]
+ *   out     f32 [batch, Hq, D]               slot 0 only: the step's attention output
+ *   lse     f32 [batch, Hkv, window, G]      every slot
+ *   logits  f32 [batch, Hkv, window, G, logits_stride]  every slot (or NULL)
+ * Requires window >= 1 (SFI_E_ARG) and G * window <= 16 (SFI_E_UNSUPPORTED); window 1 is
+ * sfi_slow_attn.  ws: sfi_slow_attn_window_ws(shape, window, n_seqs, max_seq_len) bytes.
+ */
+int sfi_slow_attn_window(const sfi_shape* shape, int32_t window, const float* q_win,
+                         const void* k_cache, const void* v_cache, const int32_t* block_table,
+                         const int32_t* seq_lens, const int32_t* seq_ids, int32_t n_seqs,
+                         int32_t max_seq_len, float* out, float* logits, int64_t logits_stride,
+                         float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * sfi_select -- the training-free Selector of a slow step (zh "2.2", fr "2.B",
  * nl "De Selector"), per listed row b and KV head g, at N = N_b:
  *   f(g,j)  = mean over the G query heads of g of exp(z(h,j) - lse(h))
@@ -156,6 +183,20 @@ int sfi_select(const sfi_shape* shape, const sfi_select_params* params, const fl
                int64_t norm_stride, const int32_t* seq_lens, const int32_t* seq_ids,
                int32_t n_seqs, int32_t max_seq_len, int32_t* sel_idx, float* dbg_scores,
                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sfi_select_window -- sfi_select on the logits and lse of sfi_slow_attn_window: the
+ * evidence f(g,j) is the mean of exp(z - lse) over the G * window rows of KV head g (every
+ * query of the window weighs the same); prior, fusion, refinement and Top-K are those of
+ * sfi_select.  Same limits as sfi_slow_attn_window.
+ * ws: sfi_select_window_ws(shape, params, window, n_seqs, max_seq_len) bytes.
+ */
+int sfi_select_window(const sfi_shape* shape, const sfi_select_params* params, int32_t window,
+                      const float* logits, int64_t logits_stride, const float* lse,
+                      const float* key_norm, int64_t norm_stride, const int32_t* seq_lens,
+                      const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len,
+                      int32_t* sel_idx, float* dbg_scores, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /*
  * sfi_pack -- gather the sink rows [0, n_sink) and the selected rows sel_idx[b][g][*]

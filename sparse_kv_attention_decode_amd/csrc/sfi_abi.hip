@@ -112,11 +112,31 @@ int sfi_key_norms(const sfi_shape* shape, const void* k_cache, const int32_t* bl
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
-int sfi_slow_attn(const sfi_shape* shape, const float* q, const void* k_cache,
-                  const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                  const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len, float* out,
-                  float* logits, int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The model's shape with every query head repeated `window` times: the row layout of a
+// windowed slow step.  Returns SFI_E_ARG for window < 1 and SFI_E_UNSUPPORTED when the
+// repeated group exceeds the kernels' group limit.
+int window_shape(const sfi_shape* shape, int32_t window, sfi_shape* out) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (window < 1) return SFI_E_ARG;
+  if ((int64_t)(shape->num_q_heads / shape->num_kv_heads) * window > sfi::kMaxGroup)
+    return SFI_E_UNSUPPORTED;
+  *out = *shape;
+  out->num_q_heads = shape->num_q_heads * window;
+  return SFI_OK;
+}
+
+// Dense attention of the rows of `shape` (already widened by the window); the output is
+// written for window slot 0 only.
+int slow_attn(const sfi_shape* shape, int32_t window, const float* q, const void* k_cache,
+              const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+              const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len, float* out,
+              float* logits, int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
+              void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !seq_ids || !out || !lse)
@@ -156,9 +176,42 @@ int sfi_slow_attn(const sfi_shape* shape, const float* q, const void* k_cache,
   p.nsplit = sp.nsplit;
   p.nsplit_a = 0;
   p.fast = 0;
+  p.win = window;
   p.scale = 1.0f / sqrtf((float)shape->head_dim);
   return finish(sfi::launch_attention(p, shape->head_dim, shape->dtype, out, lse,
                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int sfi_slow_attn(const sfi_shape* shape, const float* q, const void* k_cache,
+                  const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                  const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len, float* out,
+                  float* logits, int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
+                  void* stream) {
+  return slow_attn(shape, 1, q, k_cache, v_cache, block_table, seq_lens, seq_ids, n_seqs,
+                   max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes, stream);
+}
+
+size_t sfi_slow_attn_window_ws(const sfi_shape* shape, int32_t window, int32_t n_seqs,
+                               int32_t max_seq_len) {
+  sfi_shape sw;
+  if (window_shape(shape, window, &sw) != SFI_OK) return 0;
+  return sfi_slow_attn_ws(&sw, n_seqs, max_seq_len);
+}
+
+int sfi_slow_attn_window(const sfi_shape* shape, int32_t window, const float* q_win,
+                         const void* k_cache, const void* v_cache, const int32_t* block_table,
+                         const int32_t* seq_lens, const int32_t* seq_ids, int32_t n_seqs,
+                         int32_t max_seq_len, float* out, float* logits, int64_t logits_stride,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+  sfi_shape sw;
+  int rc = window_shape(shape, window, &sw);
+  if (rc) return rc;
+  return slow_attn(&sw, window, q_win, k_cache, v_cache, block_table, seq_lens, seq_ids, n_seqs,
+                   max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes, stream);
 }
 
 int sfi_select(const sfi_shape* shape, const sfi_select_params* params, const float* logits,
@@ -184,6 +237,28 @@ int sfi_select(const sfi_shape* shape, const sfi_select_params* params, const fl
   return finish(sfi::launch_select(*shape, *params, logits, logits_stride, lse, key_norm,
                                    norm_stride, seq_lens, seq_ids, n_seqs, max_seq_len, sel_idx,
                                    dbg_scores, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t sfi_select_window_ws(const sfi_shape* shape, const sfi_select_params* params,
+                            int32_t window, int32_t n_seqs, int32_t max_seq_len) {
+  sfi_shape sw;
+  if (window_shape(shape, window, &sw) != SFI_OK) return 0;
+  return sfi_select_ws(&sw, params, n_seqs, max_seq_len);
+}
+
+int sfi_select_window(const sfi_shape* shape, const sfi_select_params* params, int32_t window,
+                      const float* logits, int64_t logits_stride, const float* lse,
+                      const float* key_norm, int64_t norm_stride, const int32_t* seq_lens,
+                      const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len,
+                      int32_t* sel_idx, float* dbg_scores, void* ws, size_t ws_bytes,
+                      void* stream) {
+  // The evidence of KV head g is the mean over its G * window rows: the Selector of the
+  // widened shape computes exactly that.
+  sfi_shape sw;
+  int rc = window_shape(shape, window, &sw);
+  if (rc) return rc;
+  return sfi_select(&sw, params, logits, logits_stride, lse, key_norm, norm_stride, seq_lens,
+                    seq_ids, n_seqs, max_seq_len, sel_idx, dbg_scores, ws, ws_bytes, stream);
 }
 
 int sfi_pack(const sfi_shape* shape, const sfi_select_params* params, const void* k_cache,
@@ -256,6 +331,7 @@ int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
   p.nsplit = sp.nsplit;
   p.nsplit_a = sp.nsplit_a;
   p.fast = 1;
+  p.win = 1;
   p.scale = 1.0f / sqrtf((float)shape->head_dim);
   return finish(sfi::launch_attention(p, shape->head_dim, shape->dtype, out, lse,
                                       reinterpret_cast<hipStream_t>(stream)));

@@ -525,13 +525,17 @@ __global__ __launch_bounds__(64) void k_attn_partial_f32(AttnParams p) {
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm,
                                                     const float* __restrict__ pl,
                                                     const float* __restrict__ po, int nsplit,
-                                                    int Hq, int Hkv, int G, int D,
+                                                    int Hq, int Hkv, int G, int D, int win,
                                                     const int32_t* __restrict__ seq_ids,
                                                     float* __restrict__ out,
                                                     float* __restrict__ lse) {
   // Thread (grp, col) folds splits grp, grp + ngrp, ... of column block col into a running
   // (max, sum, weighted o); the loads of kUnroll splits are issued together.  The groups
   // are then combined in LDS.
+  //
+  // With a query window (win > 1) the G rows of a KV head are win slots of G / win heads;
+  // lse is written for every row, the output only for slot 0 (the current query), into
+  // the [batch][Hq / win][D] layout of the model's own heads.
   constexpr int kUnroll = 8;
   __shared__ float gm[64], gl[64];
   __shared__ float4 acc4[256];
@@ -595,8 +599,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm
       o.w += w * x.w;
     }
     const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-    reinterpret_cast<float4*>(out + ((size_t)b * Hq + h) * D)[col] =
-        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    const int G0 = G / win;
+    if (hh < G0)
+      reinterpret_cast<float4*>(out + ((size_t)b * (Hq / win) + g * G0 + hh) * D)[col] =
+          make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
     if (col == 0 && lse) lse[(size_t)b * Hq + h] = Lt > 0.f ? Mu + logf(Lt) : -INFINITY;
   }
 }
@@ -674,8 +680,8 @@ hipError_t launch_attention(const AttnParams& p0, int head_dim, int dtype, float
                                 : launch_partial<128>(p, dtype, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_merge, dim3(p.n_seqs * p.Hq), dim3(256), 0, stream, p.part_m,
-                     p.part_l, p.part_o, p.nsplit, p.Hq, p.Hkv, p.G, head_dim, p.seq_ids, out,
-                     lse);
+                     p.part_l, p.part_o, p.nsplit, p.Hq, p.Hkv, p.G, head_dim, p.win, p.seq_ids,
+                     out, lse);
   return hipGetLastError();
 }
 

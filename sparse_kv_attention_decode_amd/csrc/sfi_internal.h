@@ -46,6 +46,7 @@ struct AttnParams {
   int n_seqs, Hq, Hkv, G;
   int tps, nsplit, nsplit_a;
   int fast;
+  int win;                     // query-window slots per head (1: no window)
   float scale;
 };
 

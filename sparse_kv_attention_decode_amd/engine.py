@@ -5,7 +5,10 @@ Step s of every listed sequence is SLOW when s == 0, when its boundary flag is s
 `refresh_budget` fast steps have run since its last slow step, and FAST otherwise (es
 "Pasos Lentos", zh "2.1 触发机制").  A slow step runs dense attention and then the Selector
 and the pack for that layer; a fast step runs two-segment attention over the packed
-buffer and the recent window.
+buffer and the recent window.  With an evidence window of w > 1 queries, a slow step's
+dense attention also runs the w - 1 decode queries before the current one (as extra rows
+of each KV head's group, so K and V are read once) and the Selector pools their
+attention with the current query's.
 
 Overlap (es "3. Optimización del Sistema / Pipeline Asíncrono", zh "2.3 异步流水线"): the
 attention of every layer is issued on stream 1; the Selector and pack of layer i are
@@ -94,18 +97,35 @@ def make_plan(flags: np.ndarray, context: int, budget: int, n_sink: int, n_recen
 kGraphMinLayers = 8
 
 
+def window_query_table(q_all: torch.Tensor, num_kv_heads: int, window: int) -> torch.Tensor:
+    """Query layout of windowed slow steps: [S, B, Hkv, window, G, D] (flattened to
+    [S, B, Hq * window, D]) with slot k of step s holding the query of step max(0, s - k):
+    the current decode query and the ones before it, the first query filling the slots
+    before the first step."""
+    S, B, Hq, D = q_all.shape
+    G = Hq // num_kv_heads
+    src = torch.arange(S, device=q_all.device)
+    qg = q_all.view(S, B, num_kv_heads, G, D)
+    slots = [qg[(src - k).clamp_min(0)] for k in range(window)]
+    return torch.stack(slots, dim=3).reshape(S, B, Hq * window, D).contiguous()
+
+
 class LayerBuffers:
     """Device state of one attention layer."""
 
     def __init__(self, eng: "Engine", k_cache, v_cache, block_table, q_all):
         w, dev = eng.w, eng.device
         B, Hq, Hkv, D = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+        win = eng.window
         self.k_cache, self.v_cache = k_cache, v_cache
         self.block_table = block_table.to(dev, torch.int32).contiguous()
         self.q_all = q_all                       # [S, B, Hq, D] fp32
+        # Slow steps with a query window read q_win[s] [B, Hkv, win, G, D]: slot k holds the
+        # query of step max(0, s - k).
+        self.q_win = window_query_table(q_all, Hkv, win) if win > 1 else None
         self.key_norm = torch.zeros(B, Hkv, eng.stride, dtype=torch.float32, device=dev)
-        self.logits = torch.zeros(B, Hq, eng.stride, dtype=torch.float32, device=dev)
-        self.lse = torch.zeros(B, Hq, dtype=torch.float32, device=dev)
+        self.logits = torch.zeros(B, Hq * win, eng.stride, dtype=torch.float32, device=dev)
+        self.lse = torch.zeros(B, Hq * win, dtype=torch.float32, device=dev)
         self.sel_idx = torch.full((B, Hkv, w.top_k), -1, dtype=torch.int32, device=dev)
         dt = k_cache.dtype
         self.packed_k = torch.zeros(B, Hkv, eng.packed_cap, D, dtype=dt, device=dev)
@@ -120,9 +140,13 @@ class LayerBuffers:
 
 class Engine:
     def __init__(self, w, flags, device="cuda", two_streams: bool = True,
-                 dbg_scores: bool = False, sel_streams: int = 2):
+                 dbg_scores: bool = False, sel_streams: int = 2,
+                 window: Optional[int] = None):
         self.w = w
         self.device = torch.device(device)
+        # Decode queries pooled into the Selector's evidence at a slow step (1: the current
+        # query only).
+        self.window = int(w.evidence_window if window is None else window)
         self.two_streams = two_streams
         flags_np = np.asarray(flags.cpu() if torch.is_tensor(flags) else flags)
         self.plan = make_plan(flags_np, w.context, w.refresh_budget, w.n_sink, w.n_recent,
@@ -149,8 +173,11 @@ class Engine:
         self.all_ids_d = torch.arange(B, dtype=torch.int32, device=dev)
         # The split plan depends on the number of rows in a call, so size each workspace
         # for the largest requirement over every row count a step can pass.
-        self.ws_slow = L.workspace(max(L.sfi_slow_attn_ws(self.shape, n, self.max_len)
-                                       for n in range(1, B + 1)), dev)
+        win = self.window
+        self.ws_slow = L.workspace(max(
+            max(L.sfi_slow_attn_ws(self.shape, n, self.max_len),
+                L.sfi_slow_attn_window_ws(self.shape, win, n, self.max_len))
+            for n in range(1, B + 1)), dev)
         self.ws_fast = L.workspace(
             max(L.sfi_fast_attn_ws(self.shape, n, self.packed_cap, self.max_recent)
                 for n in range(1, B + 1)), dev)
@@ -159,8 +186,11 @@ class Engine:
         # has its own Selector workspace.  The debug score buffer is shared, so with it only
         # one stream is used.
         n_sel = max(1, sel_streams) if (two_streams and not dbg_scores) else 1
-        sel_ws = max(L.sfi_select_ws(self.shape, self.params, n, self.max_len)
+        sel_ws = max(L.sfi_select_window_ws(self.shape, self.params, win, n, self.max_len)
                      for n in range(1, B + 1))
+        if sel_ws == 0:
+            raise ValueError(f"evidence window {win} is not supported for this shape "
+                             f"(window >= 1 and group * window <= 16)")
         self.ws_sels = [L.workspace(sel_ws, dev) for _ in range(n_sel)]
         self.ws_sel = self.ws_sels[0]
         self.stream1 = torch.cuda.Stream(device=dev)
@@ -240,6 +270,11 @@ class Engine:
                 ("pk", "packed_k"), ("pv", "packed_v"), ("pp", "packed_pos"),
                 ("pl", "packed_len"), ("out", "out"))}
             lb.q_step = lb.q_all[0].numel() * lb.q_all.element_size()
+            if lb.q_win is not None:
+                lb.ptr["qw"] = lb.q_win.data_ptr()
+                lb.qw_step = lb.q_win[0].numel() * lb.q_win.element_size()
+            else:
+                lb.ptr["qw"], lb.qw_step = lb.ptr["q"], lb.q_step
         self._bound_layers = len(self.layers)
 
     def enable_graphs(self, min_layers: int = kGraphMinLayers) -> None:
@@ -317,6 +352,7 @@ class Engine:
         ws_slow, ws_slow_n = self._ws["slow"]
         ws_fast, ws_fast_n = self._ws["fast"]
         ok = self._ok
+        win = self.window
 
         def timed(li, kind, nbytes, fn):
             # every time_every-th call of the engine's life is timed (a global count, so
@@ -352,17 +388,20 @@ class Engine:
                     P["bt"], rstart, seq_len, fast_ids, n_fast, self.max_recent, P["out"],
                     None, ws_fast, ws_fast_n, h1)))
             if n_slow:
-                timed(li, "slow", db, lambda: ok("sfi_slow_attn", lib.sfi_slow_attn(
-                    shp, q, P["k"], P["v"], P["bt"], seq_len, slow_ids, n_slow, self.max_len,
-                    P["out"], P["z"], self.stride, P["lse"], ws_slow, ws_slow_n, h1)))
+                qw = P["qw"] + s * lb.qw_step
+                timed(li, "slow", db, lambda: ok(
+                    "sfi_slow_attn_window", lib.sfi_slow_attn_window(
+                        shp, win, qw, P["k"], P["v"], P["bt"], seq_len, slow_ids, n_slow,
+                        self.max_len, P["out"], P["z"], self.stride, P["lse"], ws_slow,
+                        ws_slow_n, h1)))
                 k = li % len(self.sel_streams)
                 s2, h2 = self.sel_streams[k], self._h2[k]
                 ws_sel, ws_sel_n = self._ws_sel[k]
                 if s2 is not s1:
                     lb.ev_attn.record(s1)
                     s2.wait_event(lb.ev_attn)
-                ok("sfi_select", lib.sfi_select(
-                    shp, prm, P["z"], self.stride, P["lse"], P["norm"], self.stride, seq_len,
+                ok("sfi_select_window", lib.sfi_select_window(
+                    shp, prm, win, P["z"], self.stride, P["lse"], P["norm"], self.stride, seq_len,
                     slow_ids, n_slow, self.max_len, P["sel"], self._dbg_p, ws_sel, ws_sel_n,
                     h2))
                 ok("sfi_pack", lib.sfi_pack(

@@ -22,7 +22,8 @@ SFI_BF16, SFI_F32 = 0, 1
 
 EXPORTS = ["sfi_abi_version", "sfi_status_str", "sfi_slow_attn_ws", "sfi_fast_attn_ws",
            "sfi_select_ws", "sfi_packed_cap", "sfi_key_norms", "sfi_slow_attn", "sfi_select",
-           "sfi_pack", "sfi_fast_attn"]
+           "sfi_pack", "sfi_fast_attn", "sfi_slow_attn_window_ws", "sfi_select_window_ws",
+           "sfi_slow_attn_window", "sfi_select_window"]
 
 
 class SfiShape(ctypes.Structure):
@@ -67,6 +68,12 @@ _SIGS = {
     "sfi_select": (ctypes.c_int, [_SHP, _PRM, _P, _I64, _P, _P, _I64, _P, _P, _I32, _I32, _P, _P,
                                   _P, _SZ, _P]),
     "sfi_pack": (ctypes.c_int, [_SHP, _PRM, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32, _P]),
+    "sfi_slow_attn_window_ws": (_SZ, [_SHP, _I32, _I32, _I32]),
+    "sfi_select_window_ws": (_SZ, [_SHP, _PRM, _I32, _I32, _I32]),
+    "sfi_slow_attn_window": (ctypes.c_int, [_SHP, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _P,
+                                            _P, _I64, _P, _P, _SZ, _P]),
+    "sfi_select_window": (ctypes.c_int, [_SHP, _PRM, _I32, _P, _I64, _P, _P, _I64, _P, _P, _I32,
+                                         _I32, _P, _P, _P, _SZ, _P]),
     "sfi_fast_attn": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32,
                                      _I32, _P, _P, _P, _SZ, _P]),
 }
@@ -137,6 +144,16 @@ def sfi_select_ws(shape: SfiShape, params: SfiSelectParams, n_seqs: int, max_seq
     return load().sfi_select_ws(ctypes.byref(shape), ctypes.byref(params), n_seqs, max_seq_len)
 
 
+def sfi_slow_attn_window_ws(shape: SfiShape, window: int, n_seqs: int, max_seq_len: int) -> int:
+    return load().sfi_slow_attn_window_ws(ctypes.byref(shape), window, n_seqs, max_seq_len)
+
+
+def sfi_select_window_ws(shape: SfiShape, params: SfiSelectParams, window: int, n_seqs: int,
+                         max_seq_len: int) -> int:
+    return load().sfi_select_window_ws(ctypes.byref(shape), ctypes.byref(params), window, n_seqs,
+                                       max_seq_len)
+
+
 def sfi_packed_cap(params: SfiSelectParams) -> int:
     return load().sfi_packed_cap(ctypes.byref(params))
 
@@ -170,6 +187,18 @@ def sfi_slow_attn(shape, q, k_cache, v_cache, block_table, seq_lens, seq_ids, n_
     _check("sfi_slow_attn", rc)
 
 
+def sfi_slow_attn_window(shape, window, q_win, k_cache, v_cache, block_table, seq_lens, seq_ids,
+                         n_seqs, max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes=None,
+                         stream=None) -> None:
+    ws_bytes = ws.numel() if ws_bytes is None else ws_bytes
+    rc = load().sfi_slow_attn_window(ctypes.byref(shape), window, _ptr(q_win), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                     _ptr(seq_ids), n_seqs, max_seq_len, _ptr(out), _ptr(logits),
+                                     logits_stride, _ptr(lse), _ptr(ws), ws_bytes,
+                                     _stream(stream))
+    _check("sfi_slow_attn_window", rc)
+
+
 def sfi_select(shape, params, logits, logits_stride, lse, key_norm, norm_stride, seq_lens,
                seq_ids, n_seqs, max_seq_len, sel_idx, dbg_scores, ws, ws_bytes=None,
                stream=None) -> None:
@@ -179,6 +208,18 @@ def sfi_select(shape, params, logits, logits_stride, lse, key_norm, norm_stride,
                            _ptr(seq_lens), _ptr(seq_ids), n_seqs, max_seq_len, _ptr(sel_idx),
                            _ptr(dbg_scores), _ptr(ws), ws_bytes, _stream(stream))
     _check("sfi_select", rc)
+
+
+def sfi_select_window(shape, params, window, logits, logits_stride, lse, key_norm, norm_stride,
+                      seq_lens, seq_ids, n_seqs, max_seq_len, sel_idx, dbg_scores, ws,
+                      ws_bytes=None, stream=None) -> None:
+    ws_bytes = ws.numel() if ws_bytes is None else ws_bytes
+    rc = load().sfi_select_window(ctypes.byref(shape), ctypes.byref(params), window,
+                                  _ptr(logits), logits_stride, _ptr(lse), _ptr(key_norm),
+                                  norm_stride, _ptr(seq_lens), _ptr(seq_ids), n_seqs,
+                                  max_seq_len, _ptr(sel_idx), _ptr(dbg_scores), _ptr(ws),
+                                  ws_bytes, _stream(stream))
+    _check("sfi_select_window", rc)
 
 
 def sfi_pack(shape, params, k_cache, v_cache, block_table, sel_idx, seq_ids, n_seqs, packed_k,

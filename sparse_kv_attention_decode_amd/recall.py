@@ -9,6 +9,10 @@ of the span's topic positions -- those of the G query heads of each KV head that
 candidates [n_sink, N - W) -- that the KV head's selection contains.  It is a model-free proxy
 for the pages' ablation of the prior fusion and the score refinement (zh "4 实验结果").
 
+A setting may also pool the evidence over a window of decode queries.  Then every setting is
+measured at the step window_max - 1 after the span start (spans shorter than that are
+skipped), so that all windows lie inside the span and all settings see the same steps.
+
     python -m sparse_kv_attention_decode_amd.recall --workload qwen3_4b_32k_b4
 """
 from __future__ import annotations
@@ -59,30 +63,40 @@ def default_settings(w) -> List[Dict]:
 
 def run(w, settings: Optional[List[Dict]] = None, layer: int = 0, device: str = "cuda"):
     from workload.gen import make_layer
+    from sparse_kv_attention_decode_amd.engine import window_query_table
     settings = default_settings(w) if settings is None else settings
+    wmax = max(st.get("window", 1) for st in settings)
     d = make_layer(w, layer, device=device, keep_logical=False)
-    eng = Engine(w, d["flags"], device=device)
+    # sized for the widest window: logits, lse and the slow workspace
+    eng = Engine(w, d["flags"], device=device, window=wmax)
     lb = eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
     B, G = w.batch, w.group
-    by_start: Dict[int, list] = {}
+    q_tables = {1: d["q"]}
+    by_step: Dict[int, list] = {}
     for b, s0, s1, pos in d["topics"]:
-        by_start.setdefault(s0, []).append((b, pos.numpy()))
+        s = s0 + wmax - 1
+        if s < s1:
+            by_step.setdefault(s, []).append((b, pos.numpy()))
     results = []
     for st in settings:
+        win = st.get("window", 1)
+        if win not in q_tables:
+            q_tables[win] = window_query_table(d["q"], w.num_kv_heads, win)
         params = L.make_params(w.n_sink, w.n_recent, st["top_k"], w.nms_radius, st["lam"],
                                st["alpha_soft"], st["alpha_cross"])
         sel_buf = torch.full((B, w.num_kv_heads, st["top_k"]), -1, dtype=torch.int32,
                              device=device)
-        ws = L.workspace(L.sfi_select_ws(eng.shape, params, B, eng.max_len), device)
+        ws = L.workspace(L.sfi_select_window_ws(eng.shape, params, win, B, eng.max_len), device)
         rec, rnd = [], []
-        for s0, rows in sorted(by_start.items()):
-            N = w.seq_len(s0)
+        for s, rows in sorted(by_step.items()):
+            N = w.seq_len(s)
             lens = torch.full((B,), N, dtype=torch.int32, device=device)
-            L.sfi_slow_attn(eng.shape, d["q"][s0], lb.k_cache, lb.v_cache, lb.block_table,
-                            lens, eng.all_ids_d, B, eng.max_len, lb.out, lb.logits, eng.stride,
-                            lb.lse, eng.ws_slow)
-            L.sfi_select(eng.shape, params, lb.logits, eng.stride, lb.lse, lb.key_norm,
-                         eng.stride, lens, eng.all_ids_d, B, eng.max_len, sel_buf, None, ws)
+            L.sfi_slow_attn_window(eng.shape, win, q_tables[win][s], lb.k_cache, lb.v_cache,
+                                   lb.block_table, lens, eng.all_ids_d, B, eng.max_len, lb.out,
+                                   lb.logits, eng.stride, lb.lse, eng.ws_slow)
+            L.sfi_select_window(eng.shape, params, win, lb.logits, eng.stride, lb.lse,
+                                lb.key_norm, eng.stride, lens, eng.all_ids_d, B, eng.max_len,
+                                sel_buf, None, ws)
             torch.cuda.synchronize()
             sel = sel_buf.cpu().numpy()
             lo, hi = w.n_sink, max(w.n_sink, N - w.n_recent)
@@ -90,8 +104,9 @@ def run(w, settings: Optional[List[Dict]] = None, layer: int = 0, device: str = 
                 r = topic_recall(sel[b], pos, G, lo, hi)
                 rec.extend(r[~np.isnan(r)].tolist())
                 rnd.append(min(1.0, st["top_k"] / max(1, hi - lo)))
-        results.append(dict(st, recall=float(np.mean(rec)), recall_min=float(np.min(rec)),
-                            random=float(np.mean(rnd)), samples=len(rec)))
+        results.append(dict(st, window=win, recall=float(np.mean(rec)),
+                            recall_min=float(np.min(rec)), random=float(np.mean(rnd)),
+                            samples=len(rec)))
     return results
 
 
@@ -103,6 +118,11 @@ def main() -> None:
                     help="override the topic positions per query head and span")
     ap.add_argument("--sigma", type=float, default=None,
                     help="override the log-normal key-scale sigma")
+    ap.add_argument("--query-noise", type=float, default=None,
+                    help="override the std of the per-step query noise")
+    ap.add_argument("--windows", default=None,
+                    help="comma-separated evidence windows: run the workload setting with "
+                         "each instead of the default table")
     a = ap.parse_args()
     w = get(a.workload)
     over = {}
@@ -110,19 +130,26 @@ def main() -> None:
         over["n_topics"] = a.n_topics
     if a.sigma is not None:
         over["key_scale_sigma"] = a.sigma
+    if a.query_noise is not None:
+        over["query_noise"] = a.query_noise
     name = a.workload
     if over:
         name += " " + ", ".join(f"{k}={v}" for k, v in over.items())
         w = w.replace(name=w.name + "_recall_" + "_".join(f"{k}{v}" for k, v in over.items()),
                       **over)
-    res = run(w)
-    print(f"| setting ({name}) | K | lambda | alpha_soft | alpha_cross | topic recall "
+    settings = None
+    if a.windows:
+        base = default_settings(w)[0]
+        settings = [dict(base, window=int(x), label=f"window {int(x)}")
+                    for x in a.windows.split(",")]
+    res = run(w, settings)
+    print(f"| setting ({name}) | K | lambda | alpha_soft | alpha_cross | window | topic recall "
           f"(mean / min over spans x KV heads) | K/|C| (random) |")
-    print("|---|---|---|---|---|---|---|")
+    print("|---|---|---|---|---|---|---|---|")
     for r in res:
         print(f"| {r['label']} | {r['top_k']} | {r['lam']} | {r['alpha_soft']} | "
-              f"{r['alpha_cross']} | {r['recall']:.3f} / {r['recall_min']:.3f} "
-              f"(n={r['samples']}) | {r['random']:.3f} |")
+              f"{r['alpha_cross']} | {r['window']} | {r['recall']:.3f} / "
+              f"{r['recall_min']:.3f} (n={r['samples']}) | {r['random']:.3f} |")
 
 
 if __name__ == "__main__":

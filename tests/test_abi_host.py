@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     assert sorted(L.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert L.sfi_abi_version() == 1
+    assert L.sfi_abi_version() == 2
 
 
 def test_status_strings():
@@ -135,6 +135,43 @@ def test_select_validation():
     assert L.sfi_select_ws(big, p, 1, (1 << 22) + 1) == 0
     assert _select(big, p, maxlen=(1 << 22) + 1, lstride=stride, nstride=stride) == \
         L.SFI_E_UNSUPPORTED
+
+
+def test_window_calls_validate_and_size_like_the_widened_shape():
+    """A window of w slots is the model's shape with Hq * w query heads (G * w <= 16)."""
+    s, p = _shape(), _params()              # Hq 8, Hkv 2: G = 4
+    lib = L.load()
+    for n, maxlen in ((1, 100), (2, 1000)):
+        assert L.sfi_slow_attn_window_ws(s, 1, n, maxlen) == L.sfi_slow_attn_ws(s, n, maxlen)
+        assert L.sfi_select_window_ws(s, p, 1, n, maxlen) == L.sfi_select_ws(s, p, n, maxlen)
+        wide = _shape(num_q_heads=32)
+        assert L.sfi_slow_attn_window_ws(s, 4, n, maxlen) == L.sfi_slow_attn_ws(wide, n, maxlen)
+        assert L.sfi_select_window_ws(s, p, 4, n, maxlen) == L.sfi_select_ws(wide, p, n, maxlen)
+    assert L.sfi_slow_attn_window_ws(s, 0, 1, 100) == 0
+    assert L.sfi_slow_attn_window_ws(s, 5, 1, 100) == 0      # G * w = 20 > 16
+    assert L.sfi_select_window_ws(s, p, 5, 1, 100) == 0
+
+    def slow_w(win, **over):
+        a = dict(q=FAKE, n=1, ws=FAKE, wsb=1 << 40)
+        a.update(over)
+        return lib.sfi_slow_attn_window(ctypes.byref(s), win, a["q"], FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, a["n"], 100, FAKE, FAKE, 128, FAKE, a["ws"],
+                                        a["wsb"], None)
+
+    def select_w(win):
+        return lib.sfi_select_window(ctypes.byref(s), ctypes.byref(p), win, FAKE, 128, FAKE, FAKE,
+                                     128, FAKE, FAKE, 1, 100, FAKE, None, FAKE, 1 << 40, None)
+
+    assert slow_w(0) == L.SFI_E_ARG
+    assert slow_w(-3) == L.SFI_E_ARG
+    assert slow_w(5) == L.SFI_E_UNSUPPORTED
+    assert slow_w(2, q=None) == L.SFI_E_ARG
+    assert slow_w(2, q=MIS) == L.SFI_E_ALIGN
+    assert slow_w(2, ws=None) == L.SFI_E_WORKSPACE
+    assert slow_w(2, wsb=L.sfi_slow_attn_window_ws(s, 2, 1, 100) - 1) == L.SFI_E_WORKSPACE
+    assert slow_w(4, n=0) == L.SFI_OK                         # no rows: nothing to launch
+    assert select_w(0) == L.SFI_E_ARG
+    assert select_w(5) == L.SFI_E_UNSUPPORTED
 
 
 def _pack(shape, params, **over):

@@ -155,13 +155,15 @@ def test_pack_bit_exact(name):
             assert bool((_bits(pk[g, n:]) == 0).all()) and bool((_bits(pv[g, n:]) == 0).all())
 
 
-@pytest.mark.parametrize("name", SMALL)
-def test_trajectory_lockstep(name):
+@pytest.mark.parametrize("name,win", [(n, 1) for n in SMALL] +
+                         [("tiny_fp32_1k", 3), ("qwen3_0p6b_8k", 4)])
+def test_trajectory_lockstep(name, win):
     """Every step of the seeded trajectory through the two-stream engine.  Slow steps:
     dense output and the selection (near-tie rule); the oracle then continues with the
     device's selection (teacher forcing) so the two cannot drift.  Fast steps: the
-    two-segment output against the oracle's fast step on the same memory."""
-    w = get(name)
+    two-segment output against the oracle's fast step on the same memory.  win > 1 pools
+    the Selector's evidence over that many decode queries."""
+    w = get(name).replace(evidence_window=win)
     d, eng, lb = _setup(w)
     B = w.batch
     host = [oracle_layer_arrays(d, b) for b in range(B)]
@@ -182,8 +184,17 @@ def test_trajectory_lockstep(name):
                 n_slow += 1
                 o, z, lse, p = O.attention(q[s], K[:, :N], V[:, :N])
                 worst = max(worst, check_out(out[b], o, f"slow s={s} b={b}"))
-                sel = O.select(p, norms[b][:, :N], N, w.num_kv_heads, w.n_sink, w.n_recent,
-                               w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam)
+                if win == 1:
+                    sel = O.select(p, norms[b][:, :N], N, w.num_kv_heads, w.n_sink,
+                                   w.n_recent, w.top_k, w.nms_radius, w.alpha_soft,
+                                   w.alpha_cross, w.lam)
+                else:
+                    Qw = O.window_queries(q, s, win)
+                    P = np.stack([p] + [O.attention(Qw[k], K[:, :N], V[:, :N])[3]
+                                        for k in range(1, win)])
+                    sel = O.select_window(P, norms[b][:, :N], N, w.num_kv_heads, w.n_sink,
+                                          w.n_recent, w.top_k, w.nms_radius, w.alpha_soft,
+                                          w.alpha_cross, w.lam)
                 sel_gpu = lb.sel_idx[b].cpu().numpy()
                 explain_selection_diff(sel_gpu, sel, N)
                 packed[b] = [O.packed_positions(sel_gpu[g], w.n_sink)
@@ -193,7 +204,58 @@ def test_trajectory_lockstep(name):
                 n_fast += 1
                 o, lse = O.fast_attention(q[s], K, V, packed[b], rstart[b], N)
                 worst = max(worst, check_out(out[b], o, f"fast s={s} b={b}"))
-    print(f"{name}: {n_slow} slow / {n_fast} fast steps, worst row rel err {worst:.2e}")
+    print(f"{name} window {win}: {n_slow} slow / {n_fast} fast steps, "
+          f"worst row rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("name,win", [("tiny_fp32_1k", 3), ("qwen3_0p6b_8k", 4),
+                                      ("qwen3_0p6b_8k", 8)])
+def test_slow_attention_and_select_window(name, win):
+    """sfi_slow_attn_window + sfi_select_window against the oracle's window readings: the
+    logits and lse of every slot, the output of slot 0, the pooled fused scores and the
+    selection.  Steps 0 and 1 have slots filled by the first query."""
+    w = get(name).replace(evidence_window=win)
+    d, eng, lb = _setup(w, dbg=True)
+    Hq, Hkv, G, B = w.num_q_heads, w.num_kv_heads, w.group, w.batch
+    out1 = torch.zeros_like(lb.out)
+    lse1 = torch.zeros(B, Hq, dtype=torch.float32, device="cuda")
+    for s in (0, 1, 5, w.steps - 1):
+        N = w.seq_len(s)
+        seq_len = torch.full((B,), N, dtype=torch.int32, device="cuda")
+        L.sfi_slow_attn_window(eng.shape, win, lb.q_win[s], lb.k_cache, lb.v_cache,
+                               lb.block_table, seq_len, eng.all_ids_d, B, eng.max_len, lb.out,
+                               lb.logits, eng.stride, lb.lse, eng.ws_slow)
+        L.sfi_select_window(eng.shape, eng.params, win, lb.logits, eng.stride, lb.lse,
+                            lb.key_norm, eng.stride, seq_len, eng.all_ids_d, B, eng.max_len,
+                            lb.sel_idx, eng.dbg_buf, eng.ws_sel)
+        # the step's own output does not depend on the window
+        L.sfi_slow_attn(eng.shape, d["q"][s], lb.k_cache, lb.v_cache, lb.block_table, seq_len,
+                        eng.all_ids_d, B, eng.max_len, out1, None, 0, lse1, eng.ws_slow)
+        torch.cuda.synchronize()
+        assert bool((_bits(out1) == _bits(lb.out)).all())
+        for b in range(B):
+            q, K, V = oracle_layer_arrays(d, b)
+            Qw = O.window_queries(q, s, win)
+            z_gpu = host64(lb.logits[b, :, :N]).reshape(Hkv, win, G, N)
+            lse_gpu = host64(lb.lse[b]).reshape(Hkv, win, G)
+            P = []
+            for k in range(win):
+                o, z, lse, p = O.attention(Qw[k], K[:, :N], V[:, :N])
+                P.append(p)
+                if k == 0:
+                    check_out(host64(lb.out[b]), o, f"s={s} b={b}")
+                check_lse(lse_gpu[:, k].reshape(Hq), lse, p, Qw[k], K[:, :N])
+                check_logits(z_gpu[:, k].reshape(Hq, N), z, Qw[k], K[:, :N], w.head_dim)
+            sel = O.select_window(np.stack(P), O.key_norms(K[:, :N]), N, Hkv, w.n_sink,
+                                  w.n_recent, w.top_k, w.nms_radius, w.alpha_soft,
+                                  w.alpha_cross, w.lam)
+            s_gpu = host64(eng.dbg_buf[b, :, :N])
+            np.testing.assert_allclose(s_gpu, sel.s, rtol=1e-3, atol=1e-12)
+            sel_gpu = lb.sel_idx[b].cpu().numpy()
+            np.testing.assert_array_equal(
+                sel_gpu, O.select_from_scores(s_gpu, N, w.n_sink, w.n_recent, w.top_k,
+                                              w.nms_radius, w.alpha_soft, w.alpha_cross))
+            print(name, win, "step", s, "row", b, explain_selection_diff(sel_gpu, sel, N))
 
 
 def test_two_streams_bit_identical_to_one_stream():

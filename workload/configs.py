@@ -40,6 +40,7 @@ class Workload:
     alpha_cross: float
     lam: float
     page_size: int = 16
+    evidence_window: int = 1  # decode queries whose attention the Selector pools
 
     @property
     def group(self) -> int:
