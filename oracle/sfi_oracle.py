@@ -20,7 +20,7 @@ in the docstring of the function that applies it.
 
 Parity status of each function:
   attention, merge_segments, evidence, window_evidence, window_queries, fuse, topk, pack,
-  fast_attention, schedule:
+  fast_attention, schedule, boundary_flags, step_control:
       pinned by tests (closed forms, library routines, brute force).
   key_norms: pinned (library norm).
   prior: invariants pinned (normalisation, positivity, monotonicity); the functional form
@@ -103,6 +103,51 @@ def schedule(flags: np.ndarray, budget: int) -> np.ndarray:
             else:
                 run += 1
     return mode
+
+
+def boundary_flags(tokens: np.ndarray, boundary_tokens) -> np.ndarray:
+    """flag = 1 where the decoded token is one of the semantic-boundary tokens (sentence
+    punctuation, line or paragraph breaks: es "Pasos Lentos", zh "2.1 触发机制")."""
+    tokens = np.asarray(tokens)
+    bset = set(int(t) for t in boundary_tokens)
+    out = np.zeros(tokens.shape, np.uint8)
+    for idx in np.ndindex(tokens.shape):
+        out[idx] = 1 if int(tokens[idx]) in bset else 0
+    return out
+
+
+def step_control(tokens: np.ndarray, boundary_tokens, budget: int, n_stored: int,
+                 n_sink: int, n_recent: int) -> Dict[str, np.ndarray]:
+    """The per-step state of a trajectory driven by decoded tokens, tokens [B, S].
+
+    Before step 0 every row stores n_stored positions; step s decodes token [b, s], which
+    joins the history, so N_s = n_stored + s + 1.  The mode is `schedule` of the tokens'
+    boundary flags; a slow step freezes the recent segment's left edge (recent_start_at).
+    Returns mode [S, B], seq_len [S, B], recent_start [S, B] (the edge in force at the
+    step), slow / fast row lists [S, B] in ascending order padded with -1, and the counts
+    [S, 2]."""
+    mode = schedule(boundary_flags(tokens, boundary_tokens), budget).T
+    S, B = mode.shape
+    seq_len = np.zeros((S, B), np.int64)
+    rstart = np.zeros((S, B), np.int64)
+    slow_ids = np.full((S, B), -1, np.int64)
+    fast_ids = np.full((S, B), -1, np.int64)
+    counts = np.zeros((S, 2), np.int64)
+    edge = np.zeros(B, np.int64)
+    for s in range(S):
+        for b in range(B):
+            N = n_stored + s + 1
+            seq_len[s, b] = N
+            if mode[s, b]:
+                edge[b] = recent_start_at(N, n_sink, n_recent)
+            rstart[s, b] = edge[b]
+        sl = [b for b in range(B) if mode[s, b]]
+        fa = [b for b in range(B) if not mode[s, b]]
+        slow_ids[s, :len(sl)] = sl
+        fast_ids[s, :len(fa)] = fa
+        counts[s] = (len(sl), len(fa))
+    return dict(mode=mode, seq_len=seq_len, recent_start=rstart, slow_ids=slow_ids,
+                fast_ids=fast_ids, counts=counts)
 
 
 # ------------------------------------------------------------------------------ Selector

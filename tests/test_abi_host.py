@@ -5,7 +5,9 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
+import torch
 
 from sparse_kv_attention_decode_amd import lib as L
 
@@ -27,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert sorted(L.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert L.sfi_abi_version() == 2
+    assert L.sfi_abi_version() == 3
 
 
 def test_status_strings():
@@ -256,3 +258,48 @@ def test_topic_recall_counts_candidate_topics_only():
     # head 1: candidates {4, 7, 8} (3 below lo, 50 above hi), selected {4} -> 1/3
     assert np.allclose(r, [0.75, 1 / 3])
     assert np.isnan(topic_recall(sel[:1], np.array([[1, 2]]), G=1, lo=4, hi=40)[0])
+
+
+def test_synthetic_tokens_follow_the_boundary_flags():
+    """Boundary ids exactly at the flagged steps; other ids avoid the boundary block."""
+    from oracle import sfi_oracle as O
+    from workload import get
+    from workload.gen import BOUNDARY_TOKENS, VOCAB, gen_flags, gen_tokens
+    w = get("qwen3_4b_32k_b4")
+    flags = gen_flags(w)
+    tok = gen_tokens(w, flags)
+    assert tok.shape == (w.steps, w.batch) and tok.dtype == torch.int32
+    assert int(tok.min()) >= 0 and int(tok.max()) < VOCAB
+    np.testing.assert_array_equal(O.boundary_flags(tok.numpy().T, BOUNDARY_TOKENS),
+                                  flags.numpy())
+
+
+def test_step_control_and_append_validation():
+    s, p = _shape(), _params()
+    lib = L.load()
+
+    def ctrl(budget=4, tok=FAKE, bnd=FAKE, nb=5, sl=FAKE, outs=FAKE, shape=s, params=p):
+        return lib.sfi_step_control(ctypes.byref(shape), ctypes.byref(params), budget, tok, bnd,
+                                    nb, sl, FAKE, FAKE, outs, FAKE, FAKE, None)
+
+    assert ctrl(budget=-1) == L.SFI_E_ARG
+    assert ctrl(nb=-1) == L.SFI_E_ARG
+    assert ctrl(nb=1025) == L.SFI_E_UNSUPPORTED
+    assert ctrl(tok=None) == L.SFI_E_ARG
+    assert ctrl(bnd=None) == L.SFI_E_ARG          # a table is needed when nb > 0
+    assert ctrl(sl=None) == L.SFI_E_ARG
+    assert ctrl(outs=None) == L.SFI_E_ARG
+    assert ctrl(shape=_shape(num_kv_heads=0)) == L.SFI_E_ARG
+    assert ctrl(params=_params(top_k=0)) == L.SFI_E_ARG
+
+    def app(kn=FAKE, kc=FAKE, n=1, norm=FAKE, stride=128, shape=s):
+        return lib.sfi_kv_append(ctypes.byref(shape), kn, FAKE, kc, FAKE, FAKE, FAKE, FAKE, n,
+                                 norm, stride, None)
+
+    assert app(kn=None) == L.SFI_E_ARG
+    assert app(kn=MIS) == L.SFI_E_ALIGN
+    assert app(kc=MIS) == L.SFI_E_ALIGN
+    assert app(n=3) == L.SFI_E_ARG                 # more rows than the batch
+    assert app(norm=FAKE, stride=0) == L.SFI_E_ARG
+    assert app(shape=_shape(head_dim=96)) == L.SFI_E_UNSUPPORTED
+    assert app(n=0) == L.SFI_OK                    # nothing to launch

@@ -130,6 +130,37 @@ def test_schedule_budget_zero_is_all_slow():
     assert O.schedule(np.zeros((2, 9), np.uint8), 0).all()
 
 
+def test_boundary_flags_worked_example():
+    tok = np.array([[5, 1001, 7, 1005], [1003, 1003, 0, 999999]])
+    np.testing.assert_array_equal(O.boundary_flags(tok, (1001, 1002, 1003, 1004, 1005)),
+                                  [[0, 1, 0, 1], [1, 1, 0, 0]])
+    assert not O.boundary_flags(tok, ()).any()
+
+
+def test_step_control_worked_example():
+    """Two rows, six steps, budget 2, 10 stored positions, n_sink 1, W 4, worked by hand.
+    Row 0 decodes a boundary token at step 3, row 1 at step 1; row 1's budget runs out at
+    step 4.  N_s = 11 + s; a slow step at N sets the edge max(1, N - 4)."""
+    B = 1001
+    tok = np.array([[7, 8, 9, B, 10, 11],
+                    [7, B, 9, 10, 11, 12]])
+    st = O.step_control(tok, (B,), budget=2, n_stored=10, n_sink=1, n_recent=4)
+    np.testing.assert_array_equal(st["mode"].T, [[1, 0, 0, 1, 0, 0], [1, 1, 0, 0, 1, 0]])
+    np.testing.assert_array_equal(st["seq_len"][:, 0], [11, 12, 13, 14, 15, 16])
+    np.testing.assert_array_equal(st["recent_start"].T, [[7, 7, 7, 10, 10, 10],
+                                                         [7, 8, 8, 8, 11, 11]])
+    np.testing.assert_array_equal(st["slow_ids"], [[0, 1], [1, -1], [-1, -1], [0, -1],
+                                                   [1, -1], [-1, -1]])
+    np.testing.assert_array_equal(st["fast_ids"], [[-1, -1], [0, -1], [0, 1], [1, -1],
+                                                   [0, -1], [0, 1]])
+    np.testing.assert_array_equal(st["counts"], [[2, 0], [1, 1], [0, 2], [1, 1], [1, 1],
+                                                 [0, 2]])
+    # budget 0: every step is slow; no boundary and a long budget: only the first step
+    assert O.step_control(tok, (B,), 0, 10, 1, 4)["mode"].all()
+    m = O.step_control(tok, (), 100, 10, 1, 4)["mode"]
+    assert m[0].all() and not m[1:].any()
+
+
 # ------------------------------------------------------------------------------ Selector
 def test_evidence_is_distribution():
     q, K, V = _rand_qkv(Hq=8, Hkv=2, n=40, seed=11)

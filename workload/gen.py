@@ -10,6 +10,9 @@ Recipe (one attention layer, one sequence b; per layer an independent stream):
   * keys        K[g, j] = a_j * N(0, I_D), values V[g, j] = N(0, I_D), rounded to the
                 storage dtype (bf16 round-to-nearest-even, or kept fp32);
   * flags       flag[b, s] ~ Bernoulli(p) per decode step, shared by all layers;
+  * tokens      the id decoded at step s: one of five synthetic boundary ids (standing for
+                '.', '?', '!', a line break and a paragraph break) where flag[b, s] is set,
+                otherwise a uniform id from the rest of a 151936-entry vocabulary;
   * spans       a span starts at step 0 and at every flagged step.  At a span start s,
                 each query head h draws n_topics positions uniformly without replacement
                 from [n_sink, N_s - W) and its span base is the sum of the stored keys
@@ -34,7 +37,11 @@ import torch
 from .configs import Workload
 
 ROOT_SEED = 1234
-STREAM_KV, STREAM_FLAGS, STREAM_TOPICS, STREAM_NOISE, STREAM_PAGES = 0, 1, 2, 3, 4
+STREAM_KV, STREAM_FLAGS, STREAM_TOPICS, STREAM_NOISE, STREAM_PAGES, STREAM_TOKENS = range(6)
+
+VOCAB = 151936
+# Synthetic ids of the boundary tokens (a contiguous block, so other ids can skip it).
+BOUNDARY_TOKENS = (1001, 1002, 1003, 1004, 1005)
 
 
 def seed_for(w: Workload, stream: int, layer: int = 0) -> int:
@@ -74,6 +81,20 @@ def gen_flags(w: Workload, device="cpu") -> torch.Tensor:
     g = _gen(w, STREAM_FLAGS, 0, device)
     u = torch.rand(w.batch, w.steps, generator=g, device=device)
     return (u < w.p_boundary).to(torch.uint8)
+
+
+def gen_tokens(w: Workload, flags: torch.Tensor, device="cpu") -> torch.Tensor:
+    """Token id decoded at every step, [steps, B] int32: a boundary id where the step's flag
+    is set, any other id of the vocabulary otherwise."""
+    g = _gen(w, STREAM_TOKENS, 0, "cpu")
+    B, S = flags.shape
+    nb = len(BOUNDARY_TOKENS)
+    pick = torch.randint(0, nb, (S, B), generator=g)
+    other = torch.randint(0, VOCAB - nb, (S, B), generator=g)
+    other = other + (other >= BOUNDARY_TOKENS[0]).long() * nb
+    bnd = torch.tensor(BOUNDARY_TOKENS)[pick]
+    tok = torch.where(flags.cpu().t().bool(), bnd, other).to(torch.int32)
+    return tok.to(device)
 
 
 def span_starts(w: Workload, flags_row) -> list:
