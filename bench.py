@@ -52,6 +52,10 @@ def _parse():
     ap.add_argument("--evidence-window", type=int, default=None,
                     help="decode queries pooled into the Selector's evidence at a slow step "
                          "(default: the workload's, 1)")
+    ap.add_argument("--device-control", action="store_true",
+                    help="decide slow/fast and append K/V on the device every step (token "
+                         "ids in, no host schedule); every step is replayed from a graph "
+                         "unless --no-graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a device copy of known size (for counter calibration)")
     ap.add_argument("--traffic-json",
@@ -145,7 +149,13 @@ def main():
         keep = layer == 0 and args.cpu_seconds > 0
         d = make_layer(w, layer, device="cuda", keep_logical=keep)
         if eng is None:
-            eng = Engine(w, d["flags"], two_streams=not args.one_stream)
+            if args.device_control:
+                from workload.gen import BOUNDARY_TOKENS, gen_tokens
+                eng = Engine(w, d["flags"], two_streams=not args.one_stream,
+                             device_control=True, tokens=gen_tokens(w, d["flags"]),
+                             boundary_tokens=BOUNDARY_TOKENS)
+            else:
+                eng = Engine(w, d["flags"], two_streams=not args.one_stream)
         eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
         if keep:
             d0 = {k: d[k] for k in ("q", "K", "V", "flags")}
@@ -154,7 +164,10 @@ def main():
             print(f"[bench] layer {layer + 1}/{w.layers} resident "
                   f"({time.perf_counter() - t_setup:.1f} s)", file=sys.stderr, flush=True)
     if not args.no_graphs:
-        eng.enable_graphs()
+        if args.device_control:
+            eng.enable_device_graphs()
+        else:
+            eng.enable_graphs()
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
     S = w.steps
@@ -267,7 +280,8 @@ def main():
                    "top_k": w.top_k, "n_recent": w.n_recent,
                    "streams": 1 if args.one_stream else 2,
                    "fast_step_graph": eng.graph is not None,
-                   "evidence_window": w.evidence_window},
+                   "evidence_window": w.evidence_window,
+                   "device_control": bool(args.device_control)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {

@@ -23,6 +23,9 @@
  *   Batch rows `seq_ids[0..n_seqs)` (device, int32) lists the batch rows b a call serves,
  *              so one decode step can send slow and fast sequences to different calls.
  *              Per-row tensors are indexed by b.  n_seqs == 0 is a no-op returning SFI_OK.
+ *              A negative entry marks an unused slot: every call skips it and writes
+ *              nothing for it, so the -1-padded lists of sfi_step_control can be passed
+ *              whole (n_seqs = batch) without the host reading the counts.
  *   Errors     Host-side checks run before anything is enqueued and return a negative
  *              code with nothing enqueued.  After enqueueing, a launch failure reported
  *              by hipGetLastError is returned as SFI_E_HIP.  Device-side contracts (seq
@@ -57,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SFI_ABI_VERSION 2
+#define SFI_ABI_VERSION 3
 
 enum sfi_status {
   SFI_OK = 0,
@@ -225,6 +228,42 @@ int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
                   const int32_t* recent_start, const int32_t* seq_lens,
                   const int32_t* seq_ids, int32_t n_seqs, int32_t max_recent, float* out,
                   float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sfi_step_control -- the slow/fast decision of one decode step for every row of the batch,
+ * on the device (es "Pasos Lentos", zh "2.1 触发机制": a slow step follows a semantic-
+ * boundary token such as sentence punctuation or a line break, or a spent refresh budget).
+ * For each row b:
+ *   seq_lens[b]    += 1                       (the token decoded now joins the history)
+ *   slow            = since_slow[b] < 0       (no slow step yet)
+ *                     || token_ids[b] is one of boundary_tokens[0..n_boundary)
+ *                     || since_slow[b] >= refresh_budget
+ *   since_slow[b]   = slow ? 0 : since_slow[b] + 1
+ *   recent_start[b] = max(n_sink, seq_lens[b] - n_recent)   when slow (else unchanged)
+ * slow_ids / fast_ids [batch] receive the slow and the fast rows in ascending order, each
+ * padded with -1; counts [2] = {slow rows, fast rows}.  n_sink and n_recent come from
+ * params.  Initial state: seq_lens = stored length before the first step, since_slow = -1.
+ * Requires refresh_budget >= 0 and 0 <= n_boundary <= 1024 (SFI_E_UNSUPPORTED beyond).
+ * One workgroup; rows are independent.
+ */
+int sfi_step_control(const sfi_shape* shape, const sfi_select_params* params,
+                     int32_t refresh_budget, const int32_t* token_ids,
+                     const int32_t* boundary_tokens, int32_t n_boundary, int32_t* seq_lens,
+                     int32_t* since_slow, int32_t* recent_start, int32_t* slow_ids,
+                     int32_t* fast_ids, int32_t* counts, void* stream);
+
+/*
+ * sfi_kv_append -- store the K and V rows of the token decoded now at position
+ * seq_lens[b] - 1 of each listed row (after sfi_step_control has counted it), and its key
+ * norm ||k||_2 into key_norm[b][g][seq_lens[b] - 1] when key_norm is not NULL (the cache
+ * statistic the Selector's prior reads, zh "2.2 输入"; the same bits sfi_key_norms stores).
+ *   k_new, v_new  elt [batch, Hkv, D]   16-byte aligned
+ * The page of the position must already be in block_table (device contract).
+ */
+int sfi_kv_append(const sfi_shape* shape, const void* k_new, const void* v_new, void* k_cache,
+                  void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                  const int32_t* seq_ids, int32_t n_seqs, float* key_norm, int64_t norm_stride,
+                  void* stream);
 
 #ifdef __cplusplus
 }

@@ -281,6 +281,43 @@ int sfi_pack(const sfi_shape* shape, const sfi_select_params* params, const void
                                  packed_cap, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int sfi_step_control(const sfi_shape* shape, const sfi_select_params* params,
+                     int32_t refresh_budget, const int32_t* token_ids,
+                     const int32_t* boundary_tokens, int32_t n_boundary, int32_t* seq_lens,
+                     int32_t* since_slow, int32_t* recent_start, int32_t* slow_ids,
+                     int32_t* fast_ids, int32_t* counts, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_params(params))) return rc;
+  if (refresh_budget < 0 || n_boundary < 0) return SFI_E_ARG;
+  if (n_boundary > sfi::kMaxBoundaryTokens) return SFI_E_UNSUPPORTED;
+  if (!token_ids || (n_boundary > 0 && !boundary_tokens) || !seq_lens || !since_slow ||
+      !recent_start || !slow_ids || !fast_ids || !counts)
+    return SFI_E_ARG;
+  return finish(sfi::launch_step_control(shape->batch, token_ids, boundary_tokens, n_boundary,
+                                         refresh_budget, params->n_sink, params->n_recent,
+                                         seq_lens, since_slow, recent_start, slow_ids, fast_ids,
+                                         counts, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int sfi_kv_append(const sfi_shape* shape, const void* k_new, const void* v_new, void* k_cache,
+                  void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                  const int32_t* seq_ids, int32_t n_seqs, float* key_norm, int64_t norm_stride,
+                  void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens || !seq_ids)
+    return SFI_E_ARG;
+  if (n_seqs < 0 || n_seqs > shape->batch) return SFI_E_ARG;
+  if (key_norm && norm_stride < 1) return SFI_E_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return SFI_E_ALIGN;
+  if (n_seqs == 0) return SFI_OK;
+  return finish(sfi::launch_kv_append(*shape, k_new, v_new, k_cache, v_cache, block_table,
+                                      seq_lens, seq_ids, n_seqs, key_norm, norm_stride,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
 int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
                   const void* packed_v, const int32_t* packed_len, int32_t packed_cap,
                   const void* k_cache, const void* v_cache, const int32_t* block_table,

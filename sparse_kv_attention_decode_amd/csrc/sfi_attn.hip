@@ -118,6 +118,7 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
   const int g = ig % p.Hkv;
   const int i = ig / p.Hkv;
   const int b = uniform(p.seq_ids[i]);
+  if (b < 0) return;  // unused slot of the row list (workgroup-uniform)
   const int r = lane & 15;
   const int qd = lane >> 4;
   const size_t pidx = (size_t)ig * p.nsplit + split;
@@ -413,6 +414,7 @@ __global__ __launch_bounds__(64) void k_attn_partial_f32(AttnParams p) {
   const int g = ig % p.Hkv;
   const int i = ig / p.Hkv;
   const int b = uniform(p.seq_ids[i]);
+  if (b < 0) return;  // unused slot of the row list
   const int N = uniform(p.seq_lens[b]);
   const size_t pidx = (size_t)ig * p.nsplit + split;
   const SplitRange sr = split_range(p, b, g, split, N);
@@ -544,6 +546,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm
   const int h = blockIdx.x % Hq;
   const int g = h / G, hh = h % G;
   const int b = seq_ids[i];
+  if (b < 0) return;  // unused slot of the row list (block-uniform)
   const size_t base = ((size_t)i * Hkv + g) * nsplit;
   const int cols = D / 4;
   const int ngrp = 256 / cols;

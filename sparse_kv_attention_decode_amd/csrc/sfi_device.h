@@ -52,4 +52,59 @@ __device__ __forceinline__ float wave_sum_xor(float v, int width) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Sum of squares of the 16 bytes of a cache row one lane holds (8 bf16 or 4 f32 values),
+// in a fixed order.  A row's squared norm is this summed over its D * sizeof(T) / 16
+// lanes with wave_sum_xor; every kernel that stores key norms uses the same two steps.
+template <typename T>
+__device__ __forceinline__ float sumsq16(u32x4_t v) {
+  float ss = 0.f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = u2f(v[w] << 16), c = u2f(v[w] & 0xffff0000u);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(c, c, ss);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = u2f(v[w]);
+      ss = fmaf(a, a, ss);
+    }
+  }
+  return ss;
+}
+
+// Exclusive prefix of v over a block of BLOCK threads; the block total goes to *tot.
+// wsum holds BLOCK / 64 + 1 words.
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uint32_t* tot) {
+  constexpr int NWV = BLOCK / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  if (tid < 64) {
+    const uint32_t w = tid < NWV ? wsum[tid] : 0u;
+    uint32_t s = w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(s, o);
+      if (tid >= o) s += y;
+    }
+    if (tid < NWV) wsum[tid] = s - w;  // exclusive
+    if (tid == NWV - 1) wsum[NWV] = s;
+  }
+  __syncthreads();
+  const uint32_t res = wsum[wv] + x - v;
+  *tot = wsum[NWV];
+  __syncthreads();
+  return res;
+}
+
 }  // namespace sfi

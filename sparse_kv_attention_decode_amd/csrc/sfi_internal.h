@@ -82,6 +82,19 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm,
                          const int32_t* seq_ids, int n_seqs, int max_seq_len,
                          int32_t* sel_idx, float* dbg_scores, void* ws, hipStream_t stream);
 
+hipError_t launch_step_control(int batch, const int32_t* tokens, const int32_t* boundary,
+                               int n_boundary, int budget, int n_sink, int n_recent,
+                               int32_t* seq_lens, int32_t* since, int32_t* recent_start,
+                               int32_t* slow_ids, int32_t* fast_ids, int32_t* counts,
+                               hipStream_t stream);
+// Longest boundary-token table sfi_step_control takes.
+constexpr int kMaxBoundaryTokens = 1024;
+
+hipError_t launch_kv_append(const sfi_shape& s, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, const int32_t* seq_ids, int n_seqs,
+                            float* key_norm, int64_t norm_stride, hipStream_t stream);
+
 hipError_t launch_pack(const sfi_shape& s, const sfi_select_params& prm, const void* k_cache,
                        const void* v_cache, const int32_t* block_table, const int32_t* sel_idx,
                        const int32_t* seq_ids, int n_seqs, void* packed_k, void* packed_v,

@@ -56,6 +56,7 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack(PackArgs a) {
     const int ig = work / nblk;
     const int g = ig % a.Hkv, i = ig / a.Hkv;
     const int b = a.seq_ids[i];
+    if (b < 0) continue;  // unused slot of the row list (wavefront-uniform)
     const size_t bg = (size_t)b * a.Hkv + g;
     const int32_t* selrow = a.sel + bg * a.K;
     const int row0 = blk * RB + wv * RW;

@@ -75,6 +75,7 @@ __global__ __launch_bounds__(256) void k_key_norms(const T* __restrict__ kc,
   const int pb = blockIdx.x % nblk_pos;
   const int g = ig % Hkv, i = ig / Hkv;
   const int b = seq_ids[i];
+  if (b < 0) return;  // unused slot of the row list
   const int N = seq_lens[b];
   const int j = pos_begin + pb * rows_per_block + (int)threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
@@ -83,21 +84,7 @@ __global__ __launch_bounds__(256) void k_key_norms(const T* __restrict__ kc,
   if (ok) {
     const int page = bt[(size_t)b * max_pages + j / kPage];
     const T* row = kc + (((size_t)page * Hkv + g) * kPage + (j % kPage)) * D + part * EPL;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row);
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float a = u2f(v[w] << 16), c = u2f(v[w] & 0xffff0000u);
-        ss = fmaf(a, a, ss);
-        ss = fmaf(c, c, ss);
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float a = u2f(v[w]);
-        ss = fmaf(a, a, ss);
-      }
-    }
+    ss = sumsq16<T>(*reinterpret_cast<const u32x4_t*>(row));
   }
   ss = wave_sum_xor(ss, LPR);
   if (ok && part == 0) out[((size_t)b * Hkv + g) * stride + j] = sqrtf(ss);
@@ -132,6 +119,7 @@ __global__ __launch_bounds__(256) void k_sel_zsum(const float* __restrict__ key_
   __shared__ float red[8];
   const int chunk = blockIdx.x % nchunk;
   const int ig = blockIdx.x / nchunk;
+  if (seq_ids[ig / Hkv] < 0) return;  // unused slot of the row list (block-uniform)
   if (chunk == 0) {  // clear the top-K histogram and state of this (row, head)
     uint32_t* h = topk_hist + (size_t)ig * kTopkHistWords;
     for (int k = threadIdx.x; k < kTopkHistWords; k += 256) h[k] = 0;
@@ -203,6 +191,7 @@ __device__ __forceinline__ void score_block(const ScoreArgs& a, int work, float*
   const int i = work / a.ntile;
   const int tile = work % a.ntile;
   const int b = a.seq_ids[i];
+  if (b < 0) return;  // unused slot of the row list (block-uniform)
   const int N = a.seq_lens[b];
   const int t0 = tile * TILE;
   if (t0 >= N) return;  // block-uniform
@@ -348,38 +337,6 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, int bin, bool active) {
   if (active) atomicAdd(&hist[bin], 1u);
 }
 
-// Exclusive prefix of v over a block of BLOCK threads; the block total goes to *tot.
-// wsum holds BLOCK / 64 + 1 words.
-template <int BLOCK>
-__device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uint32_t* tot) {
-  constexpr int NWV = BLOCK / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[wv] = x;
-  __syncthreads();
-  if (tid < 64) {
-    const uint32_t w = tid < NWV ? wsum[tid] : 0u;
-    uint32_t s = w;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(s, o);
-      if (tid >= o) s += y;
-    }
-    if (tid < NWV) wsum[tid] = s - w;  // exclusive
-    if (tid == NWV - 1) wsum[NWV] = s;
-  }
-  __syncthreads();
-  const uint32_t res = wsum[wv] + x - v;
-  *tot = wsum[NWV];
-  __syncthreads();
-  return res;
-}
-
 // Bin of hist[0..2048) holding the krem-th largest counted element; thread t owns the
 // 2048 / BLOCK bins just below 2048 - t * (2048 / BLOCK).  Writes (bin, count above the
 // bin) to res[0..1].  All threads call.
@@ -464,7 +421,7 @@ struct TopkRow {
 __device__ __forceinline__ TopkRow topk_row(const TopkArgs& a, int i) {
   TopkRow r;
   r.b = a.seq_ids[i];
-  const int N = a.seq_lens[r.b];
+  const int N = r.b < 0 ? 0 : a.seq_lens[r.b];  // an unused slot has no candidates
   r.lo = a.n_sink;
   const int hi = max(r.lo, N - a.n_recent);
   r.nC = hi - r.lo;
@@ -703,6 +660,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_final(TopkArgs a) {
   const int tid = threadIdx.x;
   const int ig = blockIdx.x;
   const TopkRow row = topk_row(a, ig / a.Hkv);
+  if (row.b < 0) return;  // unused slot of the row list
   const int g = ig % a.Hkv;
   int32_t* out = a.sel + ((size_t)row.b * a.Hkv + g) * a.K;
   uint32_t* st = a.state + (size_t)ig * kStWords;

@@ -97,6 +97,11 @@ def make_plan(flags: np.ndarray, context: int, budget: int, n_sink: int, n_recen
 kGraphMinLayers = 8
 
 
+def recent_bound(w) -> int:
+    """Upper bound of N - recent_start over every fast step of any schedule (see Engine)."""
+    return w.n_recent + w.refresh_budget
+
+
 def window_query_table(q_all: torch.Tensor, num_kv_heads: int, window: int) -> torch.Tensor:
     """Query layout of windowed slow steps: [S, B, Hkv, window, G, D] (flattened to
     [S, B, Hq * window, D]) with slot k of step s holding the query of step max(0, s - k):
@@ -136,14 +141,21 @@ class LayerBuffers:
         self.ev_attn = torch.cuda.Event()
         self.ev_pack = torch.cuda.Event()
         self.pack_pending = False
+        self.k_new = self.v_new = None           # [S, B, Hkv, D] (device-controlled steps)
 
 
 class Engine:
     def __init__(self, w, flags, device="cuda", two_streams: bool = True,
                  dbg_scores: bool = False, sel_streams: int = 2,
-                 window: Optional[int] = None):
+                 window: Optional[int] = None, device_control: bool = False,
+                 tokens=None, boundary_tokens=None, max_recent: Optional[int] = None,
+                 full_lists: bool = False):
         self.w = w
         self.device = torch.device(device)
+        self.device_control = device_control
+        # full_lists: every call of a host-scheduled step gets all B slots of its row list
+        # (-1 padded), the launch shape of device-controlled steps.
+        self.full_lists = full_lists
         # Decode queries pooled into the Selector's evidence at a slow step (1: the current
         # query only).
         self.window = int(w.evidence_window if window is None else window)
@@ -158,13 +170,21 @@ class Engine:
         self.packed_cap = L.sfi_packed_cap(self.params)
         self.max_len = w.total_len
         self.stride = (self.max_len + 63) // 64 * 64
-        self.max_recent = self.plan.max_recent
+        # Longest recent segment a fast call can meet.  The host plan knows it; a step decided
+        # on the device can only bound it: after a slow step at length N0 the edge is at
+        # least N0 - W and at most refresh_budget fast steps follow, so N - edge <= W + budget.
+        if max_recent is not None:
+            self.max_recent = int(max_recent)
+        elif device_control:
+            self.max_recent = recent_bound(w)
+        else:
+            self.max_recent = self.plan.max_recent
         dev = self.device
         S, B = w.steps, w.batch
         self.seq_len_d = torch.from_numpy(self.plan.seq_len).to(dev)
         self.rstart_d = torch.from_numpy(self.plan.recent_start).to(dev)
-        slow = np.zeros((S, B), np.int32)
-        fast = np.zeros((S, B), np.int32)
+        slow = np.full((S, B), -1, np.int32)
+        fast = np.full((S, B), -1, np.int32)
         for s in range(S):
             slow[s, :len(self.plan.slow_ids[s])] = self.plan.slow_ids[s]
             fast[s, :len(self.plan.fast_ids[s])] = self.plan.fast_ids[s]
@@ -198,6 +218,8 @@ class Engine:
                             if two_streams else [self.stream1])
         self.stream2 = self.sel_streams[0]
         self.layers: List[LayerBuffers] = []
+        if device_control:
+            self._init_device_control(tokens, boundary_tokens)
         self.dbg = dbg_scores
         self.graph = None
         self.graphs = {}
@@ -209,19 +231,162 @@ class Engine:
 
     def add_layer(self, k_cache, v_cache, block_table, q_all) -> LayerBuffers:
         lb = LayerBuffers(self, k_cache, v_cache, block_table, q_all)
+        n_norm = self.max_len
+        if self.device_control:
+            # The rows each step appends are taken out of the generated cache and their
+            # slots cleared, so the appends must write them back; norms are computed here
+            # only for the positions stored before the first step.
+            lb.k_new, lb.v_new = self._take_new_rows(lb)
+            n_norm = self.n_stored
         # cached key statistic for every stored position (prefill-time work)
-        full = torch.full((self.w.batch,), self.max_len, dtype=torch.int32, device=self.device)
+        full = torch.full((self.w.batch,), n_norm, dtype=torch.int32, device=self.device)
         # The caches, block table, queries and the buffers above were written on the
         # caller's stream; the engine streams are non-blocking, so order them after it.
         # Stream 2 is ordered behind stream 1 through the per-layer attention events.
         self.stream1.wait_stream(torch.cuda.current_stream(self.device))
         with torch.cuda.stream(self.stream1):
             L.sfi_key_norms(self.shape, lb.k_cache, lb.block_table, full, self.all_ids_d,
-                            self.w.batch, 0, self.max_len, lb.key_norm, self.stride,
+                            self.w.batch, 0, n_norm, lb.key_norm, self.stride,
                             stream=self.stream1)
         self.stream1.synchronize()
         self.layers.append(lb)
         return lb
+
+    # ----------------------------------------------------------- on-device step control
+    def _init_device_control(self, tokens, boundary_tokens) -> None:
+        """State of steps decided on the device: every row stores n_stored = context - 1
+        positions before step 0, and step s decodes token tokens[s, b], which joins the
+        history (N_s = context + s, as in the host plan)."""
+        w, dev = self.w, self.device
+        if tokens is None or boundary_tokens is None:
+            raise ValueError("device_control needs the decoded tokens and the boundary ids")
+        if w.context < 1:
+            raise ValueError("device_control needs context >= 1")
+        B = w.batch
+        self.n_stored = w.context - 1
+        self.tokens_d = torch.as_tensor(tokens, dtype=torch.int32).to(dev).contiguous()
+        if tuple(self.tokens_d.shape) != (w.steps, B):
+            raise ValueError(f"tokens must be [steps, batch] = {(w.steps, B)}")
+        self.boundary_d = torch.as_tensor(list(boundary_tokens) or [0],
+                                          dtype=torch.int32).to(dev)
+        self.n_boundary = len(boundary_tokens)
+        # state rows: seq_lens, since_slow, recent_start (initial values in state0)
+        self.state0 = torch.stack([
+            torch.full((B,), self.n_stored, dtype=torch.int32),
+            torch.full((B,), -1, dtype=torch.int32),
+            torch.zeros(B, dtype=torch.int32)]).to(dev)
+        self.state = self.state0.clone()
+        self.lists = torch.full((2, B), -1, dtype=torch.int32, device=dev)  # slow, fast
+        self.counts = torch.zeros(2, dtype=torch.int32, device=dev)
+
+    def _take_new_rows(self, lb: LayerBuffers):
+        """K/V rows appended at each step, [S, B, Hkv, D]: the generated rows at positions
+        N_s - 1 = context + s - 1.  Their cache slots are then zeroed."""
+        w = self.w
+        S, B = w.steps, w.batch
+        pos = torch.arange(S, device=self.device) + (w.context - 1)          # [S]
+        pages = lb.block_table[:, pos // w.page_size].t()                     # [S, B]
+        slots = (pos % w.page_size)[:, None].expand(S, B)
+        k_new = lb.k_cache[pages, :, slots].contiguous()                      # [S, B, Hkv, D]
+        v_new = lb.v_cache[pages, :, slots].contiguous()
+        lb.k_cache[pages, :, slots] = 0
+        lb.v_cache[pages, :, slots] = 0
+        return k_new, v_new
+
+    def reset_device_control(self) -> None:
+        """Back to the state before step 0 (on stream 1)."""
+        with torch.cuda.stream(self.stream1):
+            self.state.copy_(self.state0)
+
+    def _issue_device_step(self, s: int) -> None:
+        """Step s with the slow/fast decision and the K/V append on the device.  Every call
+        gets the whole -1-padded row list, so nothing here depends on the decision."""
+        w, lib, shp, prm, ok = self.w, self._lib, self._shp, self._prm, self._ok
+        B = w.batch
+        h1 = self._h1
+        s1 = self.stream1
+        sl_p, rs_p = self._dc["seq_lens"], self._dc["rstart"]
+        slow_p, fast_p = self._dc["slow"], self._dc["fast"]
+        ws_slow, ws_slow_n = self._ws["slow"]
+        ws_fast, ws_fast_n = self._ws["fast"]
+        win = self.window
+        ok("sfi_step_control", lib.sfi_step_control(
+            shp, prm, w.refresh_budget, self._dc["tok"] + s * B * 4, self._dc["bnd"],
+            self.n_boundary, sl_p, self._dc["since"], rs_p, slow_p, fast_p, self._dc["cnt"],
+            h1))
+        for li, lb in enumerate(self.layers):
+            P = lb.ptr
+            ok("sfi_kv_append", lib.sfi_kv_append(
+                shp, P["kn"] + s * lb.kn_step, P["vn"] + s * lb.kn_step, P["k"], P["v"],
+                P["bt"], sl_p, self._all_p, B, P["norm"], self.stride, h1))
+            if lb.pack_pending:
+                s1.wait_event(lb.ev_pack)
+                lb.pack_pending = False
+            ok("sfi_fast_attn", lib.sfi_fast_attn(
+                shp, P["q"] + s * lb.q_step, P["pk"], P["pv"], P["pl"], self.packed_cap,
+                P["k"], P["v"], P["bt"], rs_p, sl_p, fast_p, B, self.max_recent, P["out"],
+                None, ws_fast, ws_fast_n, h1))
+            ok("sfi_slow_attn_window", lib.sfi_slow_attn_window(
+                shp, win, P["qw"] + s * lb.qw_step, P["k"], P["v"], P["bt"], sl_p, slow_p, B,
+                self.max_len, P["out"], P["z"], self.stride, P["lse"], ws_slow, ws_slow_n, h1))
+            k = li % len(self.sel_streams)
+            s2, h2 = self.sel_streams[k], self._h2[k]
+            ws_sel, ws_sel_n = self._ws_sel[k]
+            if s2 is not s1:
+                lb.ev_attn.record(s1)
+                s2.wait_event(lb.ev_attn)
+            ok("sfi_select_window", lib.sfi_select_window(
+                shp, prm, win, P["z"], self.stride, P["lse"], P["norm"], self.stride, sl_p,
+                slow_p, B, self.max_len, P["sel"], self._dbg_p, ws_sel, ws_sel_n, h2))
+            ok("sfi_pack", lib.sfi_pack(
+                shp, prm, P["k"], P["v"], P["bt"], P["sel"], slow_p, B, P["pk"], P["pv"],
+                P["pp"], P["pl"], self.packed_cap, h2))
+            if s2 is not s1:
+                lb.ev_pack.record(s2)
+                lb.pack_pending = True
+
+    def _device_step(self, s: int, timer: Optional[list]) -> None:
+        if s == 0:
+            self.join()
+            self.reset_device_control()
+        s1 = self.stream1
+        e0 = e1 = None
+        if timer is not None:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s1)
+        if s in self.graphs:
+            self.join()
+            with torch.cuda.stream(s1):
+                self.graphs[s].replay()
+        else:
+            self._issue_device_step(s)
+        if timer is not None:
+            e1.record(s1)
+            timer.append(("step", e0, e1, 0, len(self.layers)))
+
+    def enable_device_graphs(self) -> None:
+        """Capture every step of a device-controlled trajectory as one HIP graph: the step
+        control, and for every layer the append, both attention calls and the Selector and
+        pack on their streams (joined back into stream 1 at the end of the graph).  A replay
+        needs nothing from the host but the launch.  Call after the last add_layer."""
+        if not self.device_control:
+            raise RuntimeError("enable_device_graphs needs device_control")
+        self._bind()
+        self.join()
+        self.stream1.wait_stream(torch.cuda.current_stream(self.device))
+        torch.cuda.synchronize()
+        self.graphs = {}
+        pool = None
+        for s in range(self.w.steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream1, pool=pool):
+                self._issue_device_step(s)
+                self.join()
+            pool = g.pool()
+            self.graphs[s] = g
+        self.graph = self.graphs or None
+        torch.cuda.synchronize()
 
     # ------------------------------------------------------------ algorithmic traffic
     def fast_bytes(self, s: int) -> int:
@@ -270,11 +435,20 @@ class Engine:
                 ("pk", "packed_k"), ("pv", "packed_v"), ("pp", "packed_pos"),
                 ("pl", "packed_len"), ("out", "out"))}
             lb.q_step = lb.q_all[0].numel() * lb.q_all.element_size()
+            if lb.k_new is not None:
+                lb.ptr["kn"], lb.ptr["vn"] = lb.k_new.data_ptr(), lb.v_new.data_ptr()
+                lb.kn_step = lb.k_new[0].numel() * lb.k_new.element_size()
             if lb.q_win is not None:
                 lb.ptr["qw"] = lb.q_win.data_ptr()
                 lb.qw_step = lb.q_win[0].numel() * lb.q_win.element_size()
             else:
                 lb.ptr["qw"], lb.qw_step = lb.ptr["q"], lb.q_step
+        if self.device_control:
+            st = self.state
+            self._dc = dict(tok=self.tokens_d.data_ptr(), bnd=self.boundary_d.data_ptr(),
+                            seq_lens=st[0].data_ptr(), since=st[1].data_ptr(),
+                            rstart=st[2].data_ptr(), slow=self.lists[0].data_ptr(),
+                            fast=self.lists[1].data_ptr(), cnt=self.counts.data_ptr())
         self._bound_layers = len(self.layers)
 
     def enable_graphs(self, min_layers: int = kGraphMinLayers) -> None:
@@ -333,6 +507,9 @@ class Engine:
         """
         if getattr(self, "_bound_layers", -1) != len(self.layers):
             self._bind()
+        if self.device_control and not dense_only:
+            self._device_step(s, timer)
+            return
         # The graph waits for every layer's pending pack before its first call, so the
         # first fast step after a slow step is issued call by call: its layer i then waits
         # only for layer i's pack and overlaps the Selector work still queued on stream 2.
@@ -343,6 +520,9 @@ class Engine:
         w, lib, shp, prm = self.w, self._lib, self._shp, self._prm
         n_slow = len(self.plan.slow_ids[s])
         n_fast = len(self.plan.fast_ids[s])
+        # rows each call is given (its list is -1 padded past the listed rows)
+        m_slow = w.batch if self.full_lists else n_slow
+        m_fast = w.batch if self.full_lists else n_fast
         seq_len = self._seq_len_p + s * self._rowb
         rstart = self._rstart_p + s * self._rowb
         slow_ids = self._slow_p + s * self._rowb
@@ -385,13 +565,13 @@ class Engine:
             if n_fast:
                 timed(li, "fast", fb, lambda: ok("sfi_fast_attn", lib.sfi_fast_attn(
                     shp, q, P["pk"], P["pv"], P["pl"], self.packed_cap, P["k"], P["v"],
-                    P["bt"], rstart, seq_len, fast_ids, n_fast, self.max_recent, P["out"],
+                    P["bt"], rstart, seq_len, fast_ids, m_fast, self.max_recent, P["out"],
                     None, ws_fast, ws_fast_n, h1)))
             if n_slow:
                 qw = P["qw"] + s * lb.qw_step
                 timed(li, "slow", db, lambda: ok(
                     "sfi_slow_attn_window", lib.sfi_slow_attn_window(
-                        shp, win, qw, P["k"], P["v"], P["bt"], seq_len, slow_ids, n_slow,
+                        shp, win, qw, P["k"], P["v"], P["bt"], seq_len, slow_ids, m_slow,
                         self.max_len, P["out"], P["z"], self.stride, P["lse"], ws_slow,
                         ws_slow_n, h1)))
                 k = li % len(self.sel_streams)
@@ -402,10 +582,10 @@ class Engine:
                     s2.wait_event(lb.ev_attn)
                 ok("sfi_select_window", lib.sfi_select_window(
                     shp, prm, win, P["z"], self.stride, P["lse"], P["norm"], self.stride, seq_len,
-                    slow_ids, n_slow, self.max_len, P["sel"], self._dbg_p, ws_sel, ws_sel_n,
+                    slow_ids, m_slow, self.max_len, P["sel"], self._dbg_p, ws_sel, ws_sel_n,
                     h2))
                 ok("sfi_pack", lib.sfi_pack(
-                    shp, prm, P["k"], P["v"], P["bt"], P["sel"], slow_ids, n_slow, P["pk"],
+                    shp, prm, P["k"], P["v"], P["bt"], P["sel"], slow_ids, m_slow, P["pk"],
                     P["pv"], P["pp"], P["pl"], self.packed_cap, h2))
                 if s2 is not s1:
                     lb.ev_pack.record(s2)

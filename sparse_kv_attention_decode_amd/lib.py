@@ -23,7 +23,7 @@ SFI_BF16, SFI_F32 = 0, 1
 EXPORTS = ["sfi_abi_version", "sfi_status_str", "sfi_slow_attn_ws", "sfi_fast_attn_ws",
            "sfi_select_ws", "sfi_packed_cap", "sfi_key_norms", "sfi_slow_attn", "sfi_select",
            "sfi_pack", "sfi_fast_attn", "sfi_slow_attn_window_ws", "sfi_select_window_ws",
-           "sfi_slow_attn_window", "sfi_select_window"]
+           "sfi_slow_attn_window", "sfi_select_window", "sfi_step_control", "sfi_kv_append"]
 
 
 class SfiShape(ctypes.Structure):
@@ -74,6 +74,9 @@ _SIGS = {
                                             _P, _I64, _P, _P, _SZ, _P]),
     "sfi_select_window": (ctypes.c_int, [_SHP, _PRM, _I32, _P, _I64, _P, _P, _I64, _P, _P, _I32,
                                          _I32, _P, _P, _P, _SZ, _P]),
+    "sfi_step_control": (ctypes.c_int, [_SHP, _PRM, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P,
+                                        _P]),
+    "sfi_kv_append": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I64, _P]),
     "sfi_fast_attn": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32,
                                      _I32, _P, _P, _P, _SZ, _P]),
 }
@@ -241,3 +244,21 @@ def sfi_fast_attn(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache,
                               _ptr(seq_ids), n_seqs, max_recent, _ptr(out), _ptr(lse),
                               _ptr(ws), ws_bytes, _stream(stream))
     _check("sfi_fast_attn", rc)
+
+
+def sfi_step_control(shape, params, refresh_budget, token_ids, boundary_tokens, n_boundary,
+                     seq_lens, since_slow, recent_start, slow_ids, fast_ids, counts,
+                     stream=None) -> None:
+    rc = load().sfi_step_control(ctypes.byref(shape), ctypes.byref(params), refresh_budget,
+                                 _ptr(token_ids), _ptr(boundary_tokens), n_boundary,
+                                 _ptr(seq_lens), _ptr(since_slow), _ptr(recent_start),
+                                 _ptr(slow_ids), _ptr(fast_ids), _ptr(counts), _stream(stream))
+    _check("sfi_step_control", rc)
+
+
+def sfi_kv_append(shape, k_new, v_new, k_cache, v_cache, block_table, seq_lens, seq_ids, n_seqs,
+                  key_norm, norm_stride, stream=None) -> None:
+    rc = load().sfi_kv_append(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                              _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(seq_ids),
+                              n_seqs, _ptr(key_norm), norm_stride, _stream(stream))
+    _check("sfi_kv_append", rc)
