@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SFI_ABI_VERSION 3
+#define SFI_ABI_VERSION 4
 
 enum sfi_status {
   SFI_OK = 0,
@@ -111,6 +111,11 @@ size_t sfi_slow_attn_window_ws(const sfi_shape* shape, int32_t window, int32_t n
                                int32_t max_seq_len);
 size_t sfi_select_window_ws(const sfi_shape* shape, const sfi_select_params* params,
                             int32_t window, int32_t n_seqs, int32_t max_seq_len);
+
+/* The same for sfi_decode_attn: the fast call's workspace rounded up to 256 bytes plus the
+ * windowed slow call's. */
+size_t sfi_decode_attn_ws(const sfi_shape* shape, int32_t window, int32_t n_seqs,
+                          int32_t packed_cap, int32_t max_recent, int32_t max_seq_len);
 
 /* Round-up of n_sink + top_k to a multiple of 16: rows per (b, KV head) of the packed
  * buffers. */
@@ -230,26 +235,51 @@ int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
                   float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sfi_decode_attn -- the attention of a whole decode step in one partial launch and one
+ * merge launch: the rows listed in fast_ids get sfi_fast_attn (lse not written), the rows
+ * listed in slow_ids get sfi_slow_attn_window, with the same arguments those calls take.
+ * Both lists hold n_seqs slots (-1 = unused) and must not share a row.  The results are
+ * bit-identical to the two separate calls with the same lists and n_seqs.  For steps
+ * decided on the device (sfi_step_control), where the host does not know which list is
+ * empty, this saves the launches of the empty call.
+ * ws: sfi_decode_attn_ws(shape, window, n_seqs, packed_cap, max_recent, max_seq_len) bytes.
+ */
+int sfi_decode_attn(const sfi_shape* shape, int32_t window, const float* q,
+                    const float* q_win, const void* packed_k, const void* packed_v,
+                    const int32_t* packed_len, int32_t packed_cap, const void* k_cache,
+                    const void* v_cache, const int32_t* block_table,
+                    const int32_t* recent_start, const int32_t* seq_lens,
+                    const int32_t* fast_ids, const int32_t* slow_ids, int32_t n_seqs,
+                    int32_t max_recent, int32_t max_seq_len, float* out, float* logits,
+                    int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/*
  * sfi_step_control -- the slow/fast decision of one decode step for every row of the batch,
  * on the device (es "Pasos Lentos", zh "2.1 触发机制": a slow step follows a semantic-
  * boundary token such as sentence punctuation or a line break, or a spent refresh budget).
- * For each row b:
- *   seq_lens[b]    += 1                       (the token decoded now joins the history)
- *   slow            = since_slow[b] < 0       (no slow step yet)
+ * The state is i32 [3, batch]: rows seq_lens, since_slow, recent_start.  For each row b,
+ * from state_in to state_out:
+ *   seq_lens        = seq_lens + 1            (the token decoded now joins the history)
+ *   slow            = since_slow < 0          (no slow step yet)
  *                     || token_ids[b] is one of boundary_tokens[0..n_boundary)
- *                     || since_slow[b] >= refresh_budget
- *   since_slow[b]   = slow ? 0 : since_slow[b] + 1
- *   recent_start[b] = max(n_sink, seq_lens[b] - n_recent)   when slow (else unchanged)
+ *                     || since_slow >= refresh_budget
+ *   since_slow      = slow ? 0 : since_slow + 1
+ *   recent_start    = slow ? max(n_sink, seq_lens - n_recent) : recent_start
  * slow_ids / fast_ids [batch] receive the slow and the fast rows in ascending order, each
  * padded with -1; counts [2] = {slow rows, fast rows}.  n_sink and n_recent come from
  * params.  Initial state: seq_lens = stored length before the first step, since_slow = -1.
+ * state_out may be state_in.  The calls of the step read seq_lens and recent_start from
+ * state_out (rows 0 and 2) and the lists; work of the previous step still running on
+ * another stream reads the previous buffers, so a caller that overlaps steps alternates
+ * two state buffers and two pairs of lists.
  * Requires refresh_budget >= 0 and 0 <= n_boundary <= 1024 (SFI_E_UNSUPPORTED beyond).
  * One workgroup; rows are independent.
  */
 int sfi_step_control(const sfi_shape* shape, const sfi_select_params* params,
                      int32_t refresh_budget, const int32_t* token_ids,
-                     const int32_t* boundary_tokens, int32_t n_boundary, int32_t* seq_lens,
-                     int32_t* since_slow, int32_t* recent_start, int32_t* slow_ids,
+                     const int32_t* boundary_tokens, int32_t n_boundary,
+                     const int32_t* state_in, int32_t* state_out, int32_t* slow_ids,
                      int32_t* fast_ids, int32_t* counts, void* stream);
 
 /*

@@ -130,13 +130,13 @@ int window_shape(const sfi_shape* shape, int32_t window, sfi_shape* out) {
   return SFI_OK;
 }
 
-// Dense attention of the rows of `shape` (already widened by the window); the output is
-// written for window slot 0 only.
-int slow_attn(const sfi_shape* shape, int32_t window, const float* q, const void* k_cache,
+// Checks of a slow call of `shape` (already widened by the window) and its launch
+// parameters in *p; the output is written for window slot 0 only.
+int prep_slow(const sfi_shape* shape, int32_t window, const float* q, const void* k_cache,
               const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
               const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len, float* out,
               float* logits, int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
-              void* stream) {
+              sfi::AttnParams* pp) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !seq_ids || !out || !lse)
@@ -150,9 +150,11 @@ int slow_attn(const sfi_shape* shape, int32_t window, const float* q, const void
   }
   const size_t need = sfi_slow_attn_ws(shape, n_seqs, max_seq_len);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SFI_E_WORKSPACE;
+  sfi::AttnParams& p = *pp;
+  p = {};
+  p.n_seqs = n_seqs;
   if (n_seqs == 0) return SFI_OK;
   const SplitPlan sp = sfi::plan_slow(*shape, n_seqs, max_seq_len);
-  sfi::AttnParams p = {};
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
@@ -178,6 +180,19 @@ int slow_attn(const sfi_shape* shape, int32_t window, const float* q, const void
   p.fast = 0;
   p.win = window;
   p.scale = 1.0f / sqrtf((float)shape->head_dim);
+  return SFI_OK;
+}
+
+int slow_attn(const sfi_shape* shape, int32_t window, const float* q, const void* k_cache,
+              const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+              const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len, float* out,
+              float* logits, int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
+              void* stream) {
+  sfi::AttnParams p;
+  const int rc = prep_slow(shape, window, q, k_cache, v_cache, block_table, seq_lens, seq_ids,
+                           n_seqs, max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes,
+                           &p);
+  if (rc || n_seqs == 0) return rc;
   return finish(sfi::launch_attention(p, shape->head_dim, shape->dtype, out, lse,
                                       reinterpret_cast<hipStream_t>(stream)));
 }
@@ -283,21 +298,21 @@ int sfi_pack(const sfi_shape* shape, const sfi_select_params* params, const void
 
 int sfi_step_control(const sfi_shape* shape, const sfi_select_params* params,
                      int32_t refresh_budget, const int32_t* token_ids,
-                     const int32_t* boundary_tokens, int32_t n_boundary, int32_t* seq_lens,
-                     int32_t* since_slow, int32_t* recent_start, int32_t* slow_ids,
+                     const int32_t* boundary_tokens, int32_t n_boundary,
+                     const int32_t* state_in, int32_t* state_out, int32_t* slow_ids,
                      int32_t* fast_ids, int32_t* counts, void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if ((rc = check_params(params))) return rc;
   if (refresh_budget < 0 || n_boundary < 0) return SFI_E_ARG;
   if (n_boundary > sfi::kMaxBoundaryTokens) return SFI_E_UNSUPPORTED;
-  if (!token_ids || (n_boundary > 0 && !boundary_tokens) || !seq_lens || !since_slow ||
-      !recent_start || !slow_ids || !fast_ids || !counts)
+  if (!token_ids || (n_boundary > 0 && !boundary_tokens) || !state_in || !state_out ||
+      !slow_ids || !fast_ids || !counts)
     return SFI_E_ARG;
   return finish(sfi::launch_step_control(shape->batch, token_ids, boundary_tokens, n_boundary,
                                          refresh_budget, params->n_sink, params->n_recent,
-                                         seq_lens, since_slow, recent_start, slow_ids, fast_ids,
-                                         counts, reinterpret_cast<hipStream_t>(stream)));
+                                         state_in, state_out, slow_ids, fast_ids, counts,
+                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
 int sfi_kv_append(const sfi_shape* shape, const void* k_new, const void* v_new, void* k_cache,
@@ -318,12 +333,16 @@ int sfi_kv_append(const sfi_shape* shape, const void* k_new, const void* v_new, 
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
-int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
-                  const void* packed_v, const int32_t* packed_len, int32_t packed_cap,
-                  const void* k_cache, const void* v_cache, const int32_t* block_table,
-                  const int32_t* recent_start, const int32_t* seq_lens, const int32_t* seq_ids,
-                  int32_t n_seqs, int32_t max_recent, float* out, float* lse, void* ws,
-                  size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a fast call and its launch parameters in *p.
+int prep_fast(const sfi_shape* shape, const float* q, const void* packed_k, const void* packed_v,
+              const int32_t* packed_len, int32_t packed_cap, const void* k_cache,
+              const void* v_cache, const int32_t* block_table, const int32_t* recent_start,
+              const int32_t* seq_lens, const int32_t* seq_ids, int32_t n_seqs,
+              int32_t max_recent, float* out, void* ws, size_t ws_bytes, sfi::AttnParams* pp) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!q || !packed_k || !packed_v || !packed_len || !k_cache || !v_cache || !block_table ||
@@ -338,9 +357,11 @@ int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
     return SFI_E_ALIGN;
   const size_t need = sfi_fast_attn_ws(shape, n_seqs, packed_cap, max_recent);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SFI_E_WORKSPACE;
+  sfi::AttnParams& p = *pp;
+  p = {};
+  p.n_seqs = n_seqs;
   if (n_seqs == 0) return SFI_OK;
   const SplitPlan sp = sfi::plan_fast(*shape, n_seqs, packed_cap, max_recent);
-  sfi::AttnParams p = {};
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
@@ -360,7 +381,6 @@ int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
   p.part_o = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + 2 * ml);
   p.max_pages = shape->max_pages_per_seq;
   p.packed_cap = packed_cap;
-  p.n_seqs = n_seqs;
   p.Hq = shape->num_q_heads;
   p.Hkv = shape->num_kv_heads;
   p.G = p.Hq / p.Hkv;
@@ -370,8 +390,68 @@ int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
   p.fast = 1;
   p.win = 1;
   p.scale = 1.0f / sqrtf((float)shape->head_dim);
+  return SFI_OK;
+}
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" {
+
+int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
+                  const void* packed_v, const int32_t* packed_len, int32_t packed_cap,
+                  const void* k_cache, const void* v_cache, const int32_t* block_table,
+                  const int32_t* recent_start, const int32_t* seq_lens, const int32_t* seq_ids,
+                  int32_t n_seqs, int32_t max_recent, float* out, float* lse, void* ws,
+                  size_t ws_bytes, void* stream) {
+  sfi::AttnParams p;
+  const int rc = prep_fast(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache,
+                           v_cache, block_table, recent_start, seq_lens, seq_ids, n_seqs,
+                           max_recent, out, ws, ws_bytes, &p);
+  if (rc || n_seqs == 0) return rc;
   return finish(sfi::launch_attention(p, shape->head_dim, shape->dtype, out, lse,
                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t sfi_decode_attn_ws(const sfi_shape* shape, int32_t window, int32_t n_seqs,
+                          int32_t packed_cap, int32_t max_recent, int32_t max_seq_len) {
+  const size_t f = sfi_fast_attn_ws(shape, n_seqs, packed_cap, max_recent);
+  const size_t sl = sfi_slow_attn_window_ws(shape, window, n_seqs, max_seq_len);
+  if (f == 0 || sl == 0) return 0;
+  return round256(f) + sl;
+}
+
+int sfi_decode_attn(const sfi_shape* shape, int32_t window, const float* q,
+                    const float* q_win, const void* packed_k, const void* packed_v,
+                    const int32_t* packed_len, int32_t packed_cap, const void* k_cache,
+                    const void* v_cache, const int32_t* block_table,
+                    const int32_t* recent_start, const int32_t* seq_lens,
+                    const int32_t* fast_ids, const int32_t* slow_ids, int32_t n_seqs,
+                    int32_t max_recent, int32_t max_seq_len, float* out, float* logits,
+                    int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  sfi_shape sw;
+  int rc = window_shape(shape, window, &sw);
+  if (rc) return rc;
+  const size_t need = sfi_decode_attn_ws(shape, window, n_seqs, packed_cap, max_recent,
+                                         max_seq_len);
+  // (need == 0: an invalid argument, which the checks below name)
+  if (need != 0 && (!ws || ws_bytes < need)) return SFI_E_WORKSPACE;
+  const size_t wf = round256(sfi_fast_attn_ws(shape, n_seqs, packed_cap, max_recent));
+  char* w8 = reinterpret_cast<char*>(ws);
+  sfi::AttnParams pf, ps;
+  if ((rc = prep_fast(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache, v_cache,
+                      block_table, recent_start, seq_lens, fast_ids, n_seqs, max_recent, out, ws,
+                      wf, &pf)))
+    return rc;
+  if ((rc = prep_slow(&sw, window, q_win, k_cache, v_cache, block_table, seq_lens, slow_ids,
+                      n_seqs, max_seq_len, out, logits, logits_stride, lse, w8 + wf,
+                      ws_bytes - wf, &ps)))
+    return rc;
+  if (n_seqs == 0) return SFI_OK;
+  return finish(sfi::launch_attention_pair(pf, ps, shape->head_dim, shape->dtype, out, lse,
+                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -97,21 +97,33 @@ struct Flag {
   static constexpr bool value = B;
 };
 
+constexpr int kAttnWaves = 4;  // wavefronts per bf16 workgroup; they share one split
+
+// LDS of one bf16 workgroup.
+template <int D>
+struct Bf16Lds {
+  float m[kAttnWaves][kMaxG], l[kAttnWaves][kMaxG];
+  float o[kAttnWaves - 1][kMaxG][D];
+  int32_t page[kMaxTilesPerSplit];
+  u32x4_t q[3][D / 32][kWave];  // query operand: hi, mid, lo terms
+};
+
+// Split `work` of the call described by p (one workgroup).
 template <int D, bool WRITE_Z>
-__global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
+__device__ __forceinline__ void attn_partial_bf16(AttnParams p, int work, Bf16Lds<D>& lds) {
   constexpr int NC = D / 32;   // 32-dim steps of the logit product
   constexpr int NT = D / 16;   // 16-dim output tiles of the PV product
-  constexpr int NW = 4;        // wavefronts per workgroup; they share one split
-  __shared__ float sm_m[NW][kMaxG], sm_l[NW][kMaxG];
-  __shared__ float sm_o[NW - 1][kMaxG][D];
-  __shared__ int32_t sm_page[kMaxTilesPerSplit];
-  __shared__ u32x4_t sm_q[3][NC][kWave];  // query operand: hi, mid, lo terms
+  constexpr int NW = kAttnWaves;
+  auto& sm_m = lds.m;
+  auto& sm_l = lds.l;
+  auto& sm_o = lds.o;
+  auto& sm_page = lds.page;
+  auto& sm_q = lds.q;
   const int lane = threadIdx.x & 63;
   // Wave-uniform by construction; readfirstlane lets the compiler keep tile indices and
   // page-table reads scalar (s_load, counted by lgkmcnt) instead of vector loads whose
   // wait would also drain the in-flight K/V prefetch.
   const int wave = uniform(threadIdx.x >> 6);
-  const int work = blockIdx.x;
   if (work >= p.n_seqs * p.Hkv * p.nsplit) return;  // workgroup-uniform
   const int split = work % p.nsplit;
   const int ig = work / p.nsplit;
@@ -400,14 +412,41 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
   }
 }
 
+template <int D, bool WRITE_Z>
+__global__ __launch_bounds__(256) void k_attn_partial_bf16(AttnParams p) {
+  __shared__ Bf16Lds<D> lds;
+  attn_partial_bf16<D, WRITE_Z>(p, blockIdx.x, lds);
+}
+
+// The slow rows and the fast rows of one decode step in one launch: workgroups below the
+// slow call's split count run its splits, the others the fast call's.  The slow call's
+// workgroups come first: it plans one per CU, and dispatched first onto an idle chip they
+// land one per CU as in a launch of their own (behind the fast call's workgroups, which
+// exit at once on a slow step, they were measured 35% slower).
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_partial_bf16_pair(AttnParams pf, AttnParams ps) {
+  __shared__ Bf16Lds<D> lds;
+  const int ns = ps.n_seqs * ps.Hkv * ps.nsplit;
+  if ((int)blockIdx.x < ns)
+    attn_partial_bf16<D, true>(ps, blockIdx.x, lds);
+  else
+    attn_partial_bf16<D, false>(pf, blockIdx.x - ns, lds);
+}
+
+// LDS of one fp32 workgroup.
+template <int D>
+struct F32Lds {
+  float qs[kMaxG][D];
+  float zt[kMaxG][kPage];
+};
+
 // fp32 caches: one wavefront per split, VALU only.
 template <int D, bool WRITE_Z>
-__global__ __launch_bounds__(64) void k_attn_partial_f32(AttnParams p) {
+__device__ __forceinline__ void attn_partial_f32(AttnParams p, int work, F32Lds<D>& lds) {
   constexpr int DD = D / kWave;
-  __shared__ float qs[kMaxG][D];
-  __shared__ float zt[kMaxG][kPage];
+  auto& qs = lds.qs;
+  auto& zt = lds.zt;
   const int lane = threadIdx.x;
-  const int work = blockIdx.x;
   if (work >= p.n_seqs * p.Hkv * p.nsplit) return;
   const int split = work % p.nsplit;
   const int ig = work / p.nsplit;
@@ -523,14 +562,54 @@ __global__ __launch_bounds__(64) void k_attn_partial_f32(AttnParams p) {
   }
 }
 
+template <int D, bool WRITE_Z>
+__global__ __launch_bounds__(64) void k_attn_partial_f32(AttnParams p) {
+  __shared__ F32Lds<D> lds;
+  attn_partial_f32<D, WRITE_Z>(p, blockIdx.x, lds);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void k_attn_partial_f32_pair(AttnParams pf, AttnParams ps) {
+  __shared__ F32Lds<D> lds;
+  const int ns = ps.n_seqs * ps.Hkv * ps.nsplit;
+  if ((int)blockIdx.x < ns)
+    attn_partial_f32<D, true>(ps, blockIdx.x, lds);
+  else
+    attn_partial_f32<D, false>(pf, blockIdx.x - ns, lds);
+}
+
+struct MergeArgs {
+  const float* pm;
+  const float* pl;
+  const float* po;
+  int nsplit, Hq, Hkv, G, D, win;
+  const int32_t* seq_ids;
+  float* out;
+  float* lse;
+};
+
+MergeArgs merge_args(const AttnParams& p, int D, float* out, float* lse) {
+  return MergeArgs{p.part_m, p.part_l, p.part_o, p.nsplit, p.Hq, p.Hkv, p.G, D, p.win,
+                   p.seq_ids, out, lse};
+}
+
+struct MergeLds {
+  float gm[64], gl[64];
+  float4 acc4[256];
+};
+
 // One block per (listed row, query head): log-sum-exp merge of the split partials.
-__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm,
-                                                    const float* __restrict__ pl,
-                                                    const float* __restrict__ po, int nsplit,
-                                                    int Hq, int Hkv, int G, int D, int win,
-                                                    const int32_t* __restrict__ seq_ids,
-                                                    float* __restrict__ out,
-                                                    float* __restrict__ lse) {
+__device__ __forceinline__ void attn_merge(MergeArgs a, int blk, MergeLds& lds) {
+  const float* __restrict__ pm = a.pm;
+  const float* __restrict__ pl = a.pl;
+  const float* __restrict__ po = a.po;
+  const int nsplit = a.nsplit, Hq = a.Hq, Hkv = a.Hkv, G = a.G, D = a.D, win = a.win;
+  const int32_t* __restrict__ seq_ids = a.seq_ids;
+  float* __restrict__ out = a.out;
+  float* __restrict__ lse = a.lse;
+  auto& gm = lds.gm;
+  auto& gl = lds.gl;
+  auto& acc4 = lds.acc4;
   // Thread (grp, col) folds splits grp, grp + ngrp, ... of column block col into a running
   // (max, sum, weighted o); the loads of kUnroll splits are issued together.  The groups
   // are then combined in LDS.
@@ -539,11 +618,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm
   // lse is written for every row, the output only for slot 0 (the current query), into
   // the [batch][Hq / win][D] layout of the model's own heads.
   constexpr int kUnroll = 8;
-  __shared__ float gm[64], gl[64];
-  __shared__ float4 acc4[256];
   const int tid = threadIdx.x;
-  const int i = blockIdx.x / Hq;
-  const int h = blockIdx.x % Hq;
+  const int i = blk / Hq;
+  const int h = blk % Hq;
   const int g = h / G, hh = h % G;
   const int b = seq_ids[i];
   if (b < 0) return;  // unused slot of the row list (block-uniform)
@@ -608,6 +685,20 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pm
           make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
     if (col == 0 && lse) lse[(size_t)b * Hq + h] = Lt > 0.f ? Mu + logf(Lt) : -INFINITY;
   }
+}
+
+__global__ __launch_bounds__(256) void k_attn_merge(MergeArgs a) {
+  __shared__ MergeLds lds;
+  attn_merge(a, blockIdx.x, lds);
+}
+
+// Merge blocks of the slow call, then of the fast call.
+__global__ __launch_bounds__(256) void k_attn_merge_pair(MergeArgs af, MergeArgs as, int ns) {
+  __shared__ MergeLds lds;
+  if ((int)blockIdx.x < ns)
+    attn_merge(as, blockIdx.x, lds);
+  else
+    attn_merge(af, blockIdx.x - ns, lds);
 }
 
 template <int D>
@@ -682,9 +773,32 @@ hipError_t launch_attention(const AttnParams& p0, int head_dim, int dtype, float
   hipError_t e = head_dim == 64 ? launch_partial<64>(p, dtype, stream)
                                 : launch_partial<128>(p, dtype, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(p.n_seqs * p.Hq), dim3(256), 0, stream, p.part_m,
-                     p.part_l, p.part_o, p.nsplit, p.Hq, p.Hkv, p.G, head_dim, p.win, p.seq_ids,
-                     out, lse);
+  hipLaunchKernelGGL(k_attn_merge, dim3(p.n_seqs * p.Hq), dim3(256), 0, stream,
+                     merge_args(p, head_dim, out, lse));
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_pair(const AttnParams& pf, const AttnParams& ps, int head_dim,
+                                 int dtype, float* out, float* lse_slow, hipStream_t stream) {
+  const int works = pf.n_seqs * pf.Hkv * pf.nsplit + ps.n_seqs * ps.Hkv * ps.nsplit;
+  if (dtype == SFI_BF16) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL(k_attn_partial_bf16_pair<64>, dim3(works), dim3(256), 0, stream, pf, ps);
+    else
+      hipLaunchKernelGGL(k_attn_partial_bf16_pair<128>, dim3(works), dim3(256), 0, stream, pf,
+                         ps);
+  } else {
+    if (head_dim == 64)
+      hipLaunchKernelGGL(k_attn_partial_f32_pair<64>, dim3(works), dim3(64), 0, stream, pf, ps);
+    else
+      hipLaunchKernelGGL(k_attn_partial_f32_pair<128>, dim3(works), dim3(64), 0, stream, pf, ps);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ns = ps.n_seqs * ps.Hq;
+  hipLaunchKernelGGL(k_attn_merge_pair, dim3(pf.n_seqs * pf.Hq + ns), dim3(256), 0, stream,
+                     merge_args(pf, head_dim, out, nullptr),
+                     merge_args(ps, head_dim, out, lse_slow), ns);
   return hipGetLastError();
 }
 

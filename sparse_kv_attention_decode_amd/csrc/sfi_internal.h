@@ -52,6 +52,10 @@ struct AttnParams {
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, int dtype, float* out,
                             float* lse, hipStream_t stream);
+// A fast call (pf, no lse) and a slow call (ps) in one partial and one merge launch; both
+// write `out`, for the rows of their own lists.
+hipError_t launch_attention_pair(const AttnParams& pf, const AttnParams& ps, int head_dim,
+                                 int dtype, float* out, float* lse_slow, hipStream_t stream);
 
 hipError_t launch_key_norms(const sfi_shape& s, const void* k_cache,
                             const int32_t* block_table, const int32_t* seq_lens,
@@ -84,9 +88,8 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm,
 
 hipError_t launch_step_control(int batch, const int32_t* tokens, const int32_t* boundary,
                                int n_boundary, int budget, int n_sink, int n_recent,
-                               int32_t* seq_lens, int32_t* since, int32_t* recent_start,
-                               int32_t* slow_ids, int32_t* fast_ids, int32_t* counts,
-                               hipStream_t stream);
+                               const int32_t* state_in, int32_t* state_out, int32_t* slow_ids,
+                               int32_t* fast_ids, int32_t* counts, hipStream_t stream);
 // Longest boundary-token table sfi_step_control takes.
 constexpr int kMaxBoundaryTokens = 1024;
 

@@ -18,9 +18,8 @@ constexpr int kCtrlThreads = 256;
 struct CtrlArgs {
   const int32_t* tokens;     // [batch] token each row decodes this step
   const int32_t* boundary;   // [n_boundary] boundary token ids
-  int32_t* seq_lens;         // [batch] in/out
-  int32_t* since;            // [batch] in/out: fast steps since the last slow step, < 0: none
-  int32_t* recent_start;     // [batch] in/out
+  const int32_t* state_in;   // [3][batch]: seq_lens, since_slow, recent_start
+  int32_t* state_out;        // [3][batch], may be state_in
   int32_t* slow_ids;         // [batch] out
   int32_t* fast_ids;         // [batch] out
   int32_t* counts;           // [2] out
@@ -38,16 +37,18 @@ __global__ __launch_bounds__(kCtrlThreads) void k_step_control(CtrlArgs a) {
     const bool live = b < a.batch;
     bool slow = false;
     if (live) {
-      const int N = a.seq_lens[b] + 1;  // the decoded token is appended this step
-      a.seq_lens[b] = N;
-      const int since = a.since[b];
+      const int B = a.batch;
+      const int N = a.state_in[b] + 1;  // the decoded token is appended this step
+      const int since = a.state_in[B + b];
+      const int rs = a.state_in[2 * B + b];
       const int tok = a.tokens[b];
       bool boundary = false;
       for (int k = 0; k < a.n_boundary; ++k) boundary |= a.boundary[k] == tok;
       slow = since < 0 || boundary || since >= a.budget;
-      a.since[b] = slow ? 0 : since + 1;
+      a.state_out[b] = N;
+      a.state_out[B + b] = slow ? 0 : since + 1;
       // The recent segment's left edge is frozen at the slow step.
-      if (slow) a.recent_start[b] = max(a.n_sink, N - a.n_recent);
+      a.state_out[2 * B + b] = slow ? max(a.n_sink, N - a.n_recent) : rs;
     }
     uint32_t tot_s, tot_f;
     const uint32_t ps = block_exscan<kCtrlThreads>(live && slow ? 1u : 0u, wsum, &tot_s);
@@ -144,15 +145,13 @@ hipError_t append_t(const sfi_shape& s, const void* k_new, const void* v_new, vo
 
 hipError_t launch_step_control(int batch, const int32_t* tokens, const int32_t* boundary,
                                int n_boundary, int budget, int n_sink, int n_recent,
-                               int32_t* seq_lens, int32_t* since, int32_t* recent_start,
-                               int32_t* slow_ids, int32_t* fast_ids, int32_t* counts,
-                               hipStream_t stream) {
+                               const int32_t* state_in, int32_t* state_out, int32_t* slow_ids,
+                               int32_t* fast_ids, int32_t* counts, hipStream_t stream) {
   CtrlArgs a;
   a.tokens = tokens;
   a.boundary = boundary;
-  a.seq_lens = seq_lens;
-  a.since = since;
-  a.recent_start = recent_start;
+  a.state_in = state_in;
+  a.state_out = state_out;
   a.slow_ids = slow_ids;
   a.fast_ids = fast_ids;
   a.counts = counts;

@@ -270,14 +270,21 @@ class Engine:
         self.boundary_d = torch.as_tensor(list(boundary_tokens) or [0],
                                           dtype=torch.int32).to(dev)
         self.n_boundary = len(boundary_tokens)
-        # state rows: seq_lens, since_slow, recent_start (initial values in state0)
+        # State rows: seq_lens, since_slow, recent_start; state0 holds the values before step
+        # 0.  Step s reads the state step s - 1 wrote and writes buffer s % 2 and row lists
+        # s % 2, so the Selector and pack of step s - 1, which may still run on their
+        # streams, keep reading unchanged lengths and lists.  Step s + 1 cannot overwrite
+        # them either: before each layer's attention stream 1 waits for that layer's pack
+        # of the step before.
         self.state0 = torch.stack([
             torch.full((B,), self.n_stored, dtype=torch.int32),
             torch.full((B,), -1, dtype=torch.int32),
             torch.zeros(B, dtype=torch.int32)]).to(dev)
-        self.state = self.state0.clone()
-        self.lists = torch.full((2, B), -1, dtype=torch.int32, device=dev)  # slow, fast
-        self.counts = torch.zeros(2, dtype=torch.int32, device=dev)
+        self.state_bufs = [self.state0.clone(), self.state0.clone()]
+        self.ws_decode = L.workspace(L.sfi_decode_attn_ws(
+            self.shape, self.window, B, self.packed_cap, self.max_recent, self.max_len), dev)
+        self.lists = torch.full((2, 2, B), -1, dtype=torch.int32, device=dev)  # [parity][slow, fast]
+        self.counts = torch.zeros(2, 2, dtype=torch.int32, device=dev)
 
     def _take_new_rows(self, lb: LayerBuffers):
         """K/V rows appended at each step, [S, B, Hkv, D]: the generated rows at positions
@@ -293,10 +300,9 @@ class Engine:
         lb.v_cache[pages, :, slots] = 0
         return k_new, v_new
 
-    def reset_device_control(self) -> None:
-        """Back to the state before step 0 (on stream 1)."""
-        with torch.cuda.stream(self.stream1):
-            self.state.copy_(self.state0)
+    def device_state(self, s: int) -> torch.Tensor:
+        """State [3, B] (seq_lens, since_slow, recent_start) written by step s."""
+        return self.state_bufs[s % 2]
 
     def _issue_device_step(self, s: int) -> None:
         """Step s with the slow/fast decision and the K/V append on the device.  Every call
@@ -305,15 +311,16 @@ class Engine:
         B = w.batch
         h1 = self._h1
         s1 = self.stream1
-        sl_p, rs_p = self._dc["seq_lens"], self._dc["rstart"]
-        slow_p, fast_p = self._dc["slow"], self._dc["fast"]
-        ws_slow, ws_slow_n = self._ws["slow"]
-        ws_fast, ws_fast_n = self._ws["fast"]
+        par = s % 2
+        dc = self._dc[par]
+        st_in = self._dc_state0 if s == 0 else self._dc[1 - par]["state"]
+        sl_p, rs_p = dc["seq_lens"], dc["rstart"]
+        slow_p, fast_p = dc["slow"], dc["fast"]
+        ws_dec, ws_dec_n = self._ws["decode"]
         win = self.window
         ok("sfi_step_control", lib.sfi_step_control(
-            shp, prm, w.refresh_budget, self._dc["tok"] + s * B * 4, self._dc["bnd"],
-            self.n_boundary, sl_p, self._dc["since"], rs_p, slow_p, fast_p, self._dc["cnt"],
-            h1))
+            shp, prm, w.refresh_budget, self._dc_tok + s * B * 4, self._dc_bnd,
+            self.n_boundary, st_in, dc["state"], slow_p, fast_p, dc["cnt"], h1))
         for li, lb in enumerate(self.layers):
             P = lb.ptr
             ok("sfi_kv_append", lib.sfi_kv_append(
@@ -322,13 +329,13 @@ class Engine:
             if lb.pack_pending:
                 s1.wait_event(lb.ev_pack)
                 lb.pack_pending = False
-            ok("sfi_fast_attn", lib.sfi_fast_attn(
-                shp, P["q"] + s * lb.q_step, P["pk"], P["pv"], P["pl"], self.packed_cap,
-                P["k"], P["v"], P["bt"], rs_p, sl_p, fast_p, B, self.max_recent, P["out"],
-                None, ws_fast, ws_fast_n, h1))
-            ok("sfi_slow_attn_window", lib.sfi_slow_attn_window(
-                shp, win, P["qw"] + s * lb.qw_step, P["k"], P["v"], P["bt"], sl_p, slow_p, B,
-                self.max_len, P["out"], P["z"], self.stride, P["lse"], ws_slow, ws_slow_n, h1))
+            # the fast and the slow rows in one launch pair: one of the two lists is empty
+            # at most steps, and its launches would cost as much as a short call
+            ok("sfi_decode_attn", lib.sfi_decode_attn(
+                shp, win, P["q"] + s * lb.q_step, P["qw"] + s * lb.qw_step, P["pk"], P["pv"],
+                P["pl"], self.packed_cap, P["k"], P["v"], P["bt"], rs_p, sl_p, fast_p, slow_p,
+                B, self.max_recent, self.max_len, P["out"], P["z"], self.stride, P["lse"],
+                ws_dec, ws_dec_n, h1))
             k = li % len(self.sel_streams)
             s2, h2 = self.sel_streams[k], self._h2[k]
             ws_sel, ws_sel_n = self._ws_sel[k]
@@ -347,8 +354,8 @@ class Engine:
 
     def _device_step(self, s: int, timer: Optional[list]) -> None:
         if s == 0:
+            # a new trajectory: the last step of the previous one may use buffer 0 too
             self.join()
-            self.reset_device_control()
         s1 = self.stream1
         e0 = e1 = None
         if timer is not None:
@@ -427,6 +434,8 @@ class Engine:
         self._ws_sel = [(t.data_ptr(), t.numel()) for t in self.ws_sels]
         self._ws = {k: (t.data_ptr(), t.numel()) for k, t in
                     (("slow", self.ws_slow), ("fast", self.ws_fast))}
+        if self.device_control:
+            self._ws["decode"] = (self.ws_decode.data_ptr(), self.ws_decode.numel())
         self._dbg_p = self.dbg_buf.data_ptr() if self.dbg_buf is not None else None
         for lb in self.layers:
             lb.ptr = {k: getattr(lb, a).data_ptr() for k, a in (
@@ -444,11 +453,14 @@ class Engine:
             else:
                 lb.ptr["qw"], lb.qw_step = lb.ptr["q"], lb.q_step
         if self.device_control:
-            st = self.state
-            self._dc = dict(tok=self.tokens_d.data_ptr(), bnd=self.boundary_d.data_ptr(),
-                            seq_lens=st[0].data_ptr(), since=st[1].data_ptr(),
-                            rstart=st[2].data_ptr(), slow=self.lists[0].data_ptr(),
-                            fast=self.lists[1].data_ptr(), cnt=self.counts.data_ptr())
+            self._dc_tok = self.tokens_d.data_ptr()
+            self._dc_bnd = self.boundary_d.data_ptr()
+            self._dc_state0 = self.state0.data_ptr()
+            self._dc = [dict(state=st.data_ptr(), seq_lens=st[0].data_ptr(),
+                             rstart=st[2].data_ptr(), slow=self.lists[par, 0].data_ptr(),
+                             fast=self.lists[par, 1].data_ptr(),
+                             cnt=self.counts[par].data_ptr())
+                        for par, st in enumerate(self.state_bufs)]
         self._bound_layers = len(self.layers)
 
     def enable_graphs(self, min_layers: int = kGraphMinLayers) -> None:

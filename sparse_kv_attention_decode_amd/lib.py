@@ -23,7 +23,8 @@ SFI_BF16, SFI_F32 = 0, 1
 EXPORTS = ["sfi_abi_version", "sfi_status_str", "sfi_slow_attn_ws", "sfi_fast_attn_ws",
            "sfi_select_ws", "sfi_packed_cap", "sfi_key_norms", "sfi_slow_attn", "sfi_select",
            "sfi_pack", "sfi_fast_attn", "sfi_slow_attn_window_ws", "sfi_select_window_ws",
-           "sfi_slow_attn_window", "sfi_select_window", "sfi_step_control", "sfi_kv_append"]
+           "sfi_slow_attn_window", "sfi_select_window", "sfi_step_control", "sfi_kv_append",
+           "sfi_decode_attn_ws", "sfi_decode_attn"]
 
 
 class SfiShape(ctypes.Structure):
@@ -74,9 +75,12 @@ _SIGS = {
                                             _P, _I64, _P, _P, _SZ, _P]),
     "sfi_select_window": (ctypes.c_int, [_SHP, _PRM, _I32, _P, _I64, _P, _P, _I64, _P, _P, _I32,
                                          _I32, _P, _P, _P, _SZ, _P]),
-    "sfi_step_control": (ctypes.c_int, [_SHP, _PRM, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P,
+    "sfi_step_control": (ctypes.c_int, [_SHP, _PRM, _I32, _P, _P, _I32, _P, _P, _P, _P, _P,
                                         _P]),
     "sfi_kv_append": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I64, _P]),
+    "sfi_decode_attn_ws": (_SZ, [_SHP, _I32, _I32, _I32, _I32, _I32]),
+    "sfi_decode_attn": (ctypes.c_int, [_SHP, _I32, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
+                                       _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _SZ, _P]),
     "sfi_fast_attn": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32,
                                      _I32, _P, _P, _P, _SZ, _P]),
 }
@@ -247,12 +251,11 @@ def sfi_fast_attn(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache,
 
 
 def sfi_step_control(shape, params, refresh_budget, token_ids, boundary_tokens, n_boundary,
-                     seq_lens, since_slow, recent_start, slow_ids, fast_ids, counts,
-                     stream=None) -> None:
+                     state_in, state_out, slow_ids, fast_ids, counts, stream=None) -> None:
     rc = load().sfi_step_control(ctypes.byref(shape), ctypes.byref(params), refresh_budget,
                                  _ptr(token_ids), _ptr(boundary_tokens), n_boundary,
-                                 _ptr(seq_lens), _ptr(since_slow), _ptr(recent_start),
-                                 _ptr(slow_ids), _ptr(fast_ids), _ptr(counts), _stream(stream))
+                                 _ptr(state_in), _ptr(state_out), _ptr(slow_ids),
+                                 _ptr(fast_ids), _ptr(counts), _stream(stream))
     _check("sfi_step_control", rc)
 
 
@@ -262,3 +265,23 @@ def sfi_kv_append(shape, k_new, v_new, k_cache, v_cache, block_table, seq_lens, 
                               _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(seq_ids),
                               n_seqs, _ptr(key_norm), norm_stride, _stream(stream))
     _check("sfi_kv_append", rc)
+
+
+def sfi_decode_attn_ws(shape, window, n_seqs, packed_cap, max_recent, max_seq_len) -> int:
+    return load().sfi_decode_attn_ws(ctypes.byref(shape), window, n_seqs, packed_cap, max_recent,
+                                     max_seq_len)
+
+
+def sfi_decode_attn(shape, window, q, q_win, packed_k, packed_v, packed_len, packed_cap, k_cache,
+                    v_cache, block_table, recent_start, seq_lens, fast_ids, slow_ids, n_seqs,
+                    max_recent, max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes=None,
+                    stream=None) -> None:
+    ws_bytes = ws.numel() if ws_bytes is None else ws_bytes
+    rc = load().sfi_decode_attn(ctypes.byref(shape), window, _ptr(q), _ptr(q_win),
+                                _ptr(packed_k), _ptr(packed_v), _ptr(packed_len), packed_cap,
+                                _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                _ptr(recent_start), _ptr(seq_lens), _ptr(fast_ids),
+                                _ptr(slow_ids), n_seqs, max_recent, max_seq_len, _ptr(out),
+                                _ptr(logits), logits_stride, _ptr(lse), _ptr(ws), ws_bytes,
+                                _stream(stream))
+    _check("sfi_decode_attn", rc)

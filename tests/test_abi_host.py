@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert sorted(L.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert L.sfi_abi_version() == 3
+    assert L.sfi_abi_version() == 4
 
 
 def test_status_strings():
@@ -280,7 +280,7 @@ def test_step_control_and_append_validation():
 
     def ctrl(budget=4, tok=FAKE, bnd=FAKE, nb=5, sl=FAKE, outs=FAKE, shape=s, params=p):
         return lib.sfi_step_control(ctypes.byref(shape), ctypes.byref(params), budget, tok, bnd,
-                                    nb, sl, FAKE, FAKE, outs, FAKE, FAKE, None)
+                                    nb, sl, FAKE, outs, FAKE, FAKE, None)
 
     assert ctrl(budget=-1) == L.SFI_E_ARG
     assert ctrl(nb=-1) == L.SFI_E_ARG
