@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SFI_ABI_VERSION 4
+#define SFI_ABI_VERSION 5
 
 enum sfi_status {
   SFI_OK = 0,
@@ -265,7 +265,10 @@ int sfi_decode_attn(const sfi_shape* shape, int32_t window, const float* q,
  *                     || token_ids[b] is one of boundary_tokens[0..n_boundary)
  *                     || since_slow >= refresh_budget
  *   since_slow      = slow ? 0 : since_slow + 1
- *   recent_start    = slow ? max(n_sink, seq_lens - n_recent) : recent_start
+ *   recent_start    = (slow || sliding_recent) ? max(n_sink, seq_lens - n_recent)
+ *                                              : recent_start
+ *                     (frozen at the slow step, or with sliding_recent = 1 the newest
+ *                     n_recent positions at every step)
  * slow_ids / fast_ids [batch] receive the slow and the fast rows in ascending order, each
  * padded with -1; counts [2] = {slow rows, fast rows}.  n_sink and n_recent come from
  * params.  Initial state: seq_lens = stored length before the first step, since_slow = -1.
@@ -273,11 +276,12 @@ int sfi_decode_attn(const sfi_shape* shape, int32_t window, const float* q,
  * state_out (rows 0 and 2) and the lists; work of the previous step still running on
  * another stream reads the previous buffers, so a caller that overlaps steps alternates
  * two state buffers and two pairs of lists.
- * Requires refresh_budget >= 0 and 0 <= n_boundary <= 1024 (SFI_E_UNSUPPORTED beyond).
+ * Requires refresh_budget >= 0, sliding_recent in {0, 1} and 0 <= n_boundary <= 1024
+ * (SFI_E_UNSUPPORTED beyond).
  * One workgroup; rows are independent.
  */
 int sfi_step_control(const sfi_shape* shape, const sfi_select_params* params,
-                     int32_t refresh_budget, const int32_t* token_ids,
+                     int32_t refresh_budget, int32_t sliding_recent, const int32_t* token_ids,
                      const int32_t* boundary_tokens, int32_t n_boundary,
                      const int32_t* state_in, int32_t* state_out, int32_t* slow_ids,
                      int32_t* fast_ids, int32_t* counts, void* stream);

@@ -27,6 +27,8 @@ Parity status of each function:
       of the two factors is a reading the pages do not fix -- parity unpinned for the form.
   refine: special cases pinned (identity at α=0, local maxima at α_soft=1, ownership at
       α_cross=1); intermediate α -- parity unpinned beyond those cases.
+  refine_greedy (an alternative reading, host only): pinned by a worked example, a plain
+      quadratic simulation, its reductions (α_soft = 0 or R = 0) and hard NMS at α_soft = 1.
 """
 from __future__ import annotations
 
@@ -117,12 +119,13 @@ def boundary_flags(tokens: np.ndarray, boundary_tokens) -> np.ndarray:
 
 
 def step_control(tokens: np.ndarray, boundary_tokens, budget: int, n_stored: int,
-                 n_sink: int, n_recent: int) -> Dict[str, np.ndarray]:
+                 n_sink: int, n_recent: int, sliding: bool = False) -> Dict[str, np.ndarray]:
     """The per-step state of a trajectory driven by decoded tokens, tokens [B, S].
 
     Before step 0 every row stores n_stored positions; step s decodes token [b, s], which
     joins the history, so N_s = n_stored + s + 1.  The mode is `schedule` of the tokens'
-    boundary flags; a slow step freezes the recent segment's left edge (recent_start_at).
+    boundary flags; a slow step freezes the recent segment's left edge (recent_start_at),
+    or, with sliding, the edge follows every step (recent_start_sliding).
     Returns mode [S, B], seq_len [S, B], recent_start [S, B] (the edge in force at the
     step), slow / fast row lists [S, B] in ascending order padded with -1, and the counts
     [S, 2]."""
@@ -138,7 +141,9 @@ def step_control(tokens: np.ndarray, boundary_tokens, budget: int, n_stored: int
         for b in range(B):
             N = n_stored + s + 1
             seq_len[s, b] = N
-            if mode[s, b]:
+            if sliding:
+                edge[b] = recent_start_sliding(N, n_sink, n_recent)
+            elif mode[s, b]:
                 edge[b] = recent_start_at(N, n_sink, n_recent)
             rstart[s, b] = edge[b]
         sl = [b for b in range(B) if mode[s, b]]
@@ -292,6 +297,46 @@ def refine(s: np.ndarray, lo: int, hi: int, R: int, alpha_soft: float,
     return Refined(ellp, dom, exc, dom_margin, own_margin)
 
 
+def refine_greedy(s: np.ndarray, lo: int, hi: int, R: int, alpha_soft: float,
+                  alpha_cross: float) -> np.ndarray:
+    """Classic greedy Soft-NMS as an alternative reading of the refinement's soft-NMS
+    (zh "2.2 Log-Score 细化": penalise high-scoring neighbours within a head).
+
+    Exclusivity is that of `refine` (owner = the smallest g with the largest unrefined s;
+    other heads' scores times 1 - α_cross).  Then, per head, the candidates are taken one
+    at a time: the one with the largest current score (the lower position on ties) keeps
+    that score for good, and every not yet taken candidate within ±R has its current score
+    multiplied by 1 - α_soft.  A score is thus penalised once for every neighbour taken
+    before it, where the one-pass reading penalises it once if any neighbour is larger to
+    begin with.  Scores taken are non-increasing, so the first K taken are the Top-K.
+    Returns the final scores [Hkv, |C|] (product form; take the log for `topk`)."""
+    import heapq
+    s = np.asarray(s, F64)
+    Hkv = s.shape[0]
+    sc = s[:, lo:hi]
+    n = sc.shape[1]
+    own = np.argmax(sc, axis=0) if n else np.zeros(0, int)
+    exc = (np.arange(Hkv)[:, None] != own[None, :]) & (Hkv > 1)
+    cur = sc * np.where(exc, 1.0 - alpha_cross, 1.0)
+    final = np.zeros((Hkv, n), F64)
+    for g in range(Hkv):
+        val = cur[g].copy()
+        taken = np.zeros(n, bool)
+        heap = [(-val[c], c) for c in range(n)]
+        heapq.heapify(heap)
+        while heap:
+            negv, c = heapq.heappop(heap)
+            if taken[c] or -negv != val[c]:
+                continue  # taken already, or an entry from before a penalty
+            taken[c] = True
+            final[g, c] = val[c]
+            for d in range(max(0, c - R), min(n, c + R + 1)):
+                if not taken[d]:
+                    val[d] *= 1.0 - alpha_soft
+                    heapq.heappush(heap, (-val[d], d))
+    return final
+
+
 def topk(ellp: np.ndarray, lo: int, K: int) -> np.ndarray:
     """Top-K discretisation (zh "2.2 Top-K 选择").
 
@@ -349,6 +394,15 @@ def select_from_evidence(f: np.ndarray, norms: np.ndarray, N: int, n_sink: int,
     ref = refine(s, lo, hi, R, alpha_soft, alpha_cross)
     sel = topk(ref.ellp, lo, top_k)
     return Selection(sel, f, r, s, ref, lo, hi)
+
+
+def select_greedy_from_scores(s: np.ndarray, N: int, n_sink: int, n_recent: int, top_k: int,
+                              R: int, alpha_soft: float, alpha_cross: float) -> np.ndarray:
+    """Top-K after the greedy Soft-NMS reading (refine_greedy) of given fused scores."""
+    lo, hi = candidates(N, n_sink, n_recent)
+    final = refine_greedy(np.asarray(s, F64)[:, :N], lo, hi, R, alpha_soft, alpha_cross)
+    with np.errstate(divide="ignore"):
+        return topk(np.log(final), lo, top_k)
 
 
 def select_from_scores(s: np.ndarray, N: int, n_sink: int, n_recent: int, top_k: int,
@@ -430,6 +484,14 @@ def recent_start_at(N_slow: int, n_sink: int, n_recent: int) -> int:
     return max(n_sink, N_slow - n_recent)
 
 
+def recent_start_sliding(N: int, n_sink: int, n_recent: int) -> int:
+    """Left edge of a purely sliding recent segment at KV length N: always the newest W
+    positions (the literal reading of the sliding window, es "Pasos Rápidos", nl
+    "Methodologie").  After a slow step at N0 the positions [N0 - W, N - W) then belong to
+    no segment of the fast memory until the next slow step."""
+    return max(n_sink, N - n_recent)
+
+
 # --------------------------------------------------------------------------- trajectory
 @dataclass
 class StepRecord:
@@ -445,8 +507,8 @@ class StepRecord:
 def run_sequence(q: np.ndarray, K: np.ndarray, V: np.ndarray, flags_row: np.ndarray,
                  context: int, n_sink: int, n_recent: int, top_k: int, R: int,
                  alpha_soft: float, alpha_cross: float, lam: float, budget: int,
-                 steps: Optional[int] = None, sel_override: Optional[Dict[int, np.ndarray]] = None
-                 ) -> List[StepRecord]:
+                 steps: Optional[int] = None, sel_override: Optional[Dict[int, np.ndarray]] = None,
+                 sliding: bool = False) -> List[StepRecord]:
     """Decode trajectory of one sequence in one layer.
 
     q [S, Hq, D]; K, V [Hkv, context + S, D] stored values; flags_row [S].
@@ -472,6 +534,8 @@ def run_sequence(q: np.ndarray, K: np.ndarray, V: np.ndarray, flags_row: np.ndar
             rstart = recent_start_at(N, n_sink, n_recent)
             recs.append(StepRecord(s, 1, N, o, lse, sel, rstart))
         else:
+            if sliding:
+                rstart = recent_start_sliding(N, n_sink, n_recent)
             o, lse = fast_attention(q[s], K, V, packed, rstart, N)
             recs.append(StepRecord(s, 0, N, o, lse, None, rstart))
     return recs

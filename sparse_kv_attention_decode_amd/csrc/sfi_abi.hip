@@ -297,7 +297,7 @@ int sfi_pack(const sfi_shape* shape, const sfi_select_params* params, const void
 }
 
 int sfi_step_control(const sfi_shape* shape, const sfi_select_params* params,
-                     int32_t refresh_budget, const int32_t* token_ids,
+                     int32_t refresh_budget, int32_t sliding_recent, const int32_t* token_ids,
                      const int32_t* boundary_tokens, int32_t n_boundary,
                      const int32_t* state_in, int32_t* state_out, int32_t* slow_ids,
                      int32_t* fast_ids, int32_t* counts, void* stream) {
@@ -305,12 +305,14 @@ int sfi_step_control(const sfi_shape* shape, const sfi_select_params* params,
   if (rc) return rc;
   if ((rc = check_params(params))) return rc;
   if (refresh_budget < 0 || n_boundary < 0) return SFI_E_ARG;
+  if (sliding_recent != 0 && sliding_recent != 1) return SFI_E_ARG;
   if (n_boundary > sfi::kMaxBoundaryTokens) return SFI_E_UNSUPPORTED;
   if (!token_ids || (n_boundary > 0 && !boundary_tokens) || !state_in || !state_out ||
       !slow_ids || !fast_ids || !counts)
     return SFI_E_ARG;
   return finish(sfi::launch_step_control(shape->batch, token_ids, boundary_tokens, n_boundary,
-                                         refresh_budget, params->n_sink, params->n_recent,
+                                         refresh_budget, sliding_recent, params->n_sink,
+                                         params->n_recent,
                                          state_in, state_out, slow_ids, fast_ids, counts,
                                          reinterpret_cast<hipStream_t>(stream)));
 }

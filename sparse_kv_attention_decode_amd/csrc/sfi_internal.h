@@ -87,7 +87,7 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm,
                          int32_t* sel_idx, float* dbg_scores, void* ws, hipStream_t stream);
 
 hipError_t launch_step_control(int batch, const int32_t* tokens, const int32_t* boundary,
-                               int n_boundary, int budget, int n_sink, int n_recent,
+                               int n_boundary, int budget, int sliding, int n_sink, int n_recent,
                                const int32_t* state_in, int32_t* state_out, int32_t* slow_ids,
                                int32_t* fast_ids, int32_t* counts, hipStream_t stream);
 // Longest boundary-token table sfi_step_control takes.

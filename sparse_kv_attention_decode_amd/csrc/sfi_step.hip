@@ -23,7 +23,7 @@ struct CtrlArgs {
   int32_t* slow_ids;         // [batch] out
   int32_t* fast_ids;         // [batch] out
   int32_t* counts;           // [2] out
-  int batch, n_boundary, budget, n_sink, n_recent;
+  int batch, n_boundary, budget, sliding, n_sink, n_recent;
 };
 
 // One block.  Thread t decides row c0 + t of each chunk of 256 rows; the two row lists are
@@ -47,8 +47,8 @@ __global__ __launch_bounds__(kCtrlThreads) void k_step_control(CtrlArgs a) {
       slow = since < 0 || boundary || since >= a.budget;
       a.state_out[b] = N;
       a.state_out[B + b] = slow ? 0 : since + 1;
-      // The recent segment's left edge is frozen at the slow step.
-      a.state_out[2 * B + b] = slow ? max(a.n_sink, N - a.n_recent) : rs;
+      // The recent segment's left edge is frozen at the slow step, or slides every step.
+      a.state_out[2 * B + b] = (slow || a.sliding) ? max(a.n_sink, N - a.n_recent) : rs;
     }
     uint32_t tot_s, tot_f;
     const uint32_t ps = block_exscan<kCtrlThreads>(live && slow ? 1u : 0u, wsum, &tot_s);
@@ -144,7 +144,7 @@ hipError_t append_t(const sfi_shape& s, const void* k_new, const void* v_new, vo
 }  // namespace
 
 hipError_t launch_step_control(int batch, const int32_t* tokens, const int32_t* boundary,
-                               int n_boundary, int budget, int n_sink, int n_recent,
+                               int n_boundary, int budget, int sliding, int n_sink, int n_recent,
                                const int32_t* state_in, int32_t* state_out, int32_t* slow_ids,
                                int32_t* fast_ids, int32_t* counts, hipStream_t stream) {
   CtrlArgs a;
@@ -158,6 +158,7 @@ hipError_t launch_step_control(int batch, const int32_t* tokens, const int32_t* 
   a.batch = batch;
   a.n_boundary = n_boundary;
   a.budget = budget;
+  a.sliding = sliding;
   a.n_sink = n_sink;
   a.n_recent = n_recent;
   hipLaunchKernelGGL(k_step_control, dim3(1), dim3(kCtrlThreads), 0, stream, a);

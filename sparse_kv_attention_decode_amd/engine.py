@@ -65,7 +65,9 @@ class Plan:
 
 
 def make_plan(flags: np.ndarray, context: int, budget: int, n_sink: int, n_recent: int,
-              top_k: int = 0) -> Plan:
+              top_k: int = 0, sliding: bool = False) -> Plan:
+    """Host tables of a trajectory.  The recent segment's left edge is frozen at each slow
+    step at max(n_sink, N0 - W), or with `sliding` follows every step at max(n_sink, N - W)."""
     mode = schedule(flags, budget)
     B, S = mode.shape
     seq_len = np.zeros((S, B), np.int32)
@@ -83,6 +85,8 @@ def make_plan(flags: np.ndarray, context: int, budget: int, n_sink: int, n_recen
                 cur[b] = max(n_sink, N - n_recent)
                 cur_k[b] = min(top_k, max(0, N - n_recent - n_sink))
             else:
+                if sliding:
+                    cur[b] = max(n_sink, N - n_recent)
                 max_recent = max(max_recent, N - int(cur[b]))
             rstart[s, b] = cur[b]
             keff[s, b] = cur_k[b]
@@ -99,7 +103,7 @@ kGraphMinLayers = 8
 
 def recent_bound(w) -> int:
     """Upper bound of N - recent_start over every fast step of any schedule (see Engine)."""
-    return w.n_recent + w.refresh_budget
+    return w.n_recent if w.sliding_recent else w.n_recent + w.refresh_budget
 
 
 def window_query_table(q_all: torch.Tensor, num_kv_heads: int, window: int) -> torch.Tensor:
@@ -162,7 +166,7 @@ class Engine:
         self.two_streams = two_streams
         flags_np = np.asarray(flags.cpu() if torch.is_tensor(flags) else flags)
         self.plan = make_plan(flags_np, w.context, w.refresh_budget, w.n_sink, w.n_recent,
-                              w.top_k)
+                              w.top_k, sliding=w.sliding_recent)
         self.shape = L.make_shape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                   w.pages_per_seq, w.dtype)
         self.params = L.make_params(w.n_sink, w.n_recent, w.top_k, w.nms_radius, w.lam,
@@ -283,7 +287,8 @@ class Engine:
         self.state_bufs = [self.state0.clone(), self.state0.clone()]
         self.ws_decode = L.workspace(L.sfi_decode_attn_ws(
             self.shape, self.window, B, self.packed_cap, self.max_recent, self.max_len), dev)
-        self.lists = torch.full((2, 2, B), -1, dtype=torch.int32, device=dev)  # [parity][slow, fast]
+        # row lists [parity][slow, fast][B]
+        self.lists = torch.full((2, 2, B), -1, dtype=torch.int32, device=dev)
         self.counts = torch.zeros(2, 2, dtype=torch.int32, device=dev)
 
     def _take_new_rows(self, lb: LayerBuffers):
@@ -319,7 +324,8 @@ class Engine:
         ws_dec, ws_dec_n = self._ws["decode"]
         win = self.window
         ok("sfi_step_control", lib.sfi_step_control(
-            shp, prm, w.refresh_budget, self._dc_tok + s * B * 4, self._dc_bnd,
+            shp, prm, w.refresh_budget, int(w.sliding_recent), self._dc_tok + s * B * 4,
+            self._dc_bnd,
             self.n_boundary, st_in, dc["state"], slow_p, fast_p, dc["cnt"], h1))
         for li, lb in enumerate(self.layers):
             P = lb.ptr

@@ -75,8 +75,8 @@ _SIGS = {
                                             _P, _I64, _P, _P, _SZ, _P]),
     "sfi_select_window": (ctypes.c_int, [_SHP, _PRM, _I32, _P, _I64, _P, _P, _I64, _P, _P, _I32,
                                          _I32, _P, _P, _P, _SZ, _P]),
-    "sfi_step_control": (ctypes.c_int, [_SHP, _PRM, _I32, _P, _P, _I32, _P, _P, _P, _P, _P,
-                                        _P]),
+    "sfi_step_control": (ctypes.c_int, [_SHP, _PRM, _I32, _I32, _P, _P, _I32, _P, _P, _P, _P,
+                                        _P, _P]),
     "sfi_kv_append": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I64, _P]),
     "sfi_decode_attn_ws": (_SZ, [_SHP, _I32, _I32, _I32, _I32, _I32]),
     "sfi_decode_attn": (ctypes.c_int, [_SHP, _I32, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
@@ -251,9 +251,10 @@ def sfi_fast_attn(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache,
 
 
 def sfi_step_control(shape, params, refresh_budget, token_ids, boundary_tokens, n_boundary,
-                     state_in, state_out, slow_ids, fast_ids, counts, stream=None) -> None:
+                     state_in, state_out, slow_ids, fast_ids, counts, sliding_recent=0,
+                     stream=None) -> None:
     rc = load().sfi_step_control(ctypes.byref(shape), ctypes.byref(params), refresh_budget,
-                                 _ptr(token_ids), _ptr(boundary_tokens), n_boundary,
+                                 int(sliding_recent), _ptr(token_ids), _ptr(boundary_tokens), n_boundary,
                                  _ptr(state_in), _ptr(state_out), _ptr(slow_ids),
                                  _ptr(fast_ids), _ptr(counts), _stream(stream))
     _check("sfi_step_control", rc)

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert sorted(L.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert L.sfi_abi_version() == 4
+    assert L.sfi_abi_version() == 5
 
 
 def test_status_strings():
@@ -278,11 +278,13 @@ def test_step_control_and_append_validation():
     s, p = _shape(), _params()
     lib = L.load()
 
-    def ctrl(budget=4, tok=FAKE, bnd=FAKE, nb=5, sl=FAKE, outs=FAKE, shape=s, params=p):
-        return lib.sfi_step_control(ctypes.byref(shape), ctypes.byref(params), budget, tok, bnd,
-                                    nb, sl, FAKE, outs, FAKE, FAKE, None)
+    def ctrl(budget=4, tok=FAKE, bnd=FAKE, nb=5, sl=FAKE, outs=FAKE, shape=s, params=p,
+             slide=0):
+        return lib.sfi_step_control(ctypes.byref(shape), ctypes.byref(params), budget, slide,
+                                    tok, bnd, nb, sl, FAKE, outs, FAKE, FAKE, None)
 
     assert ctrl(budget=-1) == L.SFI_E_ARG
+    assert ctrl(slide=2) == L.SFI_E_ARG
     assert ctrl(nb=-1) == L.SFI_E_ARG
     assert ctrl(nb=1025) == L.SFI_E_UNSUPPORTED
     assert ctrl(tok=None) == L.SFI_E_ARG
@@ -303,3 +305,21 @@ def test_step_control_and_append_validation():
     assert app(norm=FAKE, stride=0) == L.SFI_E_ARG
     assert app(shape=_shape(head_dim=96)) == L.SFI_E_UNSUPPORTED
     assert app(n=0) == L.SFI_OK                    # nothing to launch
+
+
+def test_coverage_helpers():
+    """memory_mask marks sink, packed rows and the recent segment; coverage_of sums the
+    softmax mass over them (uniform logits: |M| / N per head)."""
+    from sparse_kv_attention_decode_amd.coverage import coverage_of, memory_mask
+    N, n_sink = 20, 2
+    pos = torch.tensor([[0, 1, 5, 9, -1], [0, 1, 7, -1, -1]], dtype=torch.int32)
+    plen = torch.tensor([4, 3], dtype=torch.int32)
+    m = memory_mask(N, n_sink, pos, plen, 16)
+    want0 = {0, 1, 5, 9, 16, 17, 18, 19}
+    want1 = {0, 1, 7, 16, 17, 18, 19}
+    assert set(torch.nonzero(m[0]).flatten().tolist()) == want0
+    assert set(torch.nonzero(m[1]).flatten().tolist()) == want1
+    z = torch.zeros(4, N, dtype=torch.float64)     # G = 2
+    lse = torch.full((4,), float(np.log(N)), dtype=torch.float64)
+    c = coverage_of(z, lse, m)
+    np.testing.assert_allclose(c.numpy(), [8 / N, 8 / N, 7 / N, 7 / N], rtol=1e-12)

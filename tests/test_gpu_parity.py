@@ -155,15 +155,17 @@ def test_pack_bit_exact(name):
             assert bool((_bits(pk[g, n:]) == 0).all()) and bool((_bits(pv[g, n:]) == 0).all())
 
 
-@pytest.mark.parametrize("name,win", [(n, 1) for n in SMALL] +
-                         [("tiny_fp32_1k", 3), ("qwen3_0p6b_8k", 4)])
-def test_trajectory_lockstep(name, win):
+@pytest.mark.parametrize("name,win,sliding", [(n, 1, False) for n in SMALL] +
+                         [("tiny_fp32_1k", 3, False), ("qwen3_0p6b_8k", 4, False),
+                          ("qwen3_0p6b_8k", 1, True)])
+def test_trajectory_lockstep(name, win, sliding):
     """Every step of the seeded trajectory through the two-stream engine.  Slow steps:
     dense output and the selection (near-tie rule); the oracle then continues with the
     device's selection (teacher forcing) so the two cannot drift.  Fast steps: the
     two-segment output against the oracle's fast step on the same memory.  win > 1 pools
-    the Selector's evidence over that many decode queries."""
-    w = get(name).replace(evidence_window=win)
+    the Selector's evidence over that many decode queries; sliding moves the recent
+    segment to the newest W positions at every step."""
+    w = get(name).replace(evidence_window=win, sliding_recent=sliding)
     d, eng, lb = _setup(w)
     B = w.batch
     host = [oracle_layer_arrays(d, b) for b in range(B)]
@@ -202,9 +204,11 @@ def test_trajectory_lockstep(name, win):
                 rstart[b] = O.recent_start_at(N, w.n_sink, w.n_recent)
             else:
                 n_fast += 1
+                if sliding:
+                    rstart[b] = O.recent_start_sliding(N, w.n_sink, w.n_recent)
                 o, lse = O.fast_attention(q[s], K, V, packed[b], rstart[b], N)
                 worst = max(worst, check_out(out[b], o, f"fast s={s} b={b}"))
-    print(f"{name} window {win}: {n_slow} slow / {n_fast} fast steps, "
+    print(f"{name} window {win} sliding {sliding}: {n_slow} slow / {n_fast} fast steps, "
           f"worst row rel err {worst:.2e}")
 
 

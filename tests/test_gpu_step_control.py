@@ -24,8 +24,9 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
 
 
-@pytest.mark.parametrize("batch,steps,budget", [(1, 40, 3), (5, 64, 4), (600, 12, 2)])
-def test_step_control_matches_oracle(batch, steps, budget):
+@pytest.mark.parametrize("batch,steps,budget,sliding", [(1, 40, 3, False), (5, 64, 4, False),
+                                                       (600, 12, 2, False), (5, 64, 4, True)])
+def test_step_control_matches_oracle(batch, steps, budget, sliding):
     """Every output of every step, bit-exact, against the oracle's step control.  600 rows
     span three chunks of the control kernel's workgroup."""
     rng = np.random.default_rng(batch * 1000 + steps)
@@ -45,11 +46,12 @@ def test_step_control_matches_oracle(batch, steps, budget):
     slow = torch.empty(batch, dtype=torch.int32, device=dev)
     fast = torch.empty(batch, dtype=torch.int32, device=dev)
     cnt = torch.empty(2, dtype=torch.int32, device=dev)
-    ref = O.step_control(tokens, BOUNDARY_TOKENS, budget, n_stored, n_sink, n_recent)
+    ref = O.step_control(tokens, BOUNDARY_TOKENS, budget, n_stored, n_sink, n_recent,
+                         sliding=sliding)
     for s in range(steps):
         out = state if s % 3 == 0 else other
         L.sfi_step_control(shape, params, budget, tok_d[s], bnd, len(BOUNDARY_TOKENS), state,
-                           out, slow, fast, cnt)
+                           out, slow, fast, cnt, sliding_recent=sliding)
         torch.cuda.synchronize()
         state, other = out, (other if out is state else state)
         np.testing.assert_array_equal(state[0].cpu().numpy(), ref["seq_len"][s], f"step {s}")
@@ -76,14 +78,16 @@ def _engines(w, layers, graphs=False):
     return data, host, devc
 
 
-@pytest.mark.parametrize("name,batch,layers,graphs",
-                         [("tiny_fp32_1k", 1, 1, False), ("qwen3_0p6b_8k", 3, 1, False),
-                          ("qwen3_0p6b_8k", 3, 2, True)])
-def test_device_trajectory_bit_identical_to_host(name, batch, layers, graphs):
+@pytest.mark.parametrize("name,batch,layers,graphs,sliding",
+                         [("tiny_fp32_1k", 1, 1, False, False),
+                          ("qwen3_0p6b_8k", 3, 1, False, False),
+                          ("qwen3_0p6b_8k", 3, 2, True, False),
+                          ("qwen3_0p6b_8k", 3, 1, False, True)])
+def test_device_trajectory_bit_identical_to_host(name, batch, layers, graphs, sliding):
     """The whole trajectory decided on the device (tokens -> modes, K/V appended step by
     step) against the host schedule: outputs after every step, then the selections, the
     packed buffers, the re-filled caches and the key norms, all bit for bit."""
-    w = get(name).replace(batch=batch, name=f"{name}_b{batch}")
+    w = get(name).replace(batch=batch, name=f"{name}_b{batch}", sliding_recent=sliding)
     data, host, devc = _engines(w, layers, graphs)
     for s in range(w.steps):
         host.step(s)
@@ -108,7 +112,8 @@ def test_device_trajectory_bit_identical_to_host(name, batch, layers, graphs):
                     .all())
     # the device's own state at the end
     ref = O.step_control(gen_tokens(w, data[0]["flags"]).numpy().T, BOUNDARY_TOKENS,
-                         w.refresh_budget, w.context - 1, w.n_sink, w.n_recent)
+                         w.refresh_budget, w.context - 1, w.n_sink, w.n_recent,
+                         sliding=sliding)
     st = devc.device_state(w.steps - 1)
     np.testing.assert_array_equal(st[0].cpu().numpy(), ref["seq_len"][-1])
     np.testing.assert_array_equal(st[2].cpu().numpy(), ref["recent_start"][-1])

@@ -155,10 +155,42 @@ def test_step_control_worked_example():
                                                    [0, -1], [0, 1]])
     np.testing.assert_array_equal(st["counts"], [[2, 0], [1, 1], [0, 2], [1, 1], [1, 1],
                                                  [0, 2]])
+    # a purely sliding window follows every step: max(1, N - 4)
+    sl = O.step_control(tok, (B,), budget=2, n_stored=10, n_sink=1, n_recent=4, sliding=True)
+    np.testing.assert_array_equal(sl["recent_start"].T, [[7, 8, 9, 10, 11, 12]] * 2)
+    np.testing.assert_array_equal(sl["mode"], st["mode"])
     # budget 0: every step is slow; no boundary and a long budget: only the first step
     assert O.step_control(tok, (B,), 0, 10, 1, 4)["mode"].all()
     m = O.step_control(tok, (), 100, 10, 1, 4)["mode"]
     assert m[0].all() and not m[1:].any()
+
+
+def test_sliding_fast_step_attends_to_sink_selection_and_newest_window():
+    """With a purely sliding window a fast step attends to exactly the sink, the slow step's
+    selection and the newest W positions: a softmax over that set written out by hand."""
+    r = np.random.default_rng(21)
+    Hq, Hkv, D, ctx, S = 4, 2, 8, 60, 7
+    n_sink, W, K = 2, 6, 5
+    q = r.standard_normal((S, Hq, D))
+    Kc = r.standard_normal((Hkv, ctx + S, D))
+    Vc = r.standard_normal((Hkv, ctx + S, D))
+    flags = np.zeros(S, np.uint8)
+    recs = O.run_sequence(q, Kc, Vc, flags, ctx, n_sink, W, K, 1, 0.5, 0.5, 0.3, budget=100,
+                          sliding=True)
+    sel = recs[0].selection.sel
+    G = Hq // Hkv
+    for rec in recs[1:]:
+        N = rec.N
+        assert rec.recent_start == N - W
+        for h in range(Hq):
+            g = h // G
+            keep = sorted(set(range(n_sink)) | set(int(j) for j in sel[g] if j >= 0)
+                          | set(range(N - W, N)))
+            z = np.array([q[rec.step, h] @ Kc[g, j] / math.sqrt(D) for j in keep])
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            o = sum(p[i] * Vc[g, j] for i, j in enumerate(keep))
+            np.testing.assert_allclose(rec.o[h], o, rtol=1e-12, atol=1e-12)
 
 
 # ------------------------------------------------------------------------------ Selector
@@ -232,6 +264,72 @@ def test_window_selector_keeps_what_each_slot_attends_to():
     same = np.stack([P[0]] * 2)
     np.testing.assert_array_equal(O.select_window(same, norms, **kw).sel,
                                   O.select(P[0], norms, **kw).sel)
+
+
+def test_refine_greedy_worked_example():
+    """One head, R = 1, α_soft = 0.5, scores 0.1 0.5 0.4 0.45 0.05, by hand.  Greedy: take
+    1 (0.5), halving 0 and 2 to 0.05 and 0.2; take 3 (0.45), halving 2 to 0.1 and 4 to
+    0.025; then 2, 0, 4.  The one-pass reading halves only the initially dominated 0, 2, 4:
+    position 2 ends at 0.2 instead of 0.1."""
+    s = np.array([[0.1, 0.5, 0.4, 0.45, 0.05]])
+    np.testing.assert_allclose(O.refine_greedy(s, 0, 5, 1, 0.5, 0.0),
+                               [[0.05, 0.5, 0.1, 0.45, 0.025]], rtol=1e-15)
+    np.testing.assert_allclose(np.exp(O.refine(s, 0, 5, 1, 0.5, 0.0).ellp),
+                               [[0.05, 0.5, 0.2, 0.45, 0.025]], rtol=1e-15)
+
+
+def _greedy_quadratic(cur, R, a):
+    """The greedy taken one argmax at a time over a plain list (no heap)."""
+    val = list(cur)
+    n = len(val)
+    taken = [False] * n
+    final = [0.0] * n
+    for _ in range(n):
+        best = None
+        for c in range(n):
+            if not taken[c] and (best is None or val[c] > val[best]):
+                best = c
+        taken[best] = True
+        final[best] = val[best]
+        for d in range(max(0, best - R), min(n, best + R + 1)):
+            if not taken[d]:
+                val[d] *= 1.0 - a
+    return final
+
+
+def test_refine_greedy_matches_quadratic_simulation_and_reductions():
+    r = np.random.default_rng(31)
+    for trial in range(20):
+        Hkv, n, R = 3, 40, int(r.integers(0, 5))
+        a_s, a_c = float(r.choice([0.0, 0.3, 0.5, 1.0])), float(r.choice([0.0, 0.5, 1.0]))
+        s = r.random((Hkv, n + 6))
+        if trial % 4 == 0:
+            s = np.round(s * 4) / 4 + 0.01           # many exact ties
+        lo, hi = 2, n + 2
+        got = O.refine_greedy(s, lo, hi, R, a_s, a_c)
+        own = np.argmax(s[:, lo:hi], axis=0)
+        for g in range(Hkv):
+            cur = s[g, lo:hi] * np.where(own != g, 1.0 - a_c, 1.0)
+            np.testing.assert_allclose(got[g], _greedy_quadratic(cur, R, a_s), rtol=0, atol=0)
+        # no penalty or no neighbours: only exclusivity is left, as in the one-pass reading
+        base = np.exp(O.refine(s, lo, hi, R, 0.0, a_c).ellp)
+        np.testing.assert_allclose(O.refine_greedy(s, lo, hi, R, 0.0, a_c), base, rtol=1e-15)
+        np.testing.assert_allclose(O.refine_greedy(s, lo, hi, 0, a_s, a_c),
+                                   np.exp(O.refine(s, lo, hi, 0, a_s, a_c).ellp), rtol=1e-15)
+
+
+def test_refine_greedy_hard_nms_at_alpha_one():
+    """α_soft = 1 is hard NMS: the kept positions are at least R + 1 apart, the first is the
+    global maximum, and every dropped position has a kept neighbour within R."""
+    r = np.random.default_rng(32)
+    s = r.random((1, 200))
+    R = 3
+    fin = O.refine_greedy(s, 0, 200, R, 1.0, 0.0)[0]
+    kept = np.nonzero(fin > 0)[0]
+    assert np.all(np.diff(kept) > R)
+    assert int(np.argmax(s[0])) in kept
+    for j in np.nonzero(fin == 0)[0]:
+        assert np.any(np.abs(kept - j) <= R)
 
 
 def test_key_norms_library():

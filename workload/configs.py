@@ -41,6 +41,7 @@ class Workload:
     lam: float
     page_size: int = 16
     evidence_window: int = 1  # decode queries whose attention the Selector pools
+    sliding_recent: bool = False  # recent segment = newest W positions at every step
 
     @property
     def group(self) -> int:
