@@ -52,6 +52,9 @@ def _parse():
     ap.add_argument("--evidence-window", type=int, default=None,
                     help="decode queries pooled into the Selector's evidence at a slow step "
                          "(default: the workload's, 1)")
+    ap.add_argument("--full-pack", action="store_true",
+                    help="re-pack every selected row at each slow step (sfi_pack) instead of "
+                         "copying only the newly selected ones (sfi_pack_update)")
     ap.add_argument("--device-control", action="store_true",
                     help="decide slow/fast and append K/V on the device every step (token "
                          "ids in, no host schedule); every step is replayed from a graph "
@@ -153,9 +156,11 @@ def main():
                 from workload.gen import BOUNDARY_TOKENS, gen_tokens
                 eng = Engine(w, d["flags"], two_streams=not args.one_stream,
                              device_control=True, tokens=gen_tokens(w, d["flags"]),
-                             boundary_tokens=BOUNDARY_TOKENS)
+                             boundary_tokens=BOUNDARY_TOKENS,
+                             incremental_pack=not args.full_pack)
             else:
-                eng = Engine(w, d["flags"], two_streams=not args.one_stream)
+                eng = Engine(w, d["flags"], two_streams=not args.one_stream,
+                             incremental_pack=not args.full_pack)
         eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
         if keep:
             d0 = {k: d[k] for k in ("q", "K", "V", "flags")}
@@ -281,7 +286,8 @@ def main():
                    "streams": 1 if args.one_stream else 2,
                    "fast_step_graph": eng.graph is not None,
                    "evidence_window": w.evidence_window,
-                   "device_control": bool(args.device_control)},
+                   "device_control": bool(args.device_control),
+                   "pack": "full" if args.full_pack else "incremental"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {

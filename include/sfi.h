@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SFI_ABI_VERSION 5
+#define SFI_ABI_VERSION 6
 
 enum sfi_status {
   SFI_OK = 0,
@@ -218,6 +218,34 @@ int sfi_pack(const sfi_shape* shape, const sfi_select_params* params, const void
              const void* v_cache, const int32_t* block_table, const int32_t* sel_idx,
              const int32_t* seq_ids, int32_t n_seqs, void* packed_k, void* packed_v,
              int32_t* packed_pos, int32_t* packed_len, int32_t packed_cap, void* stream);
+
+/*
+ * sfi_pack_update -- sfi_pack for a buffer that already holds the previous selection: rows
+ * whose position stays selected keep their slot and are not copied again; newly selected
+ * rows are copied into the slots of dropped ones, then past the old end (K_eff grows with
+ * N).  The slow steps of one sentence select nearly the same support (the pages' within-
+ * sentence stability, nl "Kernobservatie", zh "1 问题背景"), so an update copies a few
+ * rows where a full pack copies all of them.
+ * After the call rows [0, packed_len[b][g]) of packed_k/v hold exactly the sink rows and the
+ * selected rows, each a byte copy of the cache row at packed_pos; the ORDER of the selected
+ * rows is unspecified (fast attention does not depend on it).  When a buffer is empty
+ * (packed_len 0) or the selection is smaller than what it holds, it is rebuilt in
+ * sfi_pack's order.
+ *   slot_map  i32 [batch, Hkv, map_stride]: the slot of each position, or -1.  The caller
+ *             fills it with -1, packed_pos with -1 and packed_len with 0 once; afterwards
+ *             only these calls may change slot_map, packed_pos and the packed rows.  Setting
+ *             packed_len[b][g] to 0 empties a buffer (a new sequence): the next call
+ *             rebuilds it.  map_stride >= every N_b (device contract) and >= n_sink.
+ * ws: sfi_pack_update_ws(shape, params, n_seqs) bytes (no initialisation).
+ */
+size_t sfi_pack_update_ws(const sfi_shape* shape, const sfi_select_params* params,
+                          int32_t n_seqs);
+int sfi_pack_update(const sfi_shape* shape, const sfi_select_params* params,
+                    const void* k_cache, const void* v_cache, const int32_t* block_table,
+                    const int32_t* sel_idx, const int32_t* seq_ids, int32_t n_seqs,
+                    void* packed_k, void* packed_v, int32_t* packed_pos, int32_t* packed_len,
+                    int32_t packed_cap, int32_t* slot_map, int64_t map_stride, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /*
  * sfi_fast_attn -- two-segment attention of a fast step (zh "2.3 两段式"): segment A is

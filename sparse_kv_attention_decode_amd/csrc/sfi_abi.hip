@@ -276,6 +276,39 @@ int sfi_select_window(const sfi_shape* shape, const sfi_select_params* params, i
                     seq_ids, n_seqs, max_seq_len, sel_idx, dbg_scores, ws, ws_bytes, stream);
 }
 
+size_t sfi_pack_update_ws(const sfi_shape* shape, const sfi_select_params* params,
+                          int32_t n_seqs) {
+  if (check_shape(shape) != SFI_OK || check_params(params) != SFI_OK) return 0;
+  if (n_seqs < 0 || n_seqs > shape->batch) return 0;
+  return sfi::pack_update_ws(*shape, *params, n_seqs);
+}
+
+int sfi_pack_update(const sfi_shape* shape, const sfi_select_params* params,
+                    const void* k_cache, const void* v_cache, const int32_t* block_table,
+                    const int32_t* sel_idx, const int32_t* seq_ids, int32_t n_seqs,
+                    void* packed_k, void* packed_v, int32_t* packed_pos, int32_t* packed_len,
+                    int32_t packed_cap, int32_t* slot_map, int64_t map_stride, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_params(params))) return rc;
+  if (!k_cache || !v_cache || !block_table || !sel_idx || !seq_ids || !packed_k || !packed_v ||
+      !packed_pos || !packed_len || !slot_map)
+    return SFI_E_ARG;
+  if (n_seqs < 0 || n_seqs > shape->batch) return SFI_E_ARG;
+  if (packed_cap != packed_cap_of(params)) return SFI_E_CAPACITY;
+  if (map_stride < params->n_sink || map_stride < 1) return SFI_E_CAPACITY;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(packed_k) || !aligned16(packed_v))
+    return SFI_E_ALIGN;
+  const size_t need = sfi_pack_update_ws(shape, params, n_seqs);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SFI_E_WORKSPACE;
+  if (n_seqs == 0) return SFI_OK;
+  return finish(sfi::launch_pack_update(*shape, *params, k_cache, v_cache, block_table, sel_idx,
+                                        seq_ids, n_seqs, packed_k, packed_v, packed_pos,
+                                        packed_len, packed_cap, slot_map, map_stride, ws,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
 int sfi_pack(const sfi_shape* shape, const sfi_select_params* params, const void* k_cache,
              const void* v_cache, const int32_t* block_table, const int32_t* sel_idx,
              const int32_t* seq_ids, int32_t n_seqs, void* packed_k, void* packed_v,

@@ -98,6 +98,16 @@ hipError_t launch_kv_append(const sfi_shape& s, const void* k_new, const void* v
                             const int32_t* seq_lens, const int32_t* seq_ids, int n_seqs,
                             float* key_norm, int64_t norm_stride, hipStream_t stream);
 
+// Workspace of the incremental pack and its launch (both kernels).
+size_t pack_update_ws(const sfi_shape& s, const sfi_select_params& prm, int n_seqs);
+hipError_t launch_pack_update(const sfi_shape& s, const sfi_select_params& prm,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* sel_idx,
+                              const int32_t* seq_ids, int n_seqs, void* packed_k, void* packed_v,
+                              int32_t* packed_pos, int32_t* packed_len, int packed_cap,
+                              int32_t* slot_map, int64_t map_stride, void* ws,
+                              hipStream_t stream);
+
 hipError_t launch_pack(const sfi_shape& s, const sfi_select_params& prm, const void* k_cache,
                        const void* v_cache, const int32_t* block_table, const int32_t* sel_idx,
                        const int32_t* seq_ids, int n_seqs, void* packed_k, void* packed_v,

@@ -101,7 +101,382 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack(PackArgs a) {
   }
 }
 
+// ----------------------------------------------------------------- incremental update
+// The fast step's softmax does not depend on the order of the packed rows, so the packed
+// buffer can be kept as a set: an update keeps every row whose position stays selected in
+// its slot and copies only the newly selected rows, into the slots of the dropped ones (and,
+// as K_eff grows with N, past the old end).  slot_map[b][g][j] holds the slot of position j
+// (or -1), so membership is one load.
+//
+// Each (listed row, KV head) "ig" has two lists: its selection (K entries) and its slots
+// (n_sink + K).  Both are cut into chunks of kChunk entries, one workgroup per chunk, so the
+// scattered map accesses of one ig spread over many CUs.  Four kernels, each needing the
+// previous one complete:
+//   1. mark     held positions that stay selected get kKeepBit in the map;
+//   2. count    slot chunks free the held rows not marked (and clear the marks), sel chunks
+//               flag the selected positions not held; per-chunk counts of both and of the
+//               valid selection entries;
+//   3. free     slot chunks write their free slots at (earlier chunks' count + in-chunk
+//               prefix), so the free list is in slot order;
+//   4. assign   sel chunks give the j-th new position the j-th free slot (past the old end
+//               once the freed slots are used up), record it, and copy its K/V rows.
+// Chunk prefixes are sums over at most a few dozen per-chunk counts, so every assignment is
+// deterministic.  An empty buffer (packed_len 0) or a selection smaller than the rows held
+// is rebuilt in sfi_pack's order by kernels 3 and 4.
+
+constexpr int kChunk = 1024;           // list entries per workgroup
+constexpr int kChunkThreads = 256;     // four consecutive entries per thread
+constexpr int32_t kKeepBit = 1 << 30;  // marks a held position that stays selected
+
+struct UpdArgs {
+  const int32_t* sel;
+  const int32_t* seq_ids;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const int32_t* bt;
+  uint8_t* pk;
+  uint8_t* pv;
+  int32_t* ppos;
+  int32_t* plen;
+  int32_t* map;
+  int64_t map_stride;  // >= every N and >= n_sink
+  int32_t* cnt_free;   // [n_ig][nc_slot]
+  int32_t* cnt_add;    // [n_ig][nc_sel]
+  int32_t* cnt_valid;  // [n_ig][nc_sel]
+  int32_t* free_slot;  // [n_ig][K]
+  int Hkv, K, n_sink, cap, nc_sel, nc_slot, max_pages, row_bytes;
+};
+
+struct Ig {
+  int ig, chunk, b, g;
+  size_t bg;
+};
+
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();  // red may still be read by an earlier call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < kChunkThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+// Workgroup x of a grid of n_ig * nc chunks; b < 0 for an unused slot of the row list.
+__device__ __forceinline__ Ig ig_of(const UpdArgs& a, int x, int nc) {
+  Ig r;
+  r.ig = x / nc;
+  r.chunk = x % nc;
+  r.g = r.ig % a.Hkv;
+  r.b = a.seq_ids[r.ig / a.Hkv];
+  r.bg = (size_t)(r.b < 0 ? 0 : r.b) * a.Hkv + r.g;
+  return r;
+}
+
+// The held length as these kernels maintain it (clamped, so that a corrupted value cannot
+// send the loops out of the lists).
+__device__ __forceinline__ int held_len(const UpdArgs& a, size_t bg) {
+  return min(max(a.plen[bg], 0), a.n_sink + a.K);
+}
+
+__device__ __forceinline__ bool in_map(const UpdArgs& a, int p) {
+  return p >= 0 && p < a.map_stride;
+}
+
+// Kernel 1: mark.
+__global__ __launch_bounds__(kChunkThreads) void k_upd_mark(UpdArgs a) {
+  const Ig r = ig_of(a, blockIdx.x, a.nc_sel);
+  if (r.b < 0) return;
+  const int32_t* sel = a.sel + r.bg * a.K;
+  int32_t* map = a.map + r.bg * a.map_stride;
+  const int k0 = r.chunk * kChunk + 4 * (int)threadIdx.x;
+  int q[4], v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = k0 + i < a.K ? sel[k0 + i] : -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = in_map(a, q[i]) ? map[q[i]] : -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (v[i] >= 0) map[q[i]] = v[i] | kKeepBit;
+}
+
+// Kernel 2: count.  Workgroups [0, n_ig * nc_slot) take slot chunks, the rest sel chunks.
+__global__ __launch_bounds__(kChunkThreads) void k_upd_count(UpdArgs a, int n_ig) {
+  __shared__ uint32_t red[kChunkThreads / 64];
+  const bool slots = (int)blockIdx.x < n_ig * a.nc_slot;
+  const int x = slots ? (int)blockIdx.x : (int)blockIdx.x - n_ig * a.nc_slot;
+  const Ig r = ig_of(a, x, slots ? a.nc_slot : a.nc_sel);
+  if (r.b < 0) return;
+  int32_t* map = a.map + r.bg * a.map_stride;
+  const int k0 = r.chunk * kChunk + 4 * (int)threadIdx.x;
+  uint32_t c1 = 0, c2 = 0;
+  int q[4], v[4];
+  if (slots) {
+    const int plen = held_len(a, r.bg);
+    const int32_t* ppos = a.ppos + r.bg * a.cap;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sl = k0 + i;
+      q[i] = (sl >= a.n_sink && sl < plen) ? ppos[sl] : -2;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = in_map(a, q[i]) ? map[q[i]] : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (q[i] == -2) continue;
+      if (v[i] & kKeepBit) {
+        map[q[i]] = v[i] & ~kKeepBit;
+      } else {
+        if (in_map(a, q[i])) map[q[i]] = -1;
+        ++c1;
+      }
+    }
+  } else {
+    const int32_t* sel = a.sel + r.bg * a.K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = k0 + i < a.K ? sel[k0 + i] : -1;
+    // A position not held reads -1 whatever the slot chunks do: they write held positions
+    // only, and the held positions that are not selected any more are not in this list.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = in_map(a, q[i]) ? map[q[i]] : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c1 += (q[i] >= 0 && v[i] < 0) ? 1u : 0u;  // selected, not held
+      c2 += q[i] >= 0 ? 1u : 0u;                // valid entry
+    }
+  }
+  const uint32_t t1 = block_sum_u32(c1, red), t2 = block_sum_u32(c2, red);
+  if (threadIdx.x == 0) {
+    if (slots) {
+      a.cnt_free[(size_t)r.ig * a.nc_slot + r.chunk] = (int32_t)t1;
+    } else {
+      a.cnt_add[(size_t)r.ig * a.nc_sel + r.chunk] = (int32_t)t1;
+      a.cnt_valid[(size_t)r.ig * a.nc_sel + r.chunk] = (int32_t)t2;
+    }
+  }
+}
+
+// Sums of one ig's chunk counts: before chunk `upto` and in all.
+struct Pref {
+  int before, total;
+};
+__device__ __forceinline__ Pref chunk_prefix(const int32_t* cnt, int nc, int upto) {
+  Pref p{0, 0};
+  for (int c = 0; c < nc; ++c) {
+    const int v = cnt[c];
+    p.before += c < upto ? v : 0;
+    p.total += v;
+  }
+  return p;
+}
+
+__device__ __forceinline__ bool rebuild_of(int plen_old, int n_sink, int keff) {
+  const int nsel_old = plen_old > n_sink ? plen_old - n_sink : 0;
+  return plen_old == 0 || keff < nsel_old;
+}
+
+// Kernel 3: the free list (slot chunks).  For a rebuilt ig: drop every listed position
+// from the map and clear the slots past the new length.
+__global__ __launch_bounds__(kChunkThreads) void k_upd_free(UpdArgs a) {
+  __shared__ uint32_t wsum[kChunkThreads / 64 + 1];
+  __shared__ int sh[3];
+  const Ig r = ig_of(a, blockIdx.x, a.nc_slot);
+  if (r.b < 0) return;
+  if (threadIdx.x == 0) {
+    const Pref f = chunk_prefix(a.cnt_free + (size_t)r.ig * a.nc_slot, a.nc_slot, r.chunk);
+    const Pref v = chunk_prefix(a.cnt_valid + (size_t)r.ig * a.nc_sel, a.nc_sel, 0);
+    sh[0] = f.before;
+    sh[1] = v.total;  // K_eff
+    sh[2] = held_len(a, r.bg);
+  }
+  __syncthreads();
+  const int keff = sh[1], plen = sh[2];
+  int32_t* ppos = a.ppos + r.bg * a.cap;
+  int32_t* map = a.map + r.bg * a.map_stride;
+  const int k0 = r.chunk * kChunk + 4 * (int)threadIdx.x;
+  int q[4];
+  if (rebuild_of(plen, a.n_sink, keff)) {
+    const int n = a.n_sink + keff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = (k0 + i >= a.n_sink && k0 + i < a.cap) ? ppos[k0 + i] : -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (in_map(a, q[i])) map[q[i]] = -1;
+      if (k0 + i >= n && k0 + i < a.cap) ppos[k0 + i] = -1;
+    }
+    return;
+  }
+  // free slots of this chunk: the held rows whose position is no longer in the map
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sl = k0 + i;
+    q[i] = (sl >= a.n_sink && sl < plen) ? ppos[sl] : -2;
+  }
+  uint32_t fmask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (q[i] == -2) continue;
+    if (!in_map(a, q[i]) || map[q[i]] < 0) fmask |= 1u << i;
+  }
+  uint32_t tot;
+  uint32_t j = (uint32_t)sh[0] +
+               block_exscan<kChunkThreads>(__builtin_popcount(fmask), wsum, &tot);
+  int32_t* fslot = a.free_slot + (size_t)r.ig * a.K;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (fmask & (1u << i)) fslot[j++] = k0 + i;
+}
+
+// Kernel 4: assign and copy (sel chunks).  LPR lanes copy one row (16 bytes each).
+template <int LPR>
+__global__ __launch_bounds__(kChunkThreads) void k_upd_assign(UpdArgs a) {
+  __shared__ uint32_t wsum[kChunkThreads / 64 + 1];
+  __shared__ int sh[5];
+  __shared__ int l_pos[kChunk];
+  __shared__ int l_slot[kChunk];
+  const Ig r = ig_of(a, blockIdx.x, a.nc_sel);
+  if (r.b < 0) return;
+  if (threadIdx.x == 0) {
+    const Pref ad = chunk_prefix(a.cnt_add + (size_t)r.ig * a.nc_sel, a.nc_sel, r.chunk);
+    const Pref fr = chunk_prefix(a.cnt_free + (size_t)r.ig * a.nc_slot, a.nc_slot, a.nc_slot);
+    const Pref v = chunk_prefix(a.cnt_valid + (size_t)r.ig * a.nc_sel, a.nc_sel, 0);
+    sh[0] = ad.before;
+    sh[1] = ad.total;
+    sh[2] = fr.total;
+    sh[3] = v.total;  // K_eff
+    sh[4] = held_len(a, r.bg);
+  }
+  __syncthreads();
+  const int keff = sh[3], plen = sh[4];
+  const bool rebuild = rebuild_of(plen, a.n_sink, keff);
+  const int32_t* sel = a.sel + r.bg * a.K;
+  int32_t* ppos = a.ppos + r.bg * a.cap;
+  int32_t* map = a.map + r.bg * a.map_stride;
+  const int k0 = r.chunk * kChunk + 4 * (int)threadIdx.x;
+  int q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = k0 + i < keff ? sel[k0 + i] : -1;
+  uint32_t amask = 0;
+  if (rebuild) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (q[i] >= 0) amask |= 1u << i;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (q[i] >= 0 && (!in_map(a, q[i]) || map[q[i]] < 0)) amask |= 1u << i;
+  }
+  uint32_t tot;
+  const uint32_t first = block_exscan<kChunkThreads>(__builtin_popcount(amask), wsum, &tot);
+  uint32_t j = (uint32_t)sh[0] + first;  // rank among the ig's new positions
+  uint32_t li = first;                   // rank within this chunk
+  const int32_t* fslot = a.free_slot + (size_t)r.ig * a.K;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (amask & (1u << i)) {
+      int slot;
+      if (rebuild)
+        slot = a.n_sink + k0 + i;  // the full pack's order
+      else
+        slot = j < (uint32_t)sh[2] ? fslot[j] : plen + (int)(j - (uint32_t)sh[2]);
+      ppos[slot] = q[i];
+      if (in_map(a, q[i])) map[q[i]] = slot;
+      l_pos[li] = q[i];
+      l_slot[li] = slot;
+      ++j;
+      ++li;
+    }
+  }
+  if (threadIdx.x == 0 && r.chunk == 0) a.plen[r.bg] = a.n_sink + keff;
+  __syncthreads();
+  // copy the rows listed in LDS (and, for a rebuild, the sink rows in chunk 0): LPR lanes
+  // per row, 16 bytes per lane
+  constexpr int RPB = kChunkThreads / LPR;
+  const int sub = threadIdx.x % LPR, rsub = threadIdx.x / LPR;
+  const size_t rb = (size_t)a.row_bytes;
+  const int32_t* btb = a.bt + (size_t)r.b * a.max_pages;
+  const int n_sink_copy = (rebuild && r.chunk == 0) ? a.n_sink : 0;
+  const int nl = (int)tot + n_sink_copy;
+  for (int e = rsub; e < nl; e += RPB) {
+    const bool sink = e >= (int)tot;
+    const int pos = sink ? e - (int)tot : l_pos[e];
+    const int slot = sink ? pos : l_slot[e];
+    if (sink && sub == 0) {
+      ppos[pos] = pos;
+      if (in_map(a, pos)) map[pos] = pos;
+    }
+    const int page = btb[pos / kPage];
+    const size_t src = (((size_t)page * a.Hkv + r.g) * kPage + pos % kPage) * rb + 16 * sub;
+    const size_t dst = (r.bg * a.cap + slot) * rb + 16 * sub;
+    const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(a.kc + src);
+    const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(a.vc + src);
+    *reinterpret_cast<u32x4_t*>(a.pk + dst) = kv;
+    *reinterpret_cast<u32x4_t*>(a.pv + dst) = vv;
+  }
+}
+
 }  // namespace
+
+static int ceil_div(int x, int y) { return (x + y - 1) / y; }
+
+size_t pack_update_ws(const sfi_shape& s, const sfi_select_params& prm, int n_seqs) {
+  const size_t n_ig = (size_t)n_seqs * s.num_kv_heads;
+  const size_t nc_sel = ceil_div(prm.top_k, kChunk);
+  const size_t nc_slot = ceil_div(prm.n_sink + prm.top_k + 15, kChunk);  // >= packed_cap
+  auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  return r256(n_ig * nc_slot * 4) + 2 * r256(n_ig * nc_sel * 4) +
+         r256(n_ig * (size_t)prm.top_k * 4);
+}
+
+hipError_t launch_pack_update(const sfi_shape& s, const sfi_select_params& prm,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* sel_idx,
+                              const int32_t* seq_ids, int n_seqs, void* packed_k, void* packed_v,
+                              int32_t* packed_pos, int32_t* packed_len, int packed_cap,
+                              int32_t* slot_map, int64_t map_stride, void* ws,
+                              hipStream_t stream) {
+  const int n_ig = n_seqs * s.num_kv_heads;
+  UpdArgs a;
+  a.nc_sel = ceil_div(prm.top_k, kChunk);
+  a.nc_slot = ceil_div(packed_cap, kChunk);
+  auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* w = reinterpret_cast<char*>(ws);
+  a.cnt_free = reinterpret_cast<int32_t*>(w);
+  w += r256((size_t)n_ig * a.nc_slot * 4);
+  a.cnt_add = reinterpret_cast<int32_t*>(w);
+  w += r256((size_t)n_ig * a.nc_sel * 4);
+  a.cnt_valid = reinterpret_cast<int32_t*>(w);
+  w += r256((size_t)n_ig * a.nc_sel * 4);
+  a.free_slot = reinterpret_cast<int32_t*>(w);
+  a.sel = sel_idx;
+  a.seq_ids = seq_ids;
+  a.kc = reinterpret_cast<const uint8_t*>(k_cache);
+  a.vc = reinterpret_cast<const uint8_t*>(v_cache);
+  a.bt = block_table;
+  a.pk = reinterpret_cast<uint8_t*>(packed_k);
+  a.pv = reinterpret_cast<uint8_t*>(packed_v);
+  a.ppos = packed_pos;
+  a.plen = packed_len;
+  a.map = slot_map;
+  a.map_stride = map_stride;
+  a.Hkv = s.num_kv_heads;
+  a.K = prm.top_k;
+  a.n_sink = prm.n_sink;
+  a.cap = packed_cap;
+  a.max_pages = s.max_pages_per_seq;
+  a.row_bytes = s.head_dim * (s.dtype == SFI_BF16 ? 2 : 4);
+  const dim3 blk(kChunkThreads);
+  hipLaunchKernelGGL(k_upd_mark, dim3(n_ig * a.nc_sel), blk, 0, stream, a);
+  hipLaunchKernelGGL(k_upd_count, dim3(n_ig * (a.nc_slot + a.nc_sel)), blk, 0, stream, a, n_ig);
+  hipLaunchKernelGGL(k_upd_free, dim3(n_ig * a.nc_slot), blk, 0, stream, a);
+  const dim3 g_sel(n_ig * a.nc_sel);
+  switch (a.row_bytes / 16) {
+    case 8: hipLaunchKernelGGL(k_upd_assign<8>, g_sel, blk, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(k_upd_assign<16>, g_sel, blk, 0, stream, a); break;
+    default: hipLaunchKernelGGL(k_upd_assign<32>, g_sel, blk, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const sfi_shape& s, const sfi_select_params& prm, const void* k_cache,
                        const void* v_cache, const int32_t* block_table, const int32_t* sel_idx,

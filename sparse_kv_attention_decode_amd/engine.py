@@ -146,6 +146,9 @@ class LayerBuffers:
         self.ev_pack = torch.cuda.Event()
         self.pack_pending = False
         self.k_new = self.v_new = None           # [S, B, Hkv, D] (device-controlled steps)
+        # slot of every position in the packed buffers, for the incremental pack
+        self.slot_map = (torch.full((B, Hkv, eng.stride), -1, dtype=torch.int32, device=dev)
+                         if eng.incremental_pack else None)
 
 
 class Engine:
@@ -153,13 +156,16 @@ class Engine:
                  dbg_scores: bool = False, sel_streams: int = 2,
                  window: Optional[int] = None, device_control: bool = False,
                  tokens=None, boundary_tokens=None, max_recent: Optional[int] = None,
-                 full_lists: bool = False):
+                 full_lists: bool = False, incremental_pack: bool = True):
         self.w = w
         self.device = torch.device(device)
         self.device_control = device_control
         # full_lists: every call of a host-scheduled step gets all B slots of its row list
         # (-1 padded), the launch shape of device-controlled steps.
         self.full_lists = full_lists
+        # incremental_pack: a slow step copies only the newly selected rows into the packed
+        # buffers (sfi_pack_update) instead of all of them (sfi_pack)
+        self.incremental_pack = incremental_pack
         # Decode queries pooled into the Selector's evidence at a slow step (1: the current
         # query only).
         self.window = int(w.evidence_window if window is None else window)
@@ -215,6 +221,8 @@ class Engine:
         if sel_ws == 0:
             raise ValueError(f"evidence window {win} is not supported for this shape "
                              f"(window >= 1 and group * window <= 16)")
+        if incremental_pack:
+            sel_ws = max(sel_ws, L.sfi_pack_update_ws(self.shape, self.params, B))
         self.ws_sels = [L.workspace(sel_ws, dev) for _ in range(n_sel)]
         self.ws_sel = self.ws_sels[0]
         self.stream1 = torch.cuda.Stream(device=dev)
@@ -351,17 +359,15 @@ class Engine:
             ok("sfi_select_window", lib.sfi_select_window(
                 shp, prm, win, P["z"], self.stride, P["lse"], P["norm"], self.stride, sl_p,
                 slow_p, B, self.max_len, P["sel"], self._dbg_p, ws_sel, ws_sel_n, h2))
-            ok("sfi_pack", lib.sfi_pack(
-                shp, prm, P["k"], P["v"], P["bt"], P["sel"], slow_p, B, P["pk"], P["pv"],
-                P["pp"], P["pl"], self.packed_cap, h2))
+            self._pack(P, slow_p, B, ws_sel, ws_sel_n, h2)
             if s2 is not s1:
                 lb.ev_pack.record(s2)
                 lb.pack_pending = True
 
     def _device_step(self, s: int, timer: Optional[list]) -> None:
         if s == 0:
-            # a new trajectory: the last step of the previous one may use buffer 0 too
-            self.join()
+            # a new trajectory (the last step of the previous one may use state buffer 0)
+            self._new_sequences()
         s1 = self.stream1
         e0 = e1 = None
         if timer is not None:
@@ -449,6 +455,7 @@ class Engine:
                 ("norm", "key_norm"), ("z", "logits"), ("lse", "lse"), ("sel", "sel_idx"),
                 ("pk", "packed_k"), ("pv", "packed_v"), ("pp", "packed_pos"),
                 ("pl", "packed_len"), ("out", "out"))}
+            lb.ptr["map"] = lb.slot_map.data_ptr() if lb.slot_map is not None else None
             lb.q_step = lb.q_all[0].numel() * lb.q_all.element_size()
             if lb.k_new is not None:
                 lb.ptr["kn"], lb.ptr["vn"] = lb.k_new.data_ptr(), lb.v_new.data_ptr()
@@ -508,6 +515,26 @@ class Engine:
         self.graph = self.graphs or None
         torch.cuda.synchronize()
 
+    def _pack(self, P, ids, n, ws, ws_n, h) -> None:
+        """Pack of one layer: the incremental update, or the full pack."""
+        if self.incremental_pack:
+            self._ok("sfi_pack_update", self._lib.sfi_pack_update(
+                self._shp, self._prm, P["k"], P["v"], P["bt"], P["sel"], ids, n, P["pk"],
+                P["pv"], P["pp"], P["pl"], self.packed_cap, P["map"], self.stride, ws, ws_n, h))
+        else:
+            self._ok("sfi_pack", self._lib.sfi_pack(
+                self._shp, self._prm, P["k"], P["v"], P["bt"], P["sel"], ids, n, P["pk"],
+                P["pv"], P["pp"], P["pl"], self.packed_cap, h))
+
+    def _new_sequences(self) -> None:
+        """Step 0 starts every row afresh: empty the packed buffers (on stream 1), so that the
+        trajectory's results do not depend on what an earlier run left in them."""
+        self.join()
+        if self.incremental_pack:
+            with torch.cuda.stream(self.stream1):
+                for lb in self.layers:
+                    lb.packed_len.zero_()
+
     @staticmethod
     def _ok(name: str, rc: int) -> None:
         if rc != L.SFI_OK:
@@ -528,6 +555,8 @@ class Engine:
         if self.device_control and not dense_only:
             self._device_step(s, timer)
             return
+        if s == 0 and not dense_only:
+            self._new_sequences()
         # The graph waits for every layer's pending pack before its first call, so the
         # first fast step after a slow step is issued call by call: its layer i then waits
         # only for layer i's pack and overlaps the Selector work still queued on stream 2.
@@ -602,9 +631,7 @@ class Engine:
                     shp, prm, win, P["z"], self.stride, P["lse"], P["norm"], self.stride, seq_len,
                     slow_ids, m_slow, self.max_len, P["sel"], self._dbg_p, ws_sel, ws_sel_n,
                     h2))
-                ok("sfi_pack", lib.sfi_pack(
-                    shp, prm, P["k"], P["v"], P["bt"], P["sel"], slow_ids, m_slow, P["pk"],
-                    P["pv"], P["pp"], P["pl"], self.packed_cap, h2))
+                self._pack(P, slow_ids, m_slow, ws_sel, ws_sel_n, h2)
                 if s2 is not s1:
                     lb.ev_pack.record(s2)
                     lb.pack_pending = True

@@ -24,7 +24,7 @@ EXPORTS = ["sfi_abi_version", "sfi_status_str", "sfi_slow_attn_ws", "sfi_fast_at
            "sfi_select_ws", "sfi_packed_cap", "sfi_key_norms", "sfi_slow_attn", "sfi_select",
            "sfi_pack", "sfi_fast_attn", "sfi_slow_attn_window_ws", "sfi_select_window_ws",
            "sfi_slow_attn_window", "sfi_select_window", "sfi_step_control", "sfi_kv_append",
-           "sfi_decode_attn_ws", "sfi_decode_attn"]
+           "sfi_decode_attn_ws", "sfi_decode_attn", "sfi_pack_update_ws", "sfi_pack_update"]
 
 
 class SfiShape(ctypes.Structure):
@@ -81,6 +81,9 @@ _SIGS = {
     "sfi_decode_attn_ws": (_SZ, [_SHP, _I32, _I32, _I32, _I32, _I32]),
     "sfi_decode_attn": (ctypes.c_int, [_SHP, _I32, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                        _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "sfi_pack_update_ws": (_SZ, [_SHP, _PRM, _I32]),
+    "sfi_pack_update": (ctypes.c_int, [_SHP, _PRM, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32,
+                                       _P, _I64, _P, _SZ, _P]),
     "sfi_fast_attn": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32,
                                      _I32, _P, _P, _P, _SZ, _P]),
 }
@@ -286,3 +289,19 @@ def sfi_decode_attn(shape, window, q, q_win, packed_k, packed_v, packed_len, pac
                                 _ptr(logits), logits_stride, _ptr(lse), _ptr(ws), ws_bytes,
                                 _stream(stream))
     _check("sfi_decode_attn", rc)
+
+
+def sfi_pack_update_ws(shape, params, n_seqs) -> int:
+    return load().sfi_pack_update_ws(ctypes.byref(shape), ctypes.byref(params), n_seqs)
+
+
+def sfi_pack_update(shape, params, k_cache, v_cache, block_table, sel_idx, seq_ids, n_seqs,
+                    packed_k, packed_v, packed_pos, packed_len, packed_cap, slot_map, map_stride,
+                    ws, ws_bytes=None, stream=None) -> None:
+    ws_bytes = ws.numel() if ws_bytes is None else ws_bytes
+    rc = load().sfi_pack_update(ctypes.byref(shape), ctypes.byref(params), _ptr(k_cache),
+                                _ptr(v_cache), _ptr(block_table), _ptr(sel_idx), _ptr(seq_ids),
+                                n_seqs, _ptr(packed_k), _ptr(packed_v), _ptr(packed_pos),
+                                _ptr(packed_len), packed_cap, _ptr(slot_map), map_stride,
+                                _ptr(ws), ws_bytes, _stream(stream))
+    _check("sfi_pack_update", rc)

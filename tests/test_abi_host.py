@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert sorted(L.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert L.sfi_abi_version() == 5
+    assert L.sfi_abi_version() == 6
 
 
 def test_status_strings():

@@ -566,3 +566,92 @@ def test_topk_ties_across_slices(levels):
     assert len(np.unique(s[0, 4:N - 64])) == levels
     ref = O.select_from_scores(s, N, 4, 64, K, 4, 0.0, 0.0)
     np.testing.assert_array_equal(sel[0], ref)
+
+
+# ------------------------------------------------------------------ incremental pack
+def _check_pack_state(w, lb, d, b, want_pos, N, ordered=False):
+    """Rows [0, packed_len) hold exactly sink + want_pos, each the stored row of its slot's
+    position; slot_map is the inverse of packed_pos and -1 elsewhere."""
+    Hkv = w.num_kv_heads
+    ppos = lb.packed_pos[b].cpu().numpy()
+    plen = lb.packed_len[b].cpu().numpy()
+    smap = lb.slot_map[b, :, :N].cpu().numpy()
+    for g in range(Hkv):
+        want = O.packed_positions(np.asarray(want_pos[g]), w.n_sink)
+        n = len(want)
+        assert plen[g] == n
+        held = ppos[g, :n]
+        if ordered:
+            np.testing.assert_array_equal(held, want)
+        assert sorted(held.tolist()) == sorted(want.tolist())
+        assert (ppos[g, n:] == -1).all()
+        idx = torch.from_numpy(held.astype(np.int64)).cuda()
+        assert torch.equal(_bits(lb.packed_k[b, g, :n]), _bits(d["K"][b, g, idx]))
+        assert torch.equal(_bits(lb.packed_v[b, g, :n]), _bits(d["V"][b, g, idx]))
+        inv = np.full(N, -1)
+        inv[held] = np.arange(n)
+        np.testing.assert_array_equal(smap[g], inv)
+
+
+def test_pack_update_keeps_held_rows_and_adds_new_ones():
+    """A run of selections through sfi_pack_update: growing K_eff with 0-100% turnover, a
+    shrink (rebuilt in sfi_pack's order), an emptied buffer, and a row the list skips."""
+    w = get("qwen3_0p6b_8k").replace(batch=2, top_k=300, name="pack_update")
+    d, eng, lb = _setup(w)
+    dev = "cuda"
+    N = w.context
+    lo, hi = O.candidates(N, w.n_sink, w.n_recent)
+    rng = np.random.default_rng(5)
+    ws = L.workspace(L.sfi_pack_update_ws(eng.shape, eng.params, w.batch), dev)
+    ids = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+    cur = [[np.sort(rng.choice(np.arange(lo, hi), 200, replace=False)) for _ in range(8)]
+           for _ in range(2)]
+
+    def apply(sets, ids, n):
+        sel = torch.full((w.batch, w.num_kv_heads, w.top_k), -1, dtype=torch.int32)
+        for b in range(w.batch):
+            for g in range(w.num_kv_heads):
+                sel[b, g, :len(sets[b][g])] = torch.from_numpy(sets[b][g].astype(np.int32))
+        lb.sel_idx.copy_(sel.to(dev))
+        L.sfi_pack_update(eng.shape, eng.params, lb.k_cache, lb.v_cache, lb.block_table,
+                          lb.sel_idx, ids, n, lb.packed_k, lb.packed_v, lb.packed_pos,
+                          lb.packed_len, eng.packed_cap, lb.slot_map, eng.stride, ws)
+        torch.cuda.synchronize()
+
+    # first call: an empty buffer is built in the full pack's order
+    apply(cur, ids, 2)
+    for b in range(2):
+        _check_pack_state(w, lb, d, b, cur[b], N, ordered=True)
+    for turnover, grow in ((0.0, 0), (0.05, 10), (0.5, 20), (1.0, 30), (0.2, 0)):
+        new = []
+        for b in range(2):
+            rows = []
+            for g in range(8):
+                keep_n = int(round(len(cur[b][g]) * (1 - turnover)))
+                keep = rng.choice(cur[b][g], keep_n, replace=False)
+                pool = np.setdiff1d(np.arange(lo, hi), keep)
+                add = rng.choice(pool, len(cur[b][g]) + grow - keep_n, replace=False)
+                rows.append(np.sort(np.concatenate([keep, add])))
+            new.append(rows)
+        apply(new, ids, 2)
+        cur = new
+        for b in range(2):
+            _check_pack_state(w, lb, d, b, cur[b], N)
+    # row 1 only (row 0's slot skipped with -1): row 0 keeps its state
+    before = lb.packed_pos[0].clone()
+    new = [cur[0], [np.sort(np.concatenate([c[:-3], [hi - 1]])) if hi - 1 not in c else c
+                    for c in cur[1]]]
+    apply(new, torch.tensor([-1, 1], dtype=torch.int32, device=dev), 2)
+    assert torch.equal(before, lb.packed_pos[0])
+    _check_pack_state(w, lb, d, 1, new[1], N)
+    cur = new
+    # a smaller selection is rebuilt in order
+    small = [[c[:50] for c in cur[b]] for b in range(2)]
+    apply(small, ids, 2)
+    for b in range(2):
+        _check_pack_state(w, lb, d, b, small[b], N, ordered=True)
+    # an emptied buffer (a new sequence) is rebuilt in order, with no stale map entries
+    lb.packed_len.zero_()
+    apply(cur, ids, 2)
+    for b in range(2):
+        _check_pack_state(w, lb, d, b, cur[b], N, ordered=True)
