@@ -397,21 +397,39 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_assign(UpdArgs a) {
   const int32_t* btb = a.bt + (size_t)r.b * a.max_pages;
   const int n_sink_copy = (rebuild && r.chunk == 0) ? a.n_sink : 0;
   const int nl = (int)tot + n_sink_copy;
-  for (int e = rsub; e < nl; e += RPB) {
-    const bool sink = e >= (int)tot;
-    const int pos = sink ? e - (int)tot : l_pos[e];
-    const int slot = sink ? pos : l_slot[e];
-    if (sink && sub == 0) {
-      ppos[pos] = pos;
-      if (in_map(a, pos)) map[pos] = pos;
+  // kCopyBatch rows per lane group are loaded before any of them is stored (a rebuild
+  // copies a whole chunk)
+  constexpr int kCopyBatch = 4;
+  for (int e0 = rsub; e0 < nl; e0 += kCopyBatch * RPB) {
+    u32x4_t kv[kCopyBatch], vv[kCopyBatch];
+    size_t dst[kCopyBatch];
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const int e = e0 + u * RPB;
+      dst[u] = ~(size_t)0;
+      if (e < nl) {
+        const bool sink = e >= (int)tot;
+        const int pos = sink ? e - (int)tot : l_pos[e];
+        const int slot = sink ? pos : l_slot[e];
+        if (sink && sub == 0) {
+          ppos[pos] = pos;
+          if (in_map(a, pos)) map[pos] = pos;
+        }
+        const int page = btb[pos / kPage];
+        const size_t src =
+            (((size_t)page * a.Hkv + r.g) * kPage + pos % kPage) * rb + 16 * sub;
+        dst[u] = (r.bg * a.cap + slot) * rb + 16 * sub;
+        kv[u] = *reinterpret_cast<const u32x4_t*>(a.kc + src);
+        vv[u] = *reinterpret_cast<const u32x4_t*>(a.vc + src);
+      }
     }
-    const int page = btb[pos / kPage];
-    const size_t src = (((size_t)page * a.Hkv + r.g) * kPage + pos % kPage) * rb + 16 * sub;
-    const size_t dst = (r.bg * a.cap + slot) * rb + 16 * sub;
-    const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(a.kc + src);
-    const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(a.vc + src);
-    *reinterpret_cast<u32x4_t*>(a.pk + dst) = kv;
-    *reinterpret_cast<u32x4_t*>(a.pv + dst) = vv;
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      if (dst[u] != ~(size_t)0) {
+        *reinterpret_cast<u32x4_t*>(a.pk + dst[u]) = kv[u];
+        *reinterpret_cast<u32x4_t*>(a.pv + dst[u]) = vv[u];
+      }
+    }
   }
 }
 
