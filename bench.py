@@ -52,9 +52,10 @@ def _parse():
     ap.add_argument("--evidence-window", type=int, default=None,
                     help="decode queries pooled into the Selector's evidence at a slow step "
                          "(default: the workload's, 1)")
-    ap.add_argument("--full-pack", action="store_true",
-                    help="re-pack every selected row at each slow step (sfi_pack) instead of "
-                         "copying only the newly selected ones (sfi_pack_update)")
+    ap.add_argument("--pack", choices=("auto", "full", "incremental"), default="auto",
+                    help="full: re-pack every selected row at each slow step (sfi_pack); "
+                         "incremental: copy only the newly selected ones (sfi_pack_update); "
+                         "auto: the engine's choice (incremental for a stack of layers)")
     ap.add_argument("--device-control", action="store_true",
                     help="decide slow/fast and append K/V on the device every step (token "
                          "ids in, no host schedule); every step is replayed from a graph "
@@ -142,6 +143,7 @@ def main():
     from sparse_kv_attention_decode_amd.engine import Engine
 
     w = get(args.workload)
+    inc = {"auto": None, "full": False, "incremental": True}[args.pack]
     if args.evidence_window is not None:
         w = w.replace(evidence_window=args.evidence_window)
     steps = args.steps if args.steps is not None else w.steps
@@ -156,11 +158,10 @@ def main():
                 from workload.gen import BOUNDARY_TOKENS, gen_tokens
                 eng = Engine(w, d["flags"], two_streams=not args.one_stream,
                              device_control=True, tokens=gen_tokens(w, d["flags"]),
-                             boundary_tokens=BOUNDARY_TOKENS,
-                             incremental_pack=not args.full_pack)
+                             boundary_tokens=BOUNDARY_TOKENS, incremental_pack=inc)
             else:
                 eng = Engine(w, d["flags"], two_streams=not args.one_stream,
-                             incremental_pack=not args.full_pack)
+                             incremental_pack=inc)
         eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
         if keep:
             d0 = {k: d[k] for k in ("q", "K", "V", "flags")}
@@ -287,7 +288,7 @@ def main():
                    "fast_step_graph": eng.graph is not None,
                    "evidence_window": w.evidence_window,
                    "device_control": bool(args.device_control),
-                   "pack": "full" if args.full_pack else "incremental"},
+                   "pack": "incremental" if eng.incremental_pack else "full"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {

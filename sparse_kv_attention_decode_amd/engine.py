@@ -148,7 +148,7 @@ class LayerBuffers:
         self.k_new = self.v_new = None           # [S, B, Hkv, D] (device-controlled steps)
         # slot of every position in the packed buffers, for the incremental pack
         self.slot_map = (torch.full((B, Hkv, eng.stride), -1, dtype=torch.int32, device=dev)
-                         if eng.incremental_pack else None)
+                         if eng._incremental_req is not False else None)
 
 
 class Engine:
@@ -156,7 +156,7 @@ class Engine:
                  dbg_scores: bool = False, sel_streams: int = 2,
                  window: Optional[int] = None, device_control: bool = False,
                  tokens=None, boundary_tokens=None, max_recent: Optional[int] = None,
-                 full_lists: bool = False, incremental_pack: bool = True):
+                 full_lists: bool = False, incremental_pack: Optional[bool] = None):
         self.w = w
         self.device = torch.device(device)
         self.device_control = device_control
@@ -164,8 +164,13 @@ class Engine:
         # (-1 padded), the launch shape of device-controlled steps.
         self.full_lists = full_lists
         # incremental_pack: a slow step copies only the newly selected rows into the packed
-        # buffers (sfi_pack_update) instead of all of them (sfi_pack)
+        # buffers (sfi_pack_update) instead of all of them (sfi_pack).  None chooses when the
+        # stack is known (first step): incremental for several layers, where the pack runs
+        # beside the next layer's attention and the bytes it moves slow that attention down;
+        # full for one layer, where the pack is on the step's critical path and one kernel
+        # beats the update's chain of four short ones (measured both ways on every workload).
         self.incremental_pack = incremental_pack
+        self._incremental_req = incremental_pack
         # Decode queries pooled into the Selector's evidence at a slow step (1: the current
         # query only).
         self.window = int(w.evidence_window if window is None else window)
@@ -221,7 +226,7 @@ class Engine:
         if sel_ws == 0:
             raise ValueError(f"evidence window {win} is not supported for this shape "
                              f"(window >= 1 and group * window <= 16)")
-        if incremental_pack:
+        if incremental_pack is not False:
             sel_ws = max(sel_ws, L.sfi_pack_update_ws(self.shape, self.params, B))
         self.ws_sels = [L.workspace(sel_ws, dev) for _ in range(n_sel)]
         self.ws_sel = self.ws_sels[0]
@@ -432,6 +437,8 @@ class Engine:
         step costs one foreign call per kernel launch and no tensor indexing."""
         import ctypes
         self._lib = L.load()
+        if self._incremental_req is None:
+            self.incremental_pack = len(self.layers) > 1
         self._shp = ctypes.byref(self.shape)
         self._prm = ctypes.byref(self.params)
         B = self.w.batch

@@ -20,9 +20,10 @@ if torch.cuda.is_available():
     from sparse_kv_attention_decode_amd.engine import Engine
 
 
-def _setup(w, dbg=False, two_streams=True, layer=0):
+def _setup(w, dbg=False, two_streams=True, layer=0, incremental_pack=None):
     d = make_layer(w, layer, device="cuda")
-    eng = Engine(w, d["flags"], two_streams=two_streams, dbg_scores=dbg)
+    eng = Engine(w, d["flags"], two_streams=two_streams, dbg_scores=dbg,
+                 incremental_pack=incremental_pack)
     lb = eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
     return d, eng, lb
 
@@ -155,18 +156,20 @@ def test_pack_bit_exact(name):
             assert bool((_bits(pk[g, n:]) == 0).all()) and bool((_bits(pv[g, n:]) == 0).all())
 
 
-@pytest.mark.parametrize("name,win,sliding", [(n, 1, False) for n in SMALL] +
-                         [("tiny_fp32_1k", 3, False), ("qwen3_0p6b_8k", 4, False),
-                          ("qwen3_0p6b_8k", 1, True)])
-def test_trajectory_lockstep(name, win, sliding):
+@pytest.mark.parametrize("name,win,sliding,inc", [(n, 1, False, None) for n in SMALL] +
+                         [("tiny_fp32_1k", 3, False, None), ("qwen3_0p6b_8k", 4, False, None),
+                          ("qwen3_0p6b_8k", 1, True, None), ("tiny_fp32_1k", 1, False, True),
+                          ("qwen3_0p6b_8k", 1, False, True)])
+def test_trajectory_lockstep(name, win, sliding, inc):
     """Every step of the seeded trajectory through the two-stream engine.  Slow steps:
     dense output and the selection (near-tie rule); the oracle then continues with the
     device's selection (teacher forcing) so the two cannot drift.  Fast steps: the
     two-segment output against the oracle's fast step on the same memory.  win > 1 pools
     the Selector's evidence over that many decode queries; sliding moves the recent
-    segment to the newest W positions at every step."""
+    segment to the newest W positions at every step; inc forces the incremental pack (a
+    one-layer engine packs in full by default)."""
     w = get(name).replace(evidence_window=win, sliding_recent=sliding)
-    d, eng, lb = _setup(w)
+    d, eng, lb = _setup(w, incremental_pack=inc)
     B = w.batch
     host = [oracle_layer_arrays(d, b) for b in range(B)]
     norms = [O.key_norms(K) for _, K, _ in host]

@@ -62,14 +62,15 @@ def test_step_control_matches_oracle(batch, steps, budget, sliding):
         np.testing.assert_array_equal(cnt.cpu().numpy(), ref["counts"][s], f"step {s}")
 
 
-def _engines(w, layers, graphs=False):
+def _engines(w, layers, graphs=False, inc=None):
     """A host-scheduled and a device-controlled engine over the same generated layers."""
     data = [make_layer(w, li, device="cuda") for li in range(layers)]
     tokens = gen_tokens(w, data[0]["flags"])
     # the host engine passes whole -1-padded lists too, so both launch the same splits
-    host = Engine(w, data[0]["flags"], max_recent=recent_bound(w), full_lists=True)
+    host = Engine(w, data[0]["flags"], max_recent=recent_bound(w), full_lists=True,
+                  incremental_pack=inc)
     devc = Engine(w, data[0]["flags"], device_control=True, tokens=tokens,
-                  boundary_tokens=BOUNDARY_TOKENS)
+                  boundary_tokens=BOUNDARY_TOKENS, incremental_pack=inc)
     for d in data:
         host.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
         devc.add_layer(d["k_cache"].clone(), d["v_cache"].clone(), d["block_table"], d["q"])
@@ -78,17 +79,18 @@ def _engines(w, layers, graphs=False):
     return data, host, devc
 
 
-@pytest.mark.parametrize("name,batch,layers,graphs,sliding",
-                         [("tiny_fp32_1k", 1, 1, False, False),
-                          ("qwen3_0p6b_8k", 3, 1, False, False),
-                          ("qwen3_0p6b_8k", 3, 2, True, False),
-                          ("qwen3_0p6b_8k", 3, 1, False, True)])
-def test_device_trajectory_bit_identical_to_host(name, batch, layers, graphs, sliding):
+@pytest.mark.parametrize("name,batch,layers,graphs,sliding,inc",
+                         [("tiny_fp32_1k", 1, 1, False, False, None),
+                          ("qwen3_0p6b_8k", 3, 1, False, False, None),
+                          ("qwen3_0p6b_8k", 3, 2, True, False, None),
+                          ("qwen3_0p6b_8k", 3, 1, False, True, None),
+                          ("qwen3_0p6b_8k", 3, 1, False, False, True)])
+def test_device_trajectory_bit_identical_to_host(name, batch, layers, graphs, sliding, inc):
     """The whole trajectory decided on the device (tokens -> modes, K/V appended step by
     step) against the host schedule: outputs after every step, then the selections, the
     packed buffers, the re-filled caches and the key norms, all bit for bit."""
     w = get(name).replace(batch=batch, name=f"{name}_b{batch}", sliding_recent=sliding)
-    data, host, devc = _engines(w, layers, graphs)
+    data, host, devc = _engines(w, layers, graphs, inc)
     for s in range(w.steps):
         host.step(s)
         devc.step(s)
@@ -122,7 +124,7 @@ def test_device_trajectory_bit_identical_to_host(name, batch, layers, graphs, sl
 def test_device_trajectory_restarts():
     """Running the trajectory twice (step 0 resets the state) gives the same results."""
     w = get("qwen3_0p6b_8k").replace(steps=48, name="qwen3_0p6b_8k_s48")
-    data, host, devc = _engines(w, 1)
+    data, host, devc = _engines(w, 1, inc=True)
     outs = []
     for rep in range(2):
         for s in range(w.steps):
