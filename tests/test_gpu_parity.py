@@ -658,3 +658,22 @@ def test_pack_update_keeps_held_rows_and_adds_new_ones():
     apply(cur, ids, 2)
     for b in range(2):
         _check_pack_state(w, lb, d, b, cur[b], N, ordered=True)
+
+
+def test_pack_update_full_size():
+    """The incremental pack at the benchmark's full size (131072-token context, K = 19456, one
+    layer): a rebuild at the first slow step, then updates at later slow steps of the seeded
+    schedule, each leaving exactly sink + selection in the buffer, byte for byte."""
+    w = get("qwen3_4b_128k_36l").replace(layers=1)
+    d, eng, lb = _setup(w, incremental_pack=True)
+    slow = [s for s in range(w.steps) if eng.mode(s)[0]][:3]
+    for s in range(slow[-1] + 1):
+        eng.step(s)
+        if s in slow:
+            eng.join()
+            torch.cuda.synchronize()
+            N = w.seq_len(s)
+            sel = lb.sel_idx[0].cpu().numpy()
+            want = [sel[g][sel[g] >= 0] for g in range(w.num_kv_heads)]
+            _check_pack_state(w, lb, d, 0, want, N, ordered=(s == slow[0]))
+    print("slow steps checked:", slow)
