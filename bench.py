@@ -29,6 +29,30 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 
 
+def read_ceiling(gib: float) -> float:
+    """GB/s (bytes read + bytes written) of a device-to-device copy of `gib` GiB, far larger
+    than every cache: the practical HBM ceiling the roofline fraction can be set against."""
+    import torch
+    n = int(gib * 2 ** 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = reps * 2 * n * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
 def _parse():
     from workload import BENCH_WORKLOAD
     ap = argparse.ArgumentParser(description=__doc__)
@@ -49,6 +73,11 @@ def _parse():
                          "fast-step graph")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue the Selector and pack on the attention stream")
+    ap.add_argument("--repeats", type=int, default=20,
+                    help="after the timed region, run the timed steps this many more times and "
+                         "report the median, p10 and p90 of the time per step (0: skip)")
+    ap.add_argument("--ceiling-gib", type=float, default=4.0,
+                    help="size of the copy that measures the practical HBM ceiling (0: skip)")
     ap.add_argument("--evidence-window", type=int, default=None,
                     help="decode queries pooled into the Selector's evidence at a slow step "
                          "(default: the workload's, 1)")
@@ -218,6 +247,27 @@ def main():
     slow = agg("slow")
 
     # Full-KV dense baseline: dense attention of every layer, no Selector
+    # spread: the same steps again, several times (after the timed region, not part of it)
+    rep_ms = []
+    for _ in range(max(0, args.repeats)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(eng.stream1)
+        for k in range(steps):
+            eng.step(k % S)
+        eng.join()
+        e1.record(eng.stream1)
+        torch.cuda.synchronize()
+        rep_ms.append(e0.elapsed_time(e1) / steps)
+    repeats = None
+    if rep_ms:
+        import numpy as np
+        q = np.percentile(rep_ms, [10, 50, 90])
+        repeats = {"n": len(rep_ms), "ms_per_step_p10": round(float(q[0]), 4),
+                   "ms_per_step_median": round(float(q[1]), 4),
+                   "ms_per_step_p90": round(float(q[2]), 4),
+                   "value_median": round(steps * w.layers / (float(q[1]) * steps * 1e-3), 2)}
+
     dense = None
     if args.dense_steps > 0:
         dt = []
@@ -237,6 +287,7 @@ def main():
                  "gbs": (sum(b for _, b in dk) / (sum(t for t, _ in dk) * 1e-3) / 1e9)
                  if dk else None}
 
+    ceiling = read_ceiling(args.ceiling_gib) if args.ceiling_gib > 0 else None
     ms_per_step = total_ms / steps
     value = steps * w.layers / (total_ms * 1e-3)
     traffic = None
@@ -301,6 +352,13 @@ def main():
             "fast_vs_dense": (dense["step_ms"] / mean(fast_ms)) if dense and fast_ms else None,
             "mixed_vs_dense": (dense["step_ms"] / ms_per_step) if dense else None,
             "setup_s": round(setup_s, 1),
+            "repeats": repeats,
+            "copy_ceiling_gbs": ceiling,
+            "fast_call_frac_of_copy_ceiling": (round(fast["gbs"] / ceiling, 4)
+                                               if fast and ceiling else None),
+            # K/V of one step fit in the 256 MiB Infinity Cache: repeated steps may be served
+            # from it rather than from HBM
+            "cache_resident": eng.dense_bytes(0, range(w.batch)) < 256 * 2 ** 20,
         },
     }
     print(json.dumps(line), flush=True)
