@@ -66,8 +66,8 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle CPU baseline sample (0 disables it)")
     ap.add_argument("--time-every", type=int, default=9,
-                    help="bracket every n-th attention call issued call by call with HIP "
-                         "events (0: none); graph replays are always bracketed")
+                    help="bracket every n-th attention call issued call by call, and every "
+                         "n-th fast-step graph replay, with HIP events (0: none)")
     ap.add_argument("--no-graphs", action="store_true",
                     help="issue fast steps call by call instead of replaying the captured "
                          "fast-step graph")

@@ -554,8 +554,8 @@ class Engine:
         dense_only runs the Full-KV baseline: dense attention for every sequence, no
         Selector, no logits.  When `timer` is a list, every `time_every`-th attention call
         (counted over the engine's life) is bracketed by two events on stream 1 and
-        (kind, start, end, algorithmic bytes, calls) is appended; a graph replay is
-        bracketed as a whole (calls = layers).
+        (kind, start, end, algorithmic bytes, calls) is appended; graph replays are sampled the
+        same way, each bracketed as a whole (calls = layers).
         """
         if getattr(self, "_bound_layers", -1) != len(self.layers):
             self._bind()
@@ -569,7 +569,7 @@ class Engine:
         # only for layer i's pack and overlaps the Selector work still queued on stream 2.
         if self.graph is not None and not dense_only and s in self.graphs and \
                 not any(lb.pack_pending for lb in self.layers):
-            self._step_graph(s, timer)
+            self._step_graph(s, timer, time_every)
             return
         w, lib, shp, prm = self.w, self._lib, self._shp, self._prm
         n_slow = len(self.plan.slow_ids[s])
@@ -643,12 +643,14 @@ class Engine:
                     lb.ev_pack.record(s2)
                     lb.pack_pending = True
 
-    def _step_graph(self, s: int, timer: Optional[list]) -> None:
-        """Fast step s of every row through its captured graph (no pack pending)."""
+    def _step_graph(self, s: int, timer: Optional[list], time_every: int = 1) -> None:
+        """Fast step s of every row through its captured graph (no pack pending).  With a
+        timer, every time_every-th replay (counted over the engine's life) is bracketed."""
         s1 = self.stream1
         g = self.graphs[s]
+        self._replays = getattr(self, "_replays", 0) + 1
         with torch.cuda.stream(s1):
-            if timer is None:
+            if timer is None or (self._replays - 1) % max(1, time_every):
                 g.replay()
             else:
                 e0 = torch.cuda.Event(enable_timing=True)
