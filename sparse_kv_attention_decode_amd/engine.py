@@ -27,6 +27,15 @@ holding that step's calls for every layer, with the step's own query, length and
 recent-start pointers, so a replay is the kernels alone.  This removes the host cost of
 issuing one call per layer, which is larger than a fast call's GPU time.  The first fast
 step after a slow step stays call by call (see `step`).
+
+Pack: the packed buffers are either rebuilt at each slow step (sfi_pack) or updated in
+place with only the newly selected rows (sfi_pack_update); the engine updates for a stack
+of layers and rebuilds for one layer (see `Engine.__init__`).  Step 0 empties them.
+
+Device control (`device_control=True`): the schedule is decided on the device from the
+decoded token ids instead (sfi_step_control), the new K/V rows are appended there
+(sfi_kv_append), and every step is one graph (`enable_device_graphs`); nothing on the
+host depends on the schedule.
 """
 from __future__ import annotations
 
