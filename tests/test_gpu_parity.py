@@ -625,7 +625,10 @@ def test_pack_update_keeps_held_rows_and_adds_new_ones():
     apply(cur, ids, 2)
     for b in range(2):
         _check_pack_state(w, lb, d, b, cur[b], N, ordered=True)
-    for turnover, grow in ((0.0, 0), (0.05, 10), (0.5, 20), (1.0, 30), (0.2, 0)):
+    plan = [(0.0, 0), (0.05, 10), (0.5, 20), (1.0, 30), (0.2, 0)]
+    plan += [(float(rng.choice([0.0, 0.01, 0.1, 0.3, 1.0])), int(rng.integers(0, 3)))
+             for _ in range(15)]  # seeded random turnovers, growing by at most 2
+    for turnover, grow in plan:
         new = []
         for b in range(2):
             rows = []
