@@ -680,3 +680,48 @@ def test_pack_update_full_size():
             want = [sel[g][sel[g] >= 0] for g in range(w.num_kv_heads)]
             _check_pack_state(w, lb, d, 0, want, N, ordered=(s == slow[0]))
     print("slow steps checked:", slow)
+
+
+def test_full_stack_in_bench_configuration():
+    """The benchmark's own launch configuration: all 36 layers of the 128K workload, fast steps
+    replayed from graphs, the incremental pack, two Selector streams.  At a slow step and at the
+    last fast step before the next one (a graph replay), the outputs of layers 0, 17 and 35
+    against the oracle: the dense output, then the fast output on the device's memory (its
+    packed positions as a set and its recent edge)."""
+    w = get("qwen3_4b_128k_36l")
+    sample = (0, 17, 35)
+    data, eng = {}, None
+    for li in range(w.layers):
+        d = make_layer(w, li, device="cuda", keep_logical=li in sample)
+        if eng is None:
+            eng = Engine(w, d["flags"])
+        eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
+        if li in sample:
+            data[li] = {k: d[k] for k in ("q", "K", "V")}
+        del d
+    eng.enable_graphs()
+    assert eng.graph is not None and eng.incremental_pack and len(eng.sel_streams) == 2
+    slow = [s for s in range(w.steps) if eng.mode(s)[0]]
+    i = next(i for i in range(1, len(slow) - 1) if slow[i + 1] - slow[i] >= 3)
+    s_slow, s_fast = slow[i], slow[i + 1] - 1
+    host = {li: (host64(data[li]["q"][:, 0]), host64(data[li]["K"][0]), host64(data[li]["V"][0]))
+            for li in sample}
+    for s in range(s_fast + 1):
+        eng.step(s)
+        if s not in (s_slow, s_fast):
+            continue
+        eng.join()
+        torch.cuda.synchronize()
+        N = w.seq_len(s)
+        for li in sample:
+            lb = eng.layers[li]
+            q, K, V = host[li]
+            if s == s_slow:
+                o = O.attention(q[s], K[:, :N], V[:, :N])[0]
+            else:
+                plen = lb.packed_len[0].cpu().numpy()
+                ppos = lb.packed_pos[0].cpu().numpy()
+                packed = [np.sort(ppos[g, :plen[g]]) for g in range(w.num_kv_heads)]
+                o, _ = O.fast_attention(q[s], K, V, packed, int(eng.plan.recent_start[s, 0]), N)
+            check_out(host64(lb.out[0]), o, f"layer {li} step {s}")
+    print(f"checked slow step {s_slow} and graph-replayed fast step {s_fast}")
