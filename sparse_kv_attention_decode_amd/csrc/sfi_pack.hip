@@ -120,6 +120,9 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack(PackArgs a) {
 //               prefix), so the free list is in slot order;
 //   4. assign   sel chunks give the j-th new position the j-th free slot (past the old end
 //               once the freed slots are used up), record it, and copy its K/V rows.
+// Kernel 4 publishes the new packed length from one chunk while the other chunks of the
+// same ig may not have started, so no chunk of it reads packed_len: kernel 3 keeps a copy
+// of the old length for it.
 // Chunk prefixes are sums over at most a few dozen per-chunk counts, so every assignment is
 // deterministic.  An empty buffer (packed_len 0) or a selection smaller than the rows held
 // is rebuilt in sfi_pack's order by kernels 3 and 4.
@@ -144,6 +147,7 @@ struct UpdArgs {
   int32_t* cnt_add;    // [n_ig][nc_sel]
   int32_t* cnt_valid;  // [n_ig][nc_sel]
   int32_t* free_slot;  // [n_ig][K]
+  int32_t* plen_old;   // [n_ig] held length before this update (written by kernel 3)
   int Hkv, K, n_sink, cap, nc_sel, nc_slot, max_pages, row_bytes;
 };
 
@@ -288,6 +292,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_free(UpdArgs a) {
     sh[0] = f.before;
     sh[1] = v.total;  // K_eff
     sh[2] = held_len(a, r.bg);
+    if (r.chunk == 0) a.plen_old[r.ig] = sh[2];
   }
   __syncthreads();
   const int keff = sh[1], plen = sh[2];
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_assign(UpdArgs a) {
     sh[1] = ad.total;
     sh[2] = fr.total;
     sh[3] = v.total;  // K_eff
-    sh[4] = held_len(a, r.bg);
+    sh[4] = a.plen_old[r.ig];  // not packed_len: chunk 0 of this kernel overwrites it
   }
   __syncthreads();
   const int keff = sh[3], plen = sh[4];
@@ -379,11 +384,17 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_assign(UpdArgs a) {
         slot = a.n_sink + k0 + i;  // the full pack's order
       else
         slot = j < (uint32_t)sh[2] ? fslot[j] : plen + (int)(j - (uint32_t)sh[2]);
-      ppos[slot] = q[i];
-      if (in_map(a, q[i])) map[q[i]] = slot;
-      l_pos[li] = q[i];
-      l_slot[li] = slot;
       ++j;
+      // The counts make every slot < n_sink + K_eff <= cap; a slot outside the buffer can
+      // only come from corrupted state and is dropped (position -1 in the copy list)
+      // rather than written.
+      const bool in_buf = slot >= a.n_sink && slot < a.cap;
+      if (in_buf) {
+        ppos[slot] = q[i];
+        if (in_map(a, q[i])) map[q[i]] = slot;
+      }
+      l_pos[li] = in_buf ? q[i] : -1;
+      l_slot[li] = slot;
       ++li;
     }
   }
@@ -407,7 +418,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_assign(UpdArgs a) {
     for (int u = 0; u < kCopyBatch; ++u) {
       const int e = e0 + u * RPB;
       dst[u] = ~(size_t)0;
-      if (e < nl) {
+      if (e < nl && (e >= (int)tot || l_pos[e] >= 0)) {
         const bool sink = e >= (int)tot;
         const int pos = sink ? e - (int)tot : l_pos[e];
         const int slot = sink ? pos : l_slot[e];
@@ -443,7 +454,7 @@ size_t pack_update_ws(const sfi_shape& s, const sfi_select_params& prm, int n_se
   const size_t nc_slot = ceil_div(prm.n_sink + prm.top_k + 15, kChunk);  // >= packed_cap
   auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
   return r256(n_ig * nc_slot * 4) + 2 * r256(n_ig * nc_sel * 4) +
-         r256(n_ig * (size_t)prm.top_k * 4);
+         r256(n_ig * (size_t)prm.top_k * 4) + r256(n_ig * 4);
 }
 
 hipError_t launch_pack_update(const sfi_shape& s, const sfi_select_params& prm,
@@ -466,6 +477,8 @@ hipError_t launch_pack_update(const sfi_shape& s, const sfi_select_params& prm,
   a.cnt_valid = reinterpret_cast<int32_t*>(w);
   w += r256((size_t)n_ig * a.nc_sel * 4);
   a.free_slot = reinterpret_cast<int32_t*>(w);
+  w += r256((size_t)n_ig * prm.top_k * 4);
+  a.plen_old = reinterpret_cast<int32_t*>(w);
   a.sel = sel_idx;
   a.seq_ids = seq_ids;
   a.kc = reinterpret_cast<const uint8_t*>(k_cache);

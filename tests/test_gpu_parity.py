@@ -663,6 +663,72 @@ def test_pack_update_keeps_held_rows_and_adds_new_ones():
         _check_pack_state(w, lb, d, b, cur[b], N, ordered=True)
 
 
+def test_pack_update_rebuilds_beside_a_busy_stream():
+    """Rebuilds (emptied buffer) and growing updates of sfi_pack_update while another stream
+    keeps the CUs busy, so that the workgroups of one (row, KV head) start at different times.
+    The assign kernel publishes the new packed length from one workgroup; every other
+    workgroup must still work from the old one (a workgroup that read the new length at a
+    rebuild would place rows past the buffer).  Each round must leave exactly sink +
+    selection in the buffer."""
+    w = get("qwen3_0p6b_8k").replace(batch=2, top_k=4096, name="pack_update_busy")
+    d, eng, lb = _setup(w, incremental_pack=True)
+    dev = "cuda"
+    N = w.context
+    lo, hi = O.candidates(N, w.n_sink, w.n_recent)
+    rng = np.random.default_rng(11)
+    ws = L.workspace(L.sfi_pack_update_ws(eng.shape, eng.params, w.batch), dev)
+    ids = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+    busy = torch.cuda.Stream()
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    busy.wait_stream(torch.cuda.current_stream())
+
+    def apply(sets):
+        sel = torch.full((w.batch, w.num_kv_heads, w.top_k), -1, dtype=torch.int32)
+        for b in range(w.batch):
+            for g in range(w.num_kv_heads):
+                sel[b, g, :len(sets[b][g])] = torch.from_numpy(sets[b][g].astype(np.int32))
+        with torch.cuda.stream(side):
+            lb.sel_idx.copy_(sel.to(dev))
+            L.sfi_pack_update(eng.shape, eng.params, lb.k_cache, lb.v_cache, lb.block_table,
+                              lb.sel_idx, ids, 2, lb.packed_k, lb.packed_v, lb.packed_pos,
+                              lb.packed_len, eng.packed_cap, lb.slot_map, eng.stride, ws,
+                              stream=side)
+
+    for rnd in range(6):
+        n0 = int(rng.integers(3000, 3900))
+        cur = [[np.sort(rng.choice(np.arange(lo, hi), n0, replace=False)) for _ in range(8)]
+               for _ in range(2)]
+        with torch.cuda.stream(busy):
+            for _ in range(4):
+                dst.copy_(src)
+        with torch.cuda.stream(side):
+            lb.packed_len.zero_()
+        apply(cur)
+        torch.cuda.synchronize()
+        for b in range(2):
+            _check_pack_state(w, lb, d, b, cur[b], N, ordered=True)
+        grow = int(rng.integers(1, 4096 - n0))
+        new = []
+        for b in range(2):
+            rows = []
+            for g in range(8):
+                keep = rng.choice(cur[b][g], int(0.9 * len(cur[b][g])), replace=False)
+                pool = np.setdiff1d(np.arange(lo, hi), keep)
+                add = rng.choice(pool, len(cur[b][g]) + grow - len(keep), replace=False)
+                rows.append(np.sort(np.concatenate([keep, add])))
+            new.append(rows)
+        with torch.cuda.stream(busy):
+            for _ in range(4):
+                dst.copy_(src)
+        apply(new)
+        torch.cuda.synchronize()
+        for b in range(2):
+            _check_pack_state(w, lb, d, b, new[b], N)
+
+
 def test_pack_update_full_size():
     """The incremental pack at the benchmark's full size (131072-token context, K = 19456, one
     layer): a rebuild at the first slow step, then updates at later slow steps of the seeded
