@@ -71,6 +71,9 @@ def _parse():
     ap.add_argument("--no-graphs", action="store_true",
                     help="issue fast steps call by call instead of replaying the captured "
                          "fast-step graph")
+    ap.add_argument("--pace", choices=("auto", "on", "off"), default="auto",
+                    help="host queues a Selector stream's wait only once stream 1 has reached "
+                         "the attention it waits for (auto: on)")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue the Selector and pack on the attention stream")
     ap.add_argument("--repeats", type=int, default=20,
@@ -173,6 +176,7 @@ def main():
 
     w = get(args.workload)
     inc = {"auto": None, "full": False, "incremental": True}[args.pack]
+    pace = {"auto": None, "on": True, "off": False}[args.pace]
     if args.evidence_window is not None:
         w = w.replace(evidence_window=args.evidence_window)
     steps = args.steps if args.steps is not None else w.steps
@@ -190,7 +194,7 @@ def main():
                              boundary_tokens=BOUNDARY_TOKENS, incremental_pack=inc)
             else:
                 eng = Engine(w, d["flags"], two_streams=not args.one_stream,
-                             incremental_pack=inc)
+                             incremental_pack=inc, paced=pace)
         eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
         if keep:
             d0 = {k: d[k] for k in ("q", "K", "V", "flags")}
@@ -213,9 +217,12 @@ def main():
     eng.join()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` decode steps of every layer
+    # timed region: exactly `steps` decode steps of every layer; every event it records is
+    # created beforehand (at most two sampled calls per layer and step, plus graph replays)
     timer = []
     step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    if args.time_every > 0:
+        eng.reserve_timing_events(steps * (2 * w.layers + 1) // args.time_every + 16)
     torch.cuda.synchronize()
     for k in range(steps):
         step_ev[k].record(eng.stream1)
@@ -339,7 +346,8 @@ def main():
                    "fast_step_graph": eng.graph is not None,
                    "evidence_window": w.evidence_window,
                    "device_control": bool(args.device_control),
-                   "pack": "incremental" if eng.incremental_pack else "full"},
+                   "pack": "incremental" if eng.incremental_pack else "full",
+                   "paced": bool(eng.paced) and not args.device_control},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {

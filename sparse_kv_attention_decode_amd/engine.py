@@ -165,7 +165,8 @@ class Engine:
                  dbg_scores: bool = False, sel_streams: int = 2,
                  window: Optional[int] = None, device_control: bool = False,
                  tokens=None, boundary_tokens=None, max_recent: Optional[int] = None,
-                 full_lists: bool = False, incremental_pack: Optional[bool] = None):
+                 full_lists: bool = False, incremental_pack: Optional[bool] = None,
+                 paced: Optional[bool] = None):
         self.w = w
         self.device = torch.device(device)
         self.device_control = device_control
@@ -180,6 +181,18 @@ class Engine:
         # beats the update's chain of four short ones (measured both ways on every workload).
         self.incremental_pack = incremental_pack
         self._incremental_req = incremental_pack
+        # paced: the host queues a slow step's first Selector-stream wait (on its layer's
+        # attention) only once stream 1 has finished every step before the previous one.
+        # The host can otherwise run many steps ahead of the GPU, and a wait queued there
+        # slowed every kernel on stream 1 meanwhile: fast steps took 0.97 ms instead of
+        # 0.89 ms on the 36-layer 128K stack.  One step of lead is kept so that the host's
+        # issue of the slow step stays hidden (waiting for the previous step too made slow
+        # steps host-bound in a first process on a fresh GPU machine: 6.5 ms instead of 4.8 ms).
+        # None chooses by size: paced when a layer's dense K/V per step is at least 8 MiB;
+        # below that a step is shorter than its host issue time and the wait costs more than
+        # it saves (measured both ways on every workload).
+        self.paced = paced
+        self._paced_req = paced
         # Decode queries pooled into the Selector's evidence at a slow step (1: the current
         # query only).
         self.window = int(w.evidence_window if window is None else window)
@@ -385,8 +398,7 @@ class Engine:
         s1 = self.stream1
         e0 = e1 = None
         if timer is not None:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
+            e0, e1 = self._timing_events()
             e0.record(s1)
         if s in self.graphs:
             self.join()
@@ -448,6 +460,13 @@ class Engine:
         self._lib = L.load()
         if self._incremental_req is None:
             self.incremental_pack = len(self.layers) > 1
+        if self._paced_req is None:
+            w = self.w
+            dense = w.batch * w.num_kv_heads * w.context * 2 * w.head_dim * w.elem_bytes
+            self.paced = dense >= 8 << 20
+        # start of each step on stream 1, alternating by the engine's own step count
+        self._ev_step = [torch.cuda.Event(), torch.cuda.Event()]
+        self._nstep = 0
         self._shp = ctypes.byref(self.shape)
         self._prm = ctypes.byref(self.params)
         B = self.w.batch
@@ -571,6 +590,9 @@ class Engine:
         if self.device_control and not dense_only:
             self._device_step(s, timer)
             return
+        if not dense_only:
+            self._ev_step[self._nstep % 2].record(self.stream1)
+            self._nstep += 1
         if s == 0 and not dense_only:
             self._new_sequences()
         # The graph waits for every layer's pending pack before its first call, so the
@@ -604,8 +626,7 @@ class Engine:
             if timer is None or (self._calls - 1) % time_every:
                 fn()
                 return
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
+            e0, e1 = self._timing_events()
             e0.record(s1)
             fn()
             e1.record(s1)
@@ -614,6 +635,32 @@ class Engine:
         fb = self.fast_bytes(s) if (timer is not None and n_fast) else 0
         db = self.dense_bytes(s, range(w.batch) if dense_only else self.plan.slow_ids[s]) \
             if timer is not None else 0
+
+        def selector(li, lb, P):
+            """Selector and pack of layer li on its Selector stream, behind its attention."""
+            k = li % len(self.sel_streams)
+            s2, h2 = self.sel_streams[k], self._h2[k]
+            ws_sel, ws_sel_n = self._ws_sel[k]
+            if s2 is not s1:
+                lb.ev_attn.record(s1)
+                if pace and not paced_wait[0]:
+                    # stream 1 has finished every step before the previous one; the previous
+                    # step and this step's first attention keep the GPU busy meanwhile
+                    self._ev_step[(self._nstep - 2) % 2].synchronize()
+                    paced_wait[0] = True
+                s2.wait_event(lb.ev_attn)
+            ok("sfi_select_window", lib.sfi_select_window(
+                shp, prm, win, P["z"], self.stride, P["lse"], P["norm"], self.stride, seq_len,
+                slow_ids, m_slow, self.max_len, P["sel"], self._dbg_p, ws_sel, ws_sel_n, h2))
+            self._pack(P, slow_ids, m_slow, ws_sel, ws_sel_n, h2)
+            if s2 is not s1:
+                lb.ev_pack.record(s2)
+                lb.pack_pending = True
+
+        # Pacing (see `paced`): the first Selector-stream wait of a slow step is queued only
+        # once stream 1 has finished the steps before the previous one.
+        pace = bool(n_slow) and not dense_only and self.paced and self.sel_streams[0] is not s1
+        paced_wait = [False]
         for li, lb in enumerate(self.layers):
             P = lb.ptr
             q = P["q"] + s * lb.q_step
@@ -637,20 +684,7 @@ class Engine:
                         shp, win, qw, P["k"], P["v"], P["bt"], seq_len, slow_ids, m_slow,
                         self.max_len, P["out"], P["z"], self.stride, P["lse"], ws_slow,
                         ws_slow_n, h1)))
-                k = li % len(self.sel_streams)
-                s2, h2 = self.sel_streams[k], self._h2[k]
-                ws_sel, ws_sel_n = self._ws_sel[k]
-                if s2 is not s1:
-                    lb.ev_attn.record(s1)
-                    s2.wait_event(lb.ev_attn)
-                ok("sfi_select_window", lib.sfi_select_window(
-                    shp, prm, win, P["z"], self.stride, P["lse"], P["norm"], self.stride, seq_len,
-                    slow_ids, m_slow, self.max_len, P["sel"], self._dbg_p, ws_sel, ws_sel_n,
-                    h2))
-                self._pack(P, slow_ids, m_slow, ws_sel, ws_sel_n, h2)
-                if s2 is not s1:
-                    lb.ev_pack.record(s2)
-                    lb.pack_pending = True
+                selector(li, lb, P)
 
     def _step_graph(self, s: int, timer: Optional[list], time_every: int = 1) -> None:
         """Fast step s of every row through its captured graph (no pack pending).  With a
@@ -662,13 +696,25 @@ class Engine:
             if timer is None or (self._replays - 1) % max(1, time_every):
                 g.replay()
             else:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0, e1 = self._timing_events()
                 e0.record(s1)
                 g.replay()
                 e1.record(s1)
                 nl = len(self.layers)
                 timer.append(("fast", e0, e1, self.fast_bytes(s) * nl, nl))
+
+    def reserve_timing_events(self, n: int) -> None:
+        """Create n pairs of timing events now, for the timed calls to take: event creation
+        can cost milliseconds of host time in a fresh process, which a timed region should
+        not include."""
+        self._ev_pool = [(torch.cuda.Event(enable_timing=True),
+                          torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def _timing_events(self):
+        pool = getattr(self, "_ev_pool", None)
+        if pool:
+            return pool.pop()
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def join(self) -> None:
         """Make stream 1 wait for every outstanding Selector/pack."""
