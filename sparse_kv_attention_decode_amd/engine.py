@@ -16,7 +16,9 @@ issued on a Selector stream after an event recorded behind layer i's slow attent
 they run while stream 1 continues with layer i+1.  There are two Selector streams, used by
 alternate layers, so that the short dependent kernels of two layers' Selectors overlap
 each other too.  Before layer i's next attention, stream 1 waits for layer i's pack event.
-All streams have the default priority.
+All streams have the default priority.  Before a slow step queues its first Selector-stream
+wait, the host lets stream 1 come within one step of it (`paced`), so that no such wait sits in a
+queue far ahead of the attention it depends on.
 
 All per-step tables (sequence lengths, recent-window starts, slow/fast row lists) are
 built on the host from the seeded flags and copied to the device once, so a step issues
