@@ -74,6 +74,10 @@ def _parse():
     ap.add_argument("--pace", choices=("auto", "on", "off"), default="auto",
                     help="host queues a Selector stream's wait only once stream 1 has reached "
                          "the attention it waits for (auto: on)")
+    ap.add_argument("--sel-lookahead", type=int, default=None,
+                    help="with pacing, queue layer i's Selector only after layer i's attention "
+                         "has finished, with this many attention calls queued behind it (0: off; "
+                         "default: 2 for stacks of more than two layers)")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue the Selector and pack on the attention stream")
     ap.add_argument("--repeats", type=int, default=20,
@@ -194,7 +198,8 @@ def main():
                              boundary_tokens=BOUNDARY_TOKENS, incremental_pack=inc)
             else:
                 eng = Engine(w, d["flags"], two_streams=not args.one_stream,
-                             incremental_pack=inc, paced=pace)
+                             incremental_pack=inc, paced=pace,
+                             sel_lookahead=args.sel_lookahead)
         eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
         if keep:
             d0 = {k: d[k] for k in ("q", "K", "V", "flags")}
@@ -347,7 +352,8 @@ def main():
                    "evidence_window": w.evidence_window,
                    "device_control": bool(args.device_control),
                    "pack": "incremental" if eng.incremental_pack else "full",
-                   "paced": bool(eng.paced) and not args.device_control},
+                   "paced": bool(eng.paced) and not args.device_control,
+                   "sel_lookahead": int(eng.sel_lookahead or 0) if eng.paced else 0},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {
