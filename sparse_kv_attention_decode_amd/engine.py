@@ -648,17 +648,18 @@ class Engine:
         db = self.dense_bytes(s, range(w.batch) if dense_only else self.plan.slow_ids[s]) \
             if timer is not None else 0
 
-        def selector(li, lb, P, done_first=False):
+        def selector(li, lb, P, recorded=False, host_wait=False):
             """Selector and pack of layer li on its Selector stream, behind its attention.
-            done_first: the attention event is already recorded; the host waits for it."""
+            recorded: the attention event is already recorded; host_wait: the host first
+            waits for it."""
             k = li % len(self.sel_streams)
             s2, h2 = self.sel_streams[k], self._h2[k]
             ws_sel, ws_sel_n = self._ws_sel[k]
             if s2 is not s1:
-                if done_first:
-                    lb.ev_attn.synchronize()
-                else:
+                if not recorded:
                     lb.ev_attn.record(s1)
+                if host_wait:
+                    lb.ev_attn.synchronize()
                 if pace and not paced_wait[0]:
                     # stream 1 has finished every step before the previous one; the previous
                     # step and this step's first attention keep the GPU busy meanwhile
@@ -706,11 +707,13 @@ class Engine:
                     pending.append((li, lb, P))
                     while pending and pending[0][0] <= li - self.sel_lookahead:
                         lj, lbj, Pj = pending.pop(0)
-                        selector(lj, lbj, Pj, done_first=True)
+                        selector(lj, lbj, Pj, recorded=True, host_wait=True)
                 else:
                     selector(li, lb, P)
+        # The last layers' Selectors are queued at once: their waits sit behind at most
+        # sel_lookahead attention calls, and the host goes on to the next step meanwhile.
         for lj, lbj, Pj in pending:
-            selector(lj, lbj, Pj, done_first=True)
+            selector(lj, lbj, Pj, recorded=True)
 
     def _step_graph(self, s: int, timer: Optional[list], time_every: int = 1) -> None:
         """Fast step s of every row through its captured graph (no pack pending).  With a
