@@ -170,6 +170,7 @@ int prep_slow(const sfi_shape* shape, int32_t window, const float* q, const void
   p.part_l = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ml);
   p.part_o = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + 2 * ml);
   p.max_pages = shape->max_pages_per_seq;
+  p.max_len = max_seq_len;
   p.n_seqs = n_seqs;
   p.Hq = shape->num_q_heads;
   p.Hkv = shape->num_kv_heads;
@@ -415,6 +416,7 @@ int prep_fast(const sfi_shape* shape, const float* q, const void* packed_k, cons
   p.part_l = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ml);
   p.part_o = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + 2 * ml);
   p.max_pages = shape->max_pages_per_seq;
+  p.max_len = shape->max_pages_per_seq * 16;
   p.packed_cap = packed_cap;
   p.Hq = shape->num_q_heads;
   p.Hkv = shape->num_kv_heads;

@@ -54,7 +54,7 @@ __device__ __forceinline__ SplitRange split_range(const AttnParams& p, int b, in
     sr.t0 = split * p.tps;
     sr.t1 = min(sr.t0 + p.tps, ntile);
   } else if (split < p.nsplit_a) {
-    const int plen = uniform(p.packed_len[b * p.Hkv + g]);
+    const int plen = min(max(uniform(p.packed_len[b * p.Hkv + g]), 0), p.packed_cap);
     sr.packed = true;
     sr.row_lo = 0;
     sr.row_hi = plen;
@@ -62,7 +62,7 @@ __device__ __forceinline__ SplitRange split_range(const AttnParams& p, int b, in
     sr.t0 = split * p.tps;
     sr.t1 = min(sr.t0 + p.tps, ntile);
   } else {
-    const int rs = uniform(p.recent_start[b]);
+    const int rs = min(max(uniform(p.recent_start[b]), 0), N);
     sr.packed = false;
     sr.row_lo = rs;
     sr.row_hi = N;
@@ -164,7 +164,8 @@ __device__ __forceinline__ void attn_partial_bf16(AttnParams p, int work, Bf16Ld
     load_rows((size_t)min(t0w, last) * (kPage * D) + lane_off, ka, va);
     load_rows((size_t)min(t0w + NW, last) * (kPage * D) + lane_off, kb, vb);
   }
-  const int N = uniform(p.seq_lens[b]);
+  // clamped: a length past the call's bound cannot send an index out of the buffers
+  const int N = min(max(uniform(p.seq_lens[b]), 0), p.max_len);
 
   const SplitRange sr = split_range(p, b, g, split, N);
   if (sr.t0 >= sr.t1) {  // workgroup-uniform
@@ -454,7 +455,8 @@ __device__ __forceinline__ void attn_partial_f32(AttnParams p, int work, F32Lds<
   const int i = ig / p.Hkv;
   const int b = uniform(p.seq_ids[i]);
   if (b < 0) return;  // unused slot of the row list
-  const int N = uniform(p.seq_lens[b]);
+  // clamped: a length past the call's bound cannot send an index out of the buffers
+  const int N = min(max(uniform(p.seq_lens[b]), 0), p.max_len);
   const size_t pidx = (size_t)ig * p.nsplit + split;
   const SplitRange sr = split_range(p, b, g, split, N);
   if (sr.t0 >= sr.t1) {

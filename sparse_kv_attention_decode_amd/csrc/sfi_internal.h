@@ -42,6 +42,8 @@ struct AttnParams {
   float* part_l;
   float* part_o;
   int max_pages;
+  int max_len;                 // row lengths are clamped to this (slow: max_seq_len; fast:
+                               // the page table's span), so no index leaves the buffers
   int packed_cap;
   int n_seqs, Hq, Hkv, G;
   int tps, nsplit, nsplit_a;
