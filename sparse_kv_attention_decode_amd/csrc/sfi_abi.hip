@@ -176,6 +176,7 @@ int prep_slow(const sfi_shape* shape, int32_t window, const float* q, const void
   p.Hkv = shape->num_kv_heads;
   p.G = p.Hq / p.Hkv;
   p.tps = sp.tps;
+  p.tps_b = sp.tps;
   p.nsplit = sp.nsplit;
   p.nsplit_a = 0;
   p.fast = 0;
@@ -422,6 +423,7 @@ int prep_fast(const sfi_shape* shape, const float* q, const void* packed_k, cons
   p.Hkv = shape->num_kv_heads;
   p.G = p.Hq / p.Hkv;
   p.tps = sp.tps;
+  p.tps_b = sp.tps_b;
   p.nsplit = sp.nsplit;
   p.nsplit_a = sp.nsplit_a;
   p.fast = 1;

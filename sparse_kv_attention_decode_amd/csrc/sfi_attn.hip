@@ -68,8 +68,8 @@ __device__ __forceinline__ SplitRange split_range(const AttnParams& p, int b, in
     sr.row_hi = N;
     const int first = rs / kPage;
     const int last = (N + kPage - 1) / kPage;
-    sr.t0 = first + (split - p.nsplit_a) * p.tps;
-    sr.t1 = min(sr.t0 + p.tps, last);
+    sr.t0 = first + (split - p.nsplit_a) * p.tps_b;
+    sr.t1 = min(sr.t0 + p.tps_b, last);
   }
   return sr;
 }
@@ -751,14 +751,28 @@ SplitPlan plan_slow(const sfi_shape& s, int n_seqs, int max_seq_len) {
   return sp;
 }
 
+// A paged split stages its page table in LDS before its first K/V request, so it starts
+// later than a packed split, whose first requests go out at once: it gets half the tiles,
+// and the packed splits share the rest of the workgroup target.
 SplitPlan plan_fast(const sfi_shape& s, int n_seqs, int packed_cap, int max_recent) {
   SplitPlan sp;
   const int ta = packed_cap / kPage;
   const int tb = (max_recent + kPage - 1) / kPage + 1;  // +1: the window need not start on a page
-  const int tps = tiles_per_split(s, (long)n_seqs * s.num_kv_heads * (ta + tb), kFastTargetSplits);
-  sp.tps = tps;
-  sp.nsplit_a = (ta + tps - 1) / tps;
-  sp.nsplit = sp.nsplit_a + (tb + tps - 1) / tps;
+  const long units = (long)n_seqs * s.num_kv_heads;
+  const int tps0 = tiles_per_split(s, units * (ta + tb), kFastTargetSplits);
+  const int min_tps = s.dtype == SFI_BF16 ? 4 : 2;
+  const int tps_b = (tps0 + 1) / 2 < min_tps ? min_tps : (tps0 + 1) / 2;
+  const int nsb = (tb + tps_b - 1) / tps_b;
+  long per_unit = units > 0 ? kFastTargetSplits / units : kFastTargetSplits;
+  if (per_unit < 1) per_unit = 1;
+  const long rem = per_unit - nsb > 1 ? per_unit - nsb : 1;
+  long tps_a = (ta + rem - 1) / rem;
+  if (tps_a < tps0) tps_a = tps0;
+  if (tps_a > kMaxTps) tps_a = kMaxTps;
+  sp.tps = (int)tps_a;
+  sp.tps_b = tps_b;
+  sp.nsplit_a = (ta + sp.tps - 1) / sp.tps;
+  sp.nsplit = sp.nsplit_a + nsb;
   return sp;
 }
 

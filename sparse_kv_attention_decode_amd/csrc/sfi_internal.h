@@ -16,6 +16,7 @@ constexpr int kMaxGroup = 16;  // query heads per KV head supported by the kerne
 // first `nsplit_a` splits cover the packed segment and the rest the recent segment.
 struct SplitPlan {
   int tps = 0;
+  int tps_b = 0;  // fast calls: tiles per split of the paged (recent) segment
   int nsplit = 0;
   int nsplit_a = 0;
 };
@@ -47,6 +48,7 @@ struct AttnParams {
   int packed_cap;
   int n_seqs, Hq, Hkv, G;
   int tps, nsplit, nsplit_a;
+  int tps_b;                   // fast only: tiles per split of the paged (recent) segment
   int fast;
   int win;                     // query-window slots per head (1: no window)
   float scale;
