@@ -285,6 +285,39 @@ def test_two_streams_bit_identical_to_one_stream():
         assert torch.equal(a, b)
 
 
+def test_paced_issue_bit_identical_to_unpaced():
+    """Pacing and the Selector lookahead change only when the host queues work.  A three-layer
+    stack issued with no host synchronisation between steps (so the host runs ahead of the
+    GPU) gives bit-identical outputs at every step of every layer, and the same packed
+    buffers at the end, paced with the lookahead as unpaced."""
+    w = get("qwen3_0p6b_8k").replace(steps=70, layers=3, name="paced_3l")
+    ds = [make_layer(w, layer, device="cuda") for layer in range(w.layers)]
+    runs = []
+    for paced in (False, True):
+        eng = Engine(w, ds[0]["flags"], paced=paced, sel_lookahead=2 if paced else 0)
+        lbs = [eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
+               for d in ds]
+        outs = torch.empty((w.steps, w.layers) + tuple(lbs[0].out.shape), device="cuda")
+        eng.stream1.wait_stream(torch.cuda.current_stream())
+        for s in range(w.steps):
+            eng.step(s)
+            with torch.cuda.stream(eng.stream1):
+                for li, lb in enumerate(lbs):
+                    outs[s, li].copy_(lb.out)
+        eng.join()
+        torch.cuda.synchronize()
+        assert eng.paced == paced and (eng.sel_lookahead or 0) == (2 if paced else 0)
+        runs.append((outs, [(lb.packed_k.clone(), lb.packed_pos.clone()) for lb in lbs],
+                     eng.plan.mode.copy()))
+    (o0, p0, mode), (o1, p1, _) = runs
+    assert int(mode[0].sum()) >= 3  # several slow steps, each with its Selector overlap
+    for s in range(w.steps):
+        assert torch.equal(o0[s], o1[s]), s
+    for (k0, q0), (k1, q1) in zip(p0, p1):
+        assert torch.equal(q0, q1)
+        assert torch.equal(_bits(k0), _bits(k1))
+
+
 @pytest.mark.parametrize("batch", [1, 3])
 def test_fast_step_graph_bit_identical_to_eager(batch):
     """Fast steps replayed from the captured two-layer graph, with eager slow steps,
