@@ -318,6 +318,8 @@ def main():
                 traffic = tj.get("bytes_per_call")
         except (OSError, ValueError):
             traffic = None
+    # pacing acts on host-scheduled steps with separate Selector streams only
+    paced_on = bool(eng.paced) and not args.device_control and not args.one_stream
     roof = None
     if fast:
         roof = {"bound": "hbm", "achieved": round(fast["gbs"], 1), "peak": PEAK_HBM_GBS,
@@ -352,8 +354,8 @@ def main():
                    "evidence_window": w.evidence_window,
                    "device_control": bool(args.device_control),
                    "pack": "incremental" if eng.incremental_pack else "full",
-                   "paced": bool(eng.paced) and not args.device_control,
-                   "sel_lookahead": int(eng.sel_lookahead or 0) if eng.paced else 0},
+                   "paced": paced_on,
+                   "sel_lookahead": int(eng.sel_lookahead or 0) if paced_on else 0},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {
