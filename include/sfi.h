@@ -29,7 +29,11 @@
  *   Errors     Host-side checks run before anything is enqueued and return a negative
  *              code with nothing enqueued.  After enqueueing, a launch failure reported
  *              by hipGetLastError is returned as SFI_E_HIP.  Device-side contracts (seq
- *              lengths within bounds, valid pages, indices in range) are trusted.
+ *              lengths within bounds, valid pages, indices in range) are trusted, with
+ *              one safeguard: the attention calls clamp seq_lens to max_seq_len (slow)
+ *              or to the page table's span (fast), packed_len to [0, packed_cap] and
+ *              recent_start to [0, N], so such a value cannot index past their buffers
+ *              (the results for that row are then unspecified).
  *   Layouts    (all row-major, innermost last)
  *     q            f32  [batch, Hq, D]
  *     k_cache      elt  [num_pages, Hkv, 16, D]   page p holds 16 consecutive positions
