@@ -78,6 +78,8 @@ def _parse():
                     help="with pacing, queue layer i's Selector only after layer i's attention "
                          "has finished, with this many attention calls queued behind it (0: off; "
                          "default: 2 for stacks of more than two layers)")
+    ap.add_argument("--sel-streams", type=int, default=2,
+                    help="Selector streams (layers alternate between them)")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue the Selector and pack on the attention stream")
     ap.add_argument("--repeats", type=int, default=20,
@@ -194,10 +196,12 @@ def main():
             if args.device_control:
                 from workload.gen import BOUNDARY_TOKENS, gen_tokens
                 eng = Engine(w, d["flags"], two_streams=not args.one_stream,
+                             sel_streams=args.sel_streams,
                              device_control=True, tokens=gen_tokens(w, d["flags"]),
                              boundary_tokens=BOUNDARY_TOKENS, incremental_pack=inc)
             else:
                 eng = Engine(w, d["flags"], two_streams=not args.one_stream,
+                             sel_streams=args.sel_streams,
                              incremental_pack=inc, paced=pace,
                              sel_lookahead=args.sel_lookahead)
         eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
@@ -349,7 +353,7 @@ def main():
                    "context": w.context, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "top_k": w.top_k, "n_recent": w.n_recent,
-                   "streams": 1 if args.one_stream else 2,
+                   "streams": 1 if args.one_stream else 1 + args.sel_streams,
                    "fast_step_graph": eng.graph is not None,
                    "evidence_window": w.evidence_window,
                    "device_control": bool(args.device_control),
