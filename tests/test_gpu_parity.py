@@ -156,19 +156,30 @@ def test_pack_bit_exact(name):
             assert bool((_bits(pk[g, n:]) == 0).all()) and bool((_bits(pv[g, n:]) == 0).all())
 
 
-@pytest.mark.parametrize("name,win,sliding,inc", [(n, 1, False, None) for n in SMALL] +
-                         [("tiny_fp32_1k", 3, False, None), ("qwen3_0p6b_8k", 4, False, None),
-                          ("qwen3_0p6b_8k", 1, True, None), ("tiny_fp32_1k", 1, False, True),
-                          ("qwen3_0p6b_8k", 1, False, True)])
-def test_trajectory_lockstep(name, win, sliding, inc):
+# Four rows, an odd context and a 600-position recent window: the fast calls split that
+# window into eight half-size paged splits with a ragged last one (the split plan gives paged
+# splits half the tiles of packed ones).
+RAGGED_RECENT = dict(batch=4, context=6000, n_recent=600, top_k=1500, steps=40, refresh_budget=8,
+                     name="ragged_recent_b4")
+
+
+@pytest.mark.parametrize("name,win,sliding,inc,over", [(n, 1, False, None, None) for n in SMALL] +
+                         [("tiny_fp32_1k", 3, False, None, None),
+                          ("qwen3_0p6b_8k", 4, False, None, None),
+                          ("qwen3_0p6b_8k", 1, True, None, None),
+                          ("tiny_fp32_1k", 1, False, True, None),
+                          ("qwen3_0p6b_8k", 1, False, True, None),
+                          pytest.param("qwen3_0p6b_8k", 1, False, True, RAGGED_RECENT,
+                                       id="ragged_recent_b4")])
+def test_trajectory_lockstep(name, win, sliding, inc, over):
     """Every step of the seeded trajectory through the two-stream engine.  Slow steps:
     dense output and the selection (near-tie rule); the oracle then continues with the
     device's selection (teacher forcing) so the two cannot drift.  Fast steps: the
     two-segment output against the oracle's fast step on the same memory.  win > 1 pools
     the Selector's evidence over that many decode queries; sliding moves the recent
     segment to the newest W positions at every step; inc forces the incremental pack (a
-    one-layer engine packs in full by default)."""
-    w = get(name).replace(evidence_window=win, sliding_recent=sliding)
+    one-layer engine packs in full by default); over replaces workload fields."""
+    w = get(name).replace(evidence_window=win, sliding_recent=sliding, **(over or {}))
     d, eng, lb = _setup(w, incremental_pack=inc)
     B = w.batch
     host = [oracle_layer_arrays(d, b) for b in range(B)]
