@@ -156,9 +156,12 @@ def cpu_baseline(w, d0, budget_s: float):
             break
     dt = time.perf_counter() - t0
     n_slow = int(mode[:done].sum())
-    return {"value": done * w.batch / dt, "unit": "layer decode steps/s", "cores": threads,
+    # One layer decode step serves every row of the batch; the sample ran row 0 only, so a
+    # whole step costs batch times the sample's time per step (the unit of `value`).
+    rows = f"row 0 of {w.batch} (time per step scaled by {w.batch})" if w.batch > 1 else "row 0"
+    return {"value": done / (w.batch * dt), "unit": "layer decode steps/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"layer 0, row 0, trajectory steps 0..{done - 1} ({n_slow} slow, "
+            "sample": f"layer 0, {rows}, trajectory steps 0..{done - 1} ({n_slow} slow, "
                       f"{done - n_slow} fast) in {dt:.1f} s, fp64 NumPy"}
 
 

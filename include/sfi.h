@@ -4,7 +4,7 @@
  * The method (pages: "Slow-Fast Inference: Training-Free Inference Acceleration via
  * Within-Sentence Support Stability", cited by summary language and section):
  *   - slow steps run dense attention over the whole history and hand their attention
- *     evidence to the Selector (es "2. Metodología / Pasos Lentos", zh "2.1 慢步骤");
+ *     evidence to the Selector (es "2. Metodología", zh "2.1 慢快推理框架");
  *   - the Selector fuses that evidence f with a cached-statistics prior r as
  *     s = (1-λ) f + λ r, refines the log-scores with soft-NMS and cross-head exclusivity
  *     and takes a Top-K per head (zh "2.2 训练无感的 Selector", nl "De Selector");
@@ -127,8 +127,8 @@ int32_t sfi_packed_cap(const sfi_select_params* params);
 
 /*
  * sfi_key_norms -- cached key statistic ||k_{b,g,j}||_2 for positions [pos_begin, pos_end)
- * of every KV head of the listed rows (the Selector's prior reads key norms kept with the
- * cache, zh "2.2 输入 ... 缓存的统计信息").  Run at prefill / append time.
+ * of every KV head of the listed rows (the Selector's prior is built from statistics kept
+ * with the cache, key norms among them: zh "2.2 训练无感的 Selector").  Run at prefill / append time.
  * key_norm[b][g][j] is written for j in [pos_begin, min(pos_end, N_b)).
  */
 int sfi_key_norms(const sfi_shape* shape, const void* k_cache, const int32_t* block_table,
@@ -138,7 +138,7 @@ int sfi_key_norms(const sfi_shape* shape, const void* k_cache, const int32_t* bl
 
 /*
  * sfi_slow_attn -- dense decode attention of a slow step over all N_b positions of each
- * listed row (es "Pasos Lentos": dense attention over the whole accessible history).
+ * listed row (es "2. Metodología": dense attention over the whole accessible history).
  * Writes out[b] and lse[b]; when `logits` is not NULL also z[b][h][j] for j < N_b, the
  * evidence the Selector reads.  With logits == NULL this is the Full-KV dense step.
  * max_seq_len >= every listed N_b sizes the split of the work (<= max_pages_per_seq*16).
@@ -153,8 +153,8 @@ int sfi_slow_attn(const sfi_shape* shape, const float* q, const void* k_cache,
 /*
  * sfi_slow_attn_window -- a slow step whose evidence comes from a window of `window`
  * queries per head instead of the current query alone (the pages describe the evidence as
- * the attention observed in the slow step's window: es "Metodología / El Selector",
- * zh "2.2 输入").  Slot 0 is the current query; the other slots are earlier decode queries
+ * the attention observed in the slow step's window: es "2. Metodología",
+ * zh "2.2 训练无感的 Selector").  Slot 0 is the current query; the other slots are earlier decode queries
  * chosen by the caller.  Every slot attends to all N_b positions (no causal mask between
  * the slots).  The window's queries of KV head g are extra rows of its group, so K and V
  * are read once for all of them.
@@ -172,8 +172,8 @@ int sfi_slow_attn_window(const sfi_shape* shape, int32_t window, const float* q_
                          float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * sfi_select -- the training-free Selector of a slow step (zh "2.2", fr "2.B",
- * nl "De Selector"), per listed row b and KV head g, at N = N_b:
+ * sfi_select -- the training-free Selector of a slow step (zh "2.2 训练无感的 Selector",
+ * fr "2.B", nl "De Selector"), per listed row b and KV head g, at N = N_b:
  *   f(g,j)  = mean over the G query heads of g of exp(z(h,j) - lse(h))
  *   r(g,j)  = phi_key * phi_pos / sum_{j'<N} phi_key * phi_pos,
  *             phi_key = 1 / max(key_norm, 1e-6), phi_pos = 1 + ln(1 + (N - 1 - j))
@@ -213,7 +213,7 @@ int sfi_select_window(const sfi_shape* shape, const sfi_select_params* params, i
 /*
  * sfi_pack -- gather the sink rows [0, n_sink) and the selected rows sel_idx[b][g][*]
  * (ascending, -1 padded) from the paged cache into the contiguous buffers
- * (zh "2.3 将 Sink 和 Selected Tokens 打包到连续的紧凑缓冲区").  Row i of packed_k/v[b][g]
+ * (zh "2.3 系统级优化": sink and selected rows side by side for sequential reads).  Row i of packed_k/v[b][g]
  * is a byte copy of the cache row at packed_pos[b][g][i]; rows past packed_len[b][g] are
  * zero with packed_pos -1.  sel_idx must hold its valid entries first (as sfi_select
  * writes it).  packed_cap must equal sfi_packed_cap(params).
@@ -228,7 +228,7 @@ int sfi_pack(const sfi_shape* shape, const sfi_select_params* params, const void
  * whose position stays selected keep their slot and are not copied again; newly selected
  * rows are copied into the slots of dropped ones, then past the old end (K_eff grows with
  * N).  The slow steps of one sentence select nearly the same support (the pages' within-
- * sentence stability, nl "Kernobservatie", zh "1 问题背景"), so an update copies a few
+ * sentence stability, nl "Kernobservatie", zh "1. 问题背景"), so an update copies a few
  * rows where a full pack copies all of them.
  * After the call rows [0, packed_len[b][g]) of packed_k/v hold exactly the sink rows and the
  * selected rows, each a byte copy of the cache row at packed_pos; the ORDER of the selected
@@ -252,7 +252,7 @@ int sfi_pack_update(const sfi_shape* shape, const sfi_select_params* params,
                     size_t ws_bytes, void* stream);
 
 /*
- * sfi_fast_attn -- two-segment attention of a fast step (zh "2.3 两段式"): segment A is
+ * sfi_fast_attn -- two-segment attention of a fast step (zh "2.3 系统级优化"): segment A is
  * rows [0, packed_len[b][g]) of the packed buffers, read contiguously; segment B is
  * positions [recent_start[b], N_b) read from the paged cache.  The two partial results
  * are merged by log-sum-exp into out[b] (and lse[b] if not NULL).
@@ -288,7 +288,7 @@ int sfi_decode_attn(const sfi_shape* shape, int32_t window, const float* q,
 
 /*
  * sfi_step_control -- the slow/fast decision of one decode step for every row of the batch,
- * on the device (es "Pasos Lentos", zh "2.1 触发机制": a slow step follows a semantic-
+ * on the device (es "2. Metodología", zh "2.1 慢快推理框架": a slow step follows a semantic-
  * boundary token such as sentence punctuation or a line break, or a spent refresh budget).
  * The state is i32 [3, batch]: rows seq_lens, since_slow, recent_start.  For each row b,
  * from state_in to state_out:
@@ -322,7 +322,8 @@ int sfi_step_control(const sfi_shape* shape, const sfi_select_params* params,
  * sfi_kv_append -- store the K and V rows of the token decoded now at position
  * seq_lens[b] - 1 of each listed row (after sfi_step_control has counted it), and its key
  * norm ||k||_2 into key_norm[b][g][seq_lens[b] - 1] when key_norm is not NULL (the cache
- * statistic the Selector's prior reads, zh "2.2 输入"; the same bits sfi_key_norms stores).
+ * statistic the Selector's prior reads, zh "2.2 训练无感的 Selector"; the same bits
+ * sfi_key_norms stores).
  *   k_new, v_new  elt [batch, Hkv, D]   16-byte aligned
  * The page of the position must already be in block_table (device contract).
  */

@@ -45,8 +45,8 @@ F64 = np.float64
 def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray):
     """Dense GQA decode attention of one query token over rows K, V.
 
-    Slow steps run dense attention over the whole accessible history (es "Pasos Lentos",
-    zh "2.1 慢步骤").  q [Hq, D]; K, V [Hkv, n, D]; query head h reads KV head h // G.
+    Slow steps run dense attention over the whole accessible history (es "2. Metodología",
+    zh "2.1 慢快推理框架").  q [Hq, D]; K, V [Hkv, n, D]; query head h reads KV head h // G.
     Logits z = q·k / sqrt(D) (no positional term: keys are taken as already rotated).
     Returns o [Hq, D], z [Hq, n], lse [Hq], p [Hq, n] (softmax probabilities).
     """
@@ -89,7 +89,7 @@ def schedule(flags: np.ndarray, budget: int) -> np.ndarray:
     """Slow/fast mode of every (sequence, step): 1 = SLOW, 0 = FAST.
 
     Slow steps fire near semantic boundaries or when the reuse budget is spent (es "Pasos
-    Lentos", fr "2.A", zh "2.1 触发机制").  Reading: step 0 is slow (nothing is selected
+    Lentos", fr "2.A", zh "2.1 慢快推理框架").  Reading: step 0 is slow (nothing is selected
     yet); a step is slow when its boundary flag is set or when `budget` fast steps have run
     since the last slow step.
     """
@@ -109,7 +109,7 @@ def schedule(flags: np.ndarray, budget: int) -> np.ndarray:
 
 def boundary_flags(tokens: np.ndarray, boundary_tokens) -> np.ndarray:
     """flag = 1 where the decoded token is one of the semantic-boundary tokens (sentence
-    punctuation, line or paragraph breaks: es "Pasos Lentos", zh "2.1 触发机制")."""
+    punctuation, line or paragraph breaks: es "2. Metodología", zh "2.1 慢快推理框架")."""
     tokens = np.asarray(tokens)
     bset = set(int(t) for t in boundary_tokens)
     out = np.zeros(tokens.shape, np.uint8)
@@ -159,8 +159,7 @@ def step_control(tokens: np.ndarray, boundary_tokens, budget: int, n_stored: int
 def evidence(p: np.ndarray, num_kv_heads: int) -> np.ndarray:
     """Evidence distribution f per KV head.
 
-    The Selector's evidence is the slow step's attention distribution (zh "2.2 证据分布
-    (f)").  Reading: f of KV head g is the mean of the softmax probabilities of its G query
+    The Selector's evidence is the slow step's attention distribution (zh "2.2 训练无感的 Selector").  Reading: f of KV head g is the mean of the softmax probabilities of its G query
     heads, because selection and the compact buffer are per KV head; the mean keeps f a
     distribution.  p [Hq, N] -> f [Hkv, N].
     """
@@ -175,7 +174,7 @@ def window_queries(q_steps: np.ndarray, s: int, window: int) -> np.ndarray:
     step max(0, s - k), k < window.
 
     The pages call the Selector's evidence the attention observed in the slow step's window
-    (es "Metodología / El Selector", zh "2.2 输入") without sizing the window.  Reading:
+    (es "2. Metodología", zh "2.2 训练无感的 Selector") without sizing the window.  Reading:
     the window is the current decode query and the window - 1 decode queries before it;
     before the first decode step there are none, so the first query fills the missing
     slots.  q_steps [S, Hq, D] -> [window, Hq, D]."""
@@ -207,7 +206,7 @@ def key_norms(K: np.ndarray) -> np.ndarray:
 def prior(norms: np.ndarray) -> np.ndarray:
     """Cache-aware structural prior r over positions [0, N) per KV head.
 
-    The pages give the purpose of the two factors only (zh "2.2 先验分布 (r)"): a key-norm
+    The pages give the purpose of the two factors only (zh "2.2 训练无感的 Selector"): a key-norm
     factor that suppresses spuriously high logits of large-norm keys, and a position
     factor that discourages concentration on recent positions.  Reading:
       phi_key(g, j) = 1 / max(||k_{g,j}||, 1e-6)
@@ -226,7 +225,7 @@ def prior(norms: np.ndarray) -> np.ndarray:
 
 def fuse(f: np.ndarray, r: np.ndarray, lam: float) -> np.ndarray:
     """Reverse-KL fusion in closed form, s = (1 - λ) f + λ r (nl "De Selector",
-    zh "2.2 融合目标").  The printed formula is the arithmetic mixture; it minimises
+    zh "2.2 训练无感的 Selector").  The printed formula is the arithmetic mixture; it minimises
     (1-λ) KL(f||s) + λ KL(r||s) over the simplex."""
     return (1.0 - lam) * np.asarray(f, F64) + lam * np.asarray(r, F64)
 
@@ -234,7 +233,7 @@ def fuse(f: np.ndarray, r: np.ndarray, lam: float) -> np.ndarray:
 def candidates(N: int, n_sink: int, n_recent: int) -> Tuple[int, int]:
     """Candidate range C = [n_sink, N - W) of the selected memory (empty if N-W <= n_sink).
     Sink [0, n_sink) and the recent window are always in the fast memory
-    (es "Pasos Rápidos", zh "2.1 快步骤"), so the Selector chooses among the rest."""
+    (es "2. Metodología", zh "2.1 慢快推理框架"), so the Selector chooses among the rest."""
     lo = n_sink
     hi = max(lo, N - n_recent)
     return lo, hi
@@ -251,7 +250,7 @@ class Refined:
 
 def refine(s: np.ndarray, lo: int, hi: int, R: int, alpha_soft: float,
            alpha_cross: float) -> Refined:
-    """Log-score refinement before discretisation (zh "2.2 Log-Score 细化", fr "2.B 2.").
+    """Log-score refinement before discretisation (zh "2.2 训练无感的 Selector", fr "2.B 2.").
 
     The pages name soft-NMS (penalise high-scoring neighbours in the same local region
     within a head) and cross-head exclusivity (discourage different heads from choosing
@@ -300,7 +299,7 @@ def refine(s: np.ndarray, lo: int, hi: int, R: int, alpha_soft: float,
 def refine_greedy(s: np.ndarray, lo: int, hi: int, R: int, alpha_soft: float,
                   alpha_cross: float) -> np.ndarray:
     """Classic greedy Soft-NMS as an alternative reading of the refinement's soft-NMS
-    (zh "2.2 Log-Score 细化": penalise high-scoring neighbours within a head).
+    (zh "2.2 训练无感的 Selector": penalise high-scoring neighbours within a head).
 
     Exclusivity is that of `refine` (owner = the smallest g with the largest unrefined s;
     other heads' scores times 1 - α_cross).  Then, per head, the candidates are taken one
@@ -338,7 +337,7 @@ def refine_greedy(s: np.ndarray, lo: int, hi: int, R: int, alpha_soft: float,
 
 
 def topk(ellp: np.ndarray, lo: int, K: int) -> np.ndarray:
-    """Top-K discretisation (zh "2.2 Top-K 选择").
+    """Top-K discretisation (zh "2.2 训练无感的 Selector").
 
     Per KV head: the K_eff = min(K, |C|) candidates with the largest ℓ'; equal scores go
     to the lower position.  Output ascending positions, padded with -1 to K.
@@ -416,7 +415,7 @@ def select_from_scores(s: np.ndarray, N: int, n_sink: int, n_recent: int, top_k:
 # ---------------------------------------------------------------------------------- pack
 def packed_positions(sel_row: np.ndarray, n_sink: int) -> np.ndarray:
     """Positions of the compact buffer of one KV head: the sink tokens then the selected
-    ones in ascending order (zh "2.3 显存合并的内核")."""
+    ones in ascending order (zh "2.3 系统级优化")."""
     sel_row = np.asarray(sel_row)
     return np.concatenate([np.arange(n_sink, dtype=np.int64), sel_row[sel_row >= 0]])
 
@@ -438,7 +437,7 @@ def pack(K: np.ndarray, V: np.ndarray, sel: np.ndarray, n_sink: int):
 def fast_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, packed_pos: List[np.ndarray],
                    recent_start: int, N: int):
     """Fast step: attention over the compact buffer (sink + selected) and the recent
-    window [recent_start, N) read from the cache (zh "2.3 两段式"; nl "Memory-Coalesced
+    window [recent_start, N) read from the cache (zh "2.3 系统级优化"; nl "Memory-Coalesced
     Kernel").  Computed per segment and merged by log-sum-exp.  The compact buffer's
     positions all lie below recent_start.  Returns o [Hq, D], lse [Hq]."""
     Hq, D = q.shape
@@ -486,7 +485,7 @@ def recent_start_at(N_slow: int, n_sink: int, n_recent: int) -> int:
 
 def recent_start_sliding(N: int, n_sink: int, n_recent: int) -> int:
     """Left edge of a purely sliding recent segment at KV length N: always the newest W
-    positions (the literal reading of the sliding window, es "Pasos Rápidos", nl
+    positions (the literal reading of the sliding window, es "2. Metodología", nl
     "Methodologie").  After a slow step at N0 the positions [N0 - W, N - W) then belong to
     no segment of the fast memory until the next slow step."""
     return max(n_sink, N - n_recent)

@@ -2,7 +2,7 @@
 keeps.
 
 A fast step attends to the sink, the selected rows of the last slow step and the recent
-segment instead of the whole history (es "Pasos Rápidos", zh "2.1 快步骤").  At every fast step
+segment instead of the whole history (es "2. Metodología", zh "2.1 慢快推理框架").  At every fast step
 of a one-layer trajectory this tool also runs the dense attention of the same query and
 reports, per (row, query head):
   * coverage   the dense softmax mass on the positions of the fast memory, sum_{j in M} p_j;

@@ -2,9 +2,9 @@
 // steps (two segments: the packed sink+selected buffer and the recent window in pages).
 //
 // Slow steps attend densely to the whole history and expose their logits as the
-// Selector's evidence (es "2. Metodología / Pasos Lentos", zh "2.1 慢步骤 / 2.2 输入");
+// Selector's evidence (es "2. Metodología", zh "2.1 慢快推理框架" and "2.2 训练无感的 Selector");
 // fast steps attend to the compact contiguous buffer plus the recent tokens read straight
-// from the paged cache (zh "2.3 两段式", nl "Memory-Coalesced Kernel").
+// from the paged cache (zh "2.3 系统级优化", nl "Systeemontwerp en Kernel-optimalisatie").
 //
 // One workgroup of four wavefronts owns one split: a run of 16-row tiles of one (row b,
 // KV head g); the waves take every fourth tile and merge their results in LDS, so each

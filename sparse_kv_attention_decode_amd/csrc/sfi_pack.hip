@@ -1,7 +1,7 @@
 // Compaction of the fast-step memory: sink rows and Selector-chosen rows are copied from
 // the paged cache into one contiguous buffer per (row b, KV head g), so fast steps read
-// them sequentially instead of gathering scattered pages (zh "2.3 显存合并的内核",
-// nl "Memory-Coalesced Kernel", fr "2.C Kernels Mémoire-Coalescés").
+// them sequentially instead of gathering scattered pages (zh "2.3 系统级优化",
+// nl "Systeemontwerp en Kernel-optimalisatie", fr "2.C Optimisations Système").
 //
 // Each wavefront moves a run of consecutive packed rows.  The lanes first look up one row
 // each (selected position, then its page), then every load instruction covers whole rows

@@ -3,9 +3,9 @@
 //
 // The pages trigger a slow step when the model emits a semantic-boundary token (sentence
 // punctuation, a line or paragraph break) or when a refresh budget of fast steps is spent
-// (es "Pasos Lentos", zh "2.1 触发机制", fr "2.A Le Paradigme Lente-Rapide").  The
-// Selector's prior reads key norms kept with the cache (zh "2.2 输入 ... 缓存的统计信息"), so
-// the append also stores the new key's norm.
+// (es "2. Metodología", zh "2.1 慢快推理框架", fr "2.A Le Paradigme Lente-Rapide").
+// The Selector's prior is built from statistics kept with the cache, key norms among them
+// (zh "2.2 训练无感的 Selector"), so the append also stores the new key's norm.
 #include "sfi_device.h"
 #include "sfi_internal.h"
 

@@ -3,14 +3,14 @@ streams of one GPU.
 
 Step s of every listed sequence is SLOW when s == 0, when its boundary flag is set, or when
 `refresh_budget` fast steps have run since its last slow step, and FAST otherwise (es
-"Pasos Lentos", zh "2.1 触发机制").  A slow step runs dense attention and then the Selector
+"Pasos Lentos", zh "2.1 慢快推理框架").  A slow step runs dense attention and then the Selector
 and the pack for that layer; a fast step runs two-segment attention over the packed
 buffer and the recent window.  With an evidence window of w > 1 queries, a slow step's
 dense attention also runs the w - 1 decode queries before the current one (as extra rows
 of each KV head's group, so K and V are read once) and the Selector pools their
 attention with the current query's.
 
-Overlap (es "3. Optimización del Sistema / Pipeline Asíncrono", zh "2.3 异步流水线"): the
+Overlap (es "3. Optimización del Sistema", zh "2.3 系统级优化"): the
 attention of every layer is issued on stream 1; the Selector and pack of layer i are
 issued on a Selector stream after an event recorded behind layer i's slow attention, so
 they run while stream 1 continues with layer i+1.  There are two Selector streams, used by

@@ -7,7 +7,7 @@ span lasts (the within-span stability the pages build on: nl "Kernobservatie", z
 device and measures, for each setting of (K, lambda, alpha_soft, alpha_cross), the fraction
 of the span's topic positions -- those of the G query heads of each KV head that lie among the
 candidates [n_sink, N - W) -- that the KV head's selection contains.  It is a model-free proxy
-for the pages' ablation of the prior fusion and the score refinement (zh "4 实验结果").
+for the pages' ablation of the prior fusion and the score refinement (zh "4. 实验结果").
 
 A setting may also pool the evidence over a window of decode queries.  Then every setting is
 measured at the step window_max - 1 after the span start (spans shorter than that are

@@ -3,14 +3,21 @@ fp64 copies for the oracle, and the comparison rules.
 
 Parity rules (fp32 device arithmetic on bf16/fp32 stored K/V against the fp64 oracle):
   * attention output: per (row, query head) max|o_gpu - o_ref| / max|o_ref| <= 2e-3;
-  * lse: |lse_gpu - lse_ref| <= 1e-4;
+  * lse: |lse_gpu - lse_ref| <= max(1e-4, 1e-5 * sum_j p_j |q|·|k_j| / sqrt(D)), the
+    larger of a flat 1e-4 and the logit bound below propagated through the softmax
+    (check_lse);
   * logits: |z_gpu - z_ref| <= 1e-5 * |q|·|k| / sqrt(D)  (relative to the Cauchy-Schwarz
     scale of the dot product, which a cancelling sum cannot undercut);
   * key norms: relative 1e-6;
   * Top-K on the device's own fused scores: identical index lists;
   * Top-K end to end: the device set may differ from the oracle's only at positions whose
-    oracle log-score is within relative 1e-5 of the K-th one, or where a refinement
-    decision (soft-NMS dominance, head ownership) is within relative 1e-5 in the oracle;
+    oracle refined log-score ln s' is within relative 1e-5 of the K-th one, or where a
+    refinement decision (soft-NMS dominance, head ownership) is within relative 1e-5 of
+    ln s in the oracle.  The allowance is taken on the log-score, where the refinement
+    and the Top-K compare; with |ln s'| around 7-12 it admits score differences of about
+    1e-4 relative, the size of the fp32 logit error (1e-5 of the Cauchy-Schwarz scale)
+    after the softmax.  How many of the differences also lie within relative 1e-5 of the
+    K-th score s' itself is counted and reported;
   * pack: bit-exact.
 """
 from __future__ import annotations
@@ -75,11 +82,13 @@ def check_logits(z_gpu, z_ref, q, K, D):
 
 
 def explain_selection_diff(sel_gpu: np.ndarray, selection: "O.Selection", N: int):
-    """Check that every difference between the device and oracle index sets is a near-tie.
-    Returns (n_diff, n_kth_ties, n_decision_ties)."""
+    """Check that every difference between the device and oracle index sets is a near-tie
+    (the end-to-end rule in the module docstring).  Returns (n_diff, n_kth_ties,
+    n_decision_ties, n_score_ties): the K-th ties are counted on ln s', and n_score_ties
+    counts those of them that are also within relative 1e-5 of the K-th score s'."""
     ref = selection.refined
     lo = selection.lo
-    n_diff = n_kth = n_dec = 0
+    n_diff = n_kth = n_dec = n_score = 0
     for g in range(sel_gpu.shape[0]):
         a = set(int(x) for x in sel_gpu[g] if x >= 0)
         b = set(int(x) for x in selection.sel[g] if x >= 0)
@@ -98,13 +107,26 @@ def explain_selection_diff(sel_gpu: np.ndarray, selection: "O.Selection", N: int
             n_diff += 1
             if np.isfinite(kth) and abs(v - kth) <= TIE_TOL * max(abs(kth), 1e-30):
                 n_kth += 1
+                if abs(np.expm1(v - kth)) <= TIE_TOL:
+                    n_score += 1
             elif ref.dom_margin[g, c] <= TIE_TOL or ref.own_margin[c] <= TIE_TOL:
                 n_dec += 1
             else:
                 raise AssertionError(
                     f"head {g} position {j}: ell'={v:.9g} K-th={kth:.9g} not a near-tie "
                     f"(dom margin {ref.dom_margin[g, c]:.2e}, own margin {ref.own_margin[c]:.2e})")
-    return n_diff, n_kth, n_dec
+    return n_diff, n_kth, n_dec, n_score
+
+
+def oracle_schedule(w, flags, plan=None) -> np.ndarray:
+    """Slow/fast mode [B, S] of a trajectory from the oracle's schedule of the seeded flags.
+    When the engine's host plan is given, it must agree: the tests then follow the oracle's
+    decisions, never the plan's."""
+    flags = flags.cpu().numpy() if torch.is_tensor(flags) else np.asarray(flags)
+    mode = O.schedule(flags, w.refresh_budget)
+    if plan is not None:
+        np.testing.assert_array_equal(plan.mode, mode, err_msg="host plan vs oracle schedule")
+    return mode
 
 
 def oracle_layer_arrays(d: dict, b: int):

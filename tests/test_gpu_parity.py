@@ -11,7 +11,7 @@ from oracle import sfi_oracle as O
 from workload import get
 from workload.gen import make_layer
 from sfi_testlib import (check_lse, check_logits, check_out, explain_selection_diff,
-                         host64, oracle_layer_arrays)
+                         host64, oracle_layer_arrays, oracle_schedule)
 
 pytestmark = pytest.mark.gpu
 
@@ -182,6 +182,7 @@ def test_trajectory_lockstep(name, win, sliding, inc, over):
     w = get(name).replace(evidence_window=win, sliding_recent=sliding, **(over or {}))
     d, eng, lb = _setup(w, incremental_pack=inc)
     B = w.batch
+    omode = oracle_schedule(w, d["flags"], eng.plan)
     host = [oracle_layer_arrays(d, b) for b in range(B)]
     norms = [O.key_norms(K) for _, K, _ in host]
     packed = [None] * B
@@ -193,7 +194,7 @@ def test_trajectory_lockstep(name, win, sliding, inc, over):
         torch.cuda.synchronize()
         N = w.seq_len(s)
         out = host64(lb.out)
-        mode = eng.mode(s)
+        mode = omode[:, s]
         for b in range(B):
             q, K, V = host[b]
             if mode[b]:
@@ -276,24 +277,47 @@ def test_slow_attention_and_select_window(name, win):
             print(name, win, "step", s, "row", b, explain_selection_diff(sel_gpu, sel, N))
 
 
+def _stack_outputs(w, ds, **engine_kw):
+    """Issue every step of a layer stack with no host synchronisation between steps (the
+    host runs ahead of the GPU) and copy each layer's output on the attention stream after
+    every step.  Returns the outputs [S, layers, B, Hq, D], the final Selector and pack
+    state of every layer and the engine."""
+    eng = Engine(w, ds[0]["flags"], **engine_kw)
+    lbs = [eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"]) for d in ds]
+    outs = torch.empty((w.steps, w.layers) + tuple(lbs[0].out.shape), device="cuda")
+    eng.stream1.wait_stream(torch.cuda.current_stream())
+    for s in range(w.steps):
+        eng.step(s)
+        with torch.cuda.stream(eng.stream1):
+            for li, lb in enumerate(lbs):
+                outs[s, li].copy_(lb.out)
+    eng.join()
+    torch.cuda.synchronize()
+    state = [(lb.sel_idx.clone(), lb.packed_pos.clone(), lb.packed_len.clone(),
+              lb.packed_k.clone(), lb.packed_v.clone()) for lb in lbs]
+    return outs, state, eng
+
+
 def test_two_streams_bit_identical_to_one_stream():
-    """Race check of the overlap: the two-stream schedule must give bit-identical results
-    to the same work serialised on one stream."""
-    w = get("qwen3_0p6b_8k").replace(steps=64)
-    outs = []
-    for two in (True, False):
-        d, eng, lb = _setup(w, two_streams=two)
-        res = []
-        for s in range(w.steps):
-            eng.step(s)
-            eng.join()
-            torch.cuda.synchronize()
-            res.append(lb.out.clone())
-            if eng.mode(s)[0]:
-                res.append(lb.sel_idx.clone())
-        outs.append(res)
-    for a, b in zip(*outs):
-        assert torch.equal(a, b)
+    """Race check of the overlap on a three-layer stack issued with no host synchronisation
+    between steps: with two Selector streams layer i's Selector and pack run while stream 1
+    runs the attention of layer i + 1 and of the next steps.  Every step's output of every
+    layer, and the final selections and packed buffers, must be bit-identical to the same
+    work serialised on one stream."""
+    w = get("qwen3_0p6b_8k").replace(steps=70, layers=3, name="overlap_3l")
+    ds = [make_layer(w, layer, device="cuda") for layer in range(w.layers)]
+    o2, st2, eng2 = _stack_outputs(w, ds)
+    assert len(eng2.sel_streams) == 2 and eng2.sel_streams[0] is not eng2.stream1
+    o1, st1, eng1 = _stack_outputs(w, ds, two_streams=False)
+    assert eng1.sel_streams[0] is eng1.stream1
+    mode = oracle_schedule(w, ds[0]["flags"], eng1.plan)
+    assert int(mode[0].sum()) >= 3  # several slow steps, each with its Selector overlap
+    for s in range(w.steps):
+        assert torch.equal(o1[s], o2[s]), s
+    for a, b in zip(st1, st2):
+        for x, y in zip(a, b):
+            assert torch.equal(_bits(x) if x.is_floating_point() else x,
+                               _bits(y) if y.is_floating_point() else y)
 
 
 def test_paced_issue_bit_identical_to_unpaced():
@@ -403,6 +427,7 @@ def test_edge_cases(case):
     _select_and_check(w, d, eng, lb, 0)
     # run the trajectory through the engine and compare every step
     d, eng, lb = _setup(w)
+    omode = oracle_schedule(w, d["flags"], eng.plan)
     q, K, V = oracle_layer_arrays(d, 0)
     norms = O.key_norms(K)
     packed, rstart = None, 0
@@ -410,7 +435,7 @@ def test_edge_cases(case):
         eng.step(s)
         torch.cuda.synchronize()
         N = w.seq_len(s)
-        if eng.mode(s)[0]:
+        if omode[0, s]:
             o, z, lse, p = O.attention(q[s], K[:, :N], V[:, :N])
             sel = O.select(p, norms[:, :N], N, w.num_kv_heads, w.n_sink, w.n_recent, w.top_k,
                            w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam)
@@ -538,11 +563,12 @@ def test_full_size_sampled(name):
             assert torch.equal(_bits(lb.packed_k[b, g, :n]), _bits(d["K"][b, g, idx]))
             assert torch.equal(_bits(lb.packed_v[b, g, :n]), _bits(d["V"][b, g, idx]))
     # first fast step of those rows (if the schedule makes it fast)
+    omode = oracle_schedule(w, d["flags"], eng.plan)
     eng.step(1)
     torch.cuda.synchronize()
     out1 = host64(lb.out)
     for b in rows:
-        if eng.mode(1)[b]:
+        if omode[b, 1]:
             continue
         q, K, V = oracle_layer_arrays(d, b)
         sel_gpu = lb.sel_idx[b].cpu().numpy()
@@ -779,7 +805,7 @@ def test_pack_update_full_size():
     schedule, each leaving exactly sink + selection in the buffer, byte for byte."""
     w = get("qwen3_4b_128k_36l").replace(layers=1)
     d, eng, lb = _setup(w, incremental_pack=True)
-    slow = [s for s in range(w.steps) if eng.mode(s)[0]][:3]
+    slow = [s for s in range(w.steps) if oracle_schedule(w, d["flags"], eng.plan)[0, s]][:3]
     for s in range(slow[-1] + 1):
         eng.step(s)
         if s in slow:
@@ -794,28 +820,34 @@ def test_pack_update_full_size():
 
 def test_full_stack_in_bench_configuration():
     """The benchmark's own launch configuration: all 36 layers of the 128K workload, fast steps
-    replayed from graphs, the incremental pack, two Selector streams.  At a slow step and at the
-    last fast step before the next one (a graph replay), the outputs of layers 0, 17 and 35
-    against the oracle: the dense output, then the fast output on the device's memory (its
-    packed positions as a set and its recent edge)."""
+    replayed from graphs, the incremental pack, two Selector streams.  The schedule and the
+    recent edge come from the oracle (the engine's plan must agree).  At a slow step, for
+    layers 0, 17 and 35: the dense output, the selection against the oracle's Selector (the
+    near-tie rule) and the packed buffer, which must hold exactly the sink rows and that
+    selection, byte for byte.  At the last fast step before the next slow step (a graph
+    replay): the fast output against the oracle's fast step on that memory."""
     w = get("qwen3_4b_128k_36l")
     sample = (0, 17, 35)
-    data, eng = {}, None
+    data, eng, flags = {}, None, None
     for li in range(w.layers):
         d = make_layer(w, li, device="cuda", keep_logical=li in sample)
         if eng is None:
             eng = Engine(w, d["flags"])
+            flags = d["flags"]
         eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
         if li in sample:
             data[li] = {k: d[k] for k in ("q", "K", "V")}
         del d
     eng.enable_graphs()
     assert eng.graph is not None and eng.incremental_pack and len(eng.sel_streams) == 2
-    slow = [s for s in range(w.steps) if eng.mode(s)[0]]
+    omode = oracle_schedule(w, flags, eng.plan)
+    slow = [s for s in range(w.steps) if omode[0, s]]
     i = next(i for i in range(1, len(slow) - 1) if slow[i + 1] - slow[i] >= 3)
     s_slow, s_fast = slow[i], slow[i + 1] - 1
     host = {li: (host64(data[li]["q"][:, 0]), host64(data[li]["K"][0]), host64(data[li]["V"][0]))
             for li in sample}
+    packed = {}
+    rstart = O.recent_start_at(w.seq_len(s_slow), w.n_sink, w.n_recent)
     for s in range(s_fast + 1):
         eng.step(s)
         if s not in (s_slow, s_fast):
@@ -827,11 +859,27 @@ def test_full_stack_in_bench_configuration():
             lb = eng.layers[li]
             q, K, V = host[li]
             if s == s_slow:
-                o = O.attention(q[s], K[:, :N], V[:, :N])[0]
-            else:
+                o, _, _, p = O.attention(q[s], K[:, :N], V[:, :N])
+                check_out(host64(lb.out[0]), o, f"layer {li} step {s}")
+                sel = O.select(p, O.key_norms(K[:, :N]), N, w.num_kv_heads, w.n_sink,
+                               w.n_recent, w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross,
+                               w.lam)
+                sel_gpu = lb.sel_idx[0].cpu().numpy()
+                print(f"layer {li} step {s} selection diff (n, kth, decision, score):",
+                      explain_selection_diff(sel_gpu, sel, N))
+                packed[li] = [O.packed_positions(sel_gpu[g], w.n_sink)
+                              for g in range(w.num_kv_heads)]
                 plen = lb.packed_len[0].cpu().numpy()
                 ppos = lb.packed_pos[0].cpu().numpy()
-                packed = [np.sort(ppos[g, :plen[g]]) for g in range(w.num_kv_heads)]
-                o, _ = O.fast_attention(q[s], K, V, packed, int(eng.plan.recent_start[s, 0]), N)
-            check_out(host64(lb.out[0]), o, f"layer {li} step {s}")
+                for g in range(w.num_kv_heads):
+                    n = len(packed[li][g])
+                    assert plen[g] == n, (li, g)
+                    held = ppos[g, :n]
+                    assert sorted(held.tolist()) == packed[li][g].tolist(), (li, g)
+                    idx = torch.from_numpy(held.astype(np.int64)).cuda()
+                    assert torch.equal(_bits(lb.packed_k[0, g, :n]), _bits(data[li]["K"][0, g, idx]))
+                    assert torch.equal(_bits(lb.packed_v[0, g, :n]), _bits(data[li]["V"][0, g, idx]))
+            else:
+                o, _ = O.fast_attention(q[s], K, V, packed[li], rstart, N)
+                check_out(host64(lb.out[0]), o, f"layer {li} step {s}")
     print(f"checked slow step {s_slow} and graph-replayed fast step {s_fast}")

@@ -40,7 +40,7 @@ def test_greedy_soft_nms_against_one_pass(name, top_k):
     d = make_layer(w, 0, device=dev)
     eng = Engine(w, d["flags"], dbg_scores=True)
     lb = eng.add_layer(d["k_cache"], d["v_cache"], d["block_table"], d["q"])
-    mode = eng.plan.mode[0]
+    mode = O.schedule(d["flags"].cpu().numpy(), w.refresh_budget)[0]
     slow_steps = [s for s in range(w.steps) if mode[s]][:5]
     z = torch.empty(1, w.num_q_heads, eng.stride, device=dev)
     lse = torch.empty(1, w.num_q_heads, device=dev)

@@ -204,6 +204,21 @@ def test_evidence_is_distribution():
     np.testing.assert_allclose(O.evidence(p, 8), p, atol=0)
 
 
+def test_evidence_grouping_worked_example():
+    """Two KV heads of two query heads each: each KV head's f is the mean of its own query
+    heads' rows (h div G), evaluated by hand in the golden file.  An interleaved grouping
+    (h mod Hkv) gives different values there, so it fails this pin."""
+    g = json.load(open(os.path.join(GOLDEN, "evidence_grouping.json")))
+    p = np.array(g["p"])
+    f = O.evidence(p, g["num_kv_heads"])
+    np.testing.assert_allclose(f, g["f"], rtol=0, atol=1e-15)
+    assert np.abs(f - np.array(g["f_interleaved_wrong"])).max() > 0.1
+    # the same grouping when the evidence is pooled over a window of two slots
+    P = np.stack([p, p[g["window_slot1_head_order"]]])
+    fw = O.window_evidence(P, g["num_kv_heads"])
+    np.testing.assert_allclose(fw, g["f_window2"], rtol=0, atol=1e-15)
+
+
 def test_window_evidence_worked_example():
     """Two slots, two query heads of one KV head, three positions, summed by hand:
     f = (0.5+0.2+1+0, 0.25+0.3+0+0, 0.25+0.5+0+1) / 4."""

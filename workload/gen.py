@@ -21,7 +21,7 @@ Recipe (one attention layer, one sequence b; per layer an independent stream):
   * paging      physical pages are a seeded random permutation, so paged reads scatter.
 
 The attention support this produces is stable within a span and moves at flagged steps,
-the behaviour the pages describe for sentences ("Kernobservatie", "核心观察").
+the behaviour the pages describe for sentences (nl "Kernobservatie", zh "1. 问题背景").
 
 Random numbers come from torch's generators on the device where the tensors are made
 (Philox on a GPU, Mersenne Twister on the CPU), so the same seed gives different values
