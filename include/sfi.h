@@ -16,7 +16,8 @@
  *   Memory     Every pointer argument except `shape`/`params` is DEVICE memory owned by
  *              the caller.  The library never allocates, frees or retains memory and
  *              keeps no mutable global state; it is safe to call from several threads on
- *              different streams.
+ *              different streams.  The one exception is sfi_fast_attn_noalloc, whose
+ *              scratch is a device array inside the library (see there).
  *   Streams    `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *              work and never synchronise; buffers must stay alive until the stream has
  *              passed the work.
@@ -265,6 +266,27 @@ int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
                   const int32_t* recent_start, const int32_t* seq_lens,
                   const int32_t* seq_ids, int32_t n_seqs, int32_t max_recent, float* out,
                   float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sfi_fast_attn_noalloc -- sfi_fast_attn for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as sfi_fast_attn, without the workspace: the split
+ * partials go to a device array inside the library, SFI_NOALLOC_SCRATCH_BYTES per GPU,
+ * which each GPU holds from the library's load until the process ends.  A call whose
+ * workspace, sfi_fast_attn_ws(shape, n_seqs, packed_cap, max_recent), exceeds it returns
+ * SFI_E_WORKSPACE with nothing enqueued.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race on it and must be serialised by the caller.  The array
+ * needs no initialisation; what a call leaves there is never read by a later call.  The
+ * calling thread's current device must be the device of `stream` (SFI_E_ARG otherwise).
+ */
+#define SFI_NOALLOC_SCRATCH_BYTES (8u << 20)
+int sfi_fast_attn_noalloc(const sfi_shape* shape, const float* q, const void* packed_k,
+                          const void* packed_v, const int32_t* packed_len, int32_t packed_cap,
+                          const void* k_cache, const void* v_cache, const int32_t* block_table,
+                          const int32_t* recent_start, const int32_t* seq_lens,
+                          const int32_t* seq_ids, int32_t n_seqs, int32_t max_recent,
+                          float* out, float* lse, void* stream);
 
 /*
  * sfi_decode_attn -- the attention of a whole decode step in one partial launch and one

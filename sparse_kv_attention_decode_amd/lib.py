@@ -24,7 +24,8 @@ EXPORTS = ["sfi_abi_version", "sfi_status_str", "sfi_slow_attn_ws", "sfi_fast_at
            "sfi_select_ws", "sfi_packed_cap", "sfi_key_norms", "sfi_slow_attn", "sfi_select",
            "sfi_pack", "sfi_fast_attn", "sfi_slow_attn_window_ws", "sfi_select_window_ws",
            "sfi_slow_attn_window", "sfi_select_window", "sfi_step_control", "sfi_kv_append",
-           "sfi_decode_attn_ws", "sfi_decode_attn", "sfi_pack_update_ws", "sfi_pack_update"]
+           "sfi_decode_attn_ws", "sfi_decode_attn", "sfi_pack_update_ws", "sfi_pack_update",
+           "sfi_fast_attn_noalloc"]
 
 
 class SfiShape(ctypes.Structure):
@@ -86,6 +87,8 @@ _SIGS = {
                                        _P, _I64, _P, _SZ, _P]),
     "sfi_fast_attn": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32,
                                      _I32, _P, _P, _P, _SZ, _P]),
+    "sfi_fast_attn_noalloc": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P,
+                                             _I32, _I32, _P, _P, _P]),
 }
 
 
@@ -251,6 +254,17 @@ def sfi_fast_attn(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache,
                               _ptr(seq_ids), n_seqs, max_recent, _ptr(out), _ptr(lse),
                               _ptr(ws), ws_bytes, _stream(stream))
     _check("sfi_fast_attn", rc)
+
+
+def sfi_fast_attn_noalloc(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache,
+                          v_cache, block_table, recent_start, seq_lens, seq_ids, n_seqs,
+                          max_recent, out, lse, stream=None) -> None:
+    rc = load().sfi_fast_attn_noalloc(ctypes.byref(shape), _ptr(q), _ptr(packed_k),
+                                      _ptr(packed_v), _ptr(packed_len), packed_cap,
+                                      _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                      _ptr(recent_start), _ptr(seq_lens), _ptr(seq_ids), n_seqs,
+                                      max_recent, _ptr(out), _ptr(lse), _stream(stream))
+    _check("sfi_fast_attn_noalloc", rc)
 
 
 def sfi_step_control(shape, params, refresh_budget, token_ids, boundary_tokens, n_boundary,

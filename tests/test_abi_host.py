@@ -216,6 +216,32 @@ def test_fast_attn_validation():
     assert _fast(s, n=0) == L.SFI_OK
 
 
+def _fast_noalloc(shape, **over):
+    a = dict(q=FAKE, pk=FAKE, pv=FAKE, pl=FAKE, cap=144, k=FAKE, v=FAKE, bt=FAKE, rs=FAKE,
+             sl=FAKE, ids=FAKE, n=1, maxrec=100, out=FAKE, lse=None)
+    a.update(over)
+    return L.load().sfi_fast_attn_noalloc(
+        ctypes.byref(shape), a["q"], a["pk"], a["pv"], a["pl"], a["cap"], a["k"], a["v"],
+        a["bt"], a["rs"], a["sl"], a["ids"], a["n"], a["maxrec"], a["out"], a["lse"], None)
+
+
+def test_fast_attn_noalloc_validation():
+    """The allocation-free fast call rejects what sfi_fast_attn rejects, and calls whose split
+    partials exceed its fixed scratch array, before touching the device."""
+    s = _shape()
+    assert _fast_noalloc(s, rs=None) == L.SFI_E_ARG
+    assert _fast_noalloc(s, cap=100) == L.SFI_E_CAPACITY
+    assert _fast_noalloc(s, maxrec=-1) == L.SFI_E_ARG
+    assert _fast_noalloc(s, pv=MIS) == L.SFI_E_ALIGN
+    assert _fast_noalloc(s, n=3) == L.SFI_E_ARG            # more rows than the batch
+    assert _fast_noalloc(s, n=0) == L.SFI_OK
+    # 64 rows of 16 KV heads with G = 16: the partials outgrow the 8 MiB array
+    big = _shape(batch=64, num_q_heads=256, num_kv_heads=16, max_pages_per_seq=8192)
+    need = L.sfi_fast_attn_ws(big, 64, 65536, 4096)
+    assert need > 8 << 20
+    assert _fast_noalloc(big, n=64, cap=65536, maxrec=4096) == L.SFI_E_WORKSPACE
+
+
 def test_key_norms_validation():
     s = _shape()
     lib = L.load()
