@@ -105,7 +105,6 @@ struct Bf16Lds {
   float m[kAttnWaves][kMaxG], l[kAttnWaves][kMaxG];
   float o[kAttnWaves - 1][kMaxG][D];
   int32_t page[kMaxTilesPerSplit];
-  u32x4_t q[3][D / 32][kWave];  // query operand: hi, mid, lo terms
 };
 
 // Split `work` of the call described by p (one workgroup).
@@ -118,7 +117,6 @@ __device__ __forceinline__ void attn_partial_bf16(AttnParams p, int work, Bf16Ld
   auto& sm_l = lds.l;
   auto& sm_o = lds.o;
   auto& sm_page = lds.page;
-  auto& sm_q = lds.q;
   const int lane = threadIdx.x & 63;
   // Wave-uniform by construction; readfirstlane lets the compiler keep tile indices and
   // page-table reads scalar (s_load, counted by lgkmcnt) instead of vector loads whose
@@ -135,6 +133,20 @@ __device__ __forceinline__ void attn_partial_bf16(AttnParams p, int work, Bf16Ld
   const int qd = lane >> 4;
   const size_t pidx = (size_t)ig * p.nsplit + split;
   const int lane_off = r * D + 8 * qd;
+
+  // Query of head r, dims 32c + 8qd .. +8 for c < NC: requested before any K/V tile, so it
+  // is the first load of the wave to return (the wave's loads return in order) and the
+  // first tile's products never wait for it behind the tile requests of the whole chip.
+  float4 qraw[2 * NC];
+  {
+    const bool hv = r < p.G;
+    const float* qrow = p.q + ((size_t)b * p.Hq + (size_t)g * p.G + (hv ? r : 0)) * D + 8 * qd;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qraw[2 * c] = *reinterpret_cast<const float4*>(qrow + 32 * c);
+      qraw[2 * c + 1] = *reinterpret_cast<const float4*>(qrow + 32 * c + 4);
+    }
+  }
 
   const bool packed = p.fast && split < p.nsplit_a;
   const uint16_t* kbase;
@@ -201,36 +213,21 @@ __device__ __forceinline__ void attn_partial_bf16(AttnParams p, int work, Bf16Ld
     load_tile(min(wt0 + NW, sr.t1 - 1), kb, vb);
   }
 
-  // Query operand, in LDS: lane (qd, r) of every wave reads head r, dims 32c + 8qd .. +8,
-  // pre-scaled by 1/sqrt(D) and split into three bf16 terms.  Wave 0 prepares it.
-  if (wave == 0) {
-    const bool hv = r < p.G;
-    const float* qrow = p.q + ((size_t)b * p.Hq + (size_t)g * p.G + (hv ? r : 0)) * D;
+  // Query operand of head r (lane (qd, r)), pre-scaled by 1/sqrt(D) and split into three
+  // bf16 terms, held in registers for the whole split.  Rows past the group are zero.
+  u32x4_t qh[NC], qm[NC], ql[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float x[8];
-      if (hv) {
-        const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * c + 8 * qd);
-        const float4 bq = *reinterpret_cast<const float4*>(qrow + 32 * c + 8 * qd + 4);
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = bq.x; x[5] = bq.y; x[6] = bq.z; x[7] = bq.w;
-      } else {
+  for (int c = 0; c < NC; ++c) {
+    float x[8] = {qraw[2 * c].x, qraw[2 * c].y, qraw[2 * c].z, qraw[2 * c].w,
+                  qraw[2 * c + 1].x, qraw[2 * c + 1].y, qraw[2 * c + 1].z, qraw[2 * c + 1].w};
+    float h8[8], m8[8], l8[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = 0.f;
-      }
-      float h8[8], m8[8], l8[8];
+    for (int j = 0; j < 8; ++j) split3(r < p.G ? x[j] * p.scale : 0.f, h8[j], m8[j], l8[j]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) split3(x[j] * p.scale, h8[j], m8[j], l8[j]);
-      u32x4_t qh, qm, ql;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        qh[w] = pack_hi16(h8[2 * w], h8[2 * w + 1]);
-        qm[w] = pack_hi16(m8[2 * w], m8[2 * w + 1]);
-        ql[w] = pack_hi16(l8[2 * w], l8[2 * w + 1]);
-      }
-      sm_q[0][c][lane] = qh;
-      sm_q[1][c][lane] = qm;
-      sm_q[2][c][lane] = ql;
+    for (int w = 0; w < 4; ++w) {
+      qh[c][w] = pack_hi16(h8[2 * w], h8[2 * w + 1]);
+      qm[c][w] = pack_hi16(m8[2 * w], m8[2 * w + 1]);
+      ql[c][w] = pack_hi16(l8[2 * w], l8[2 * w + 1]);
     }
   }
   // Selection matrices E_e[k][n] = (k == n + 16 e), lane (qd, r): k = 8qd + j, n = r.
@@ -250,7 +247,6 @@ __device__ __forceinline__ void attn_partial_bf16(AttnParams p, int work, Bf16Ld
 #pragma unroll
   for (int t = 0; t < NT; ++t) O[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  __syncthreads();
 
   // One tile step: request the wave's next tile t + NW into (kpf, vpf), then consume
   // tile t from (kr, vr).  The two buffers swap roles by unrolling the loop twice, so no
@@ -261,17 +257,6 @@ __device__ __forceinline__ void attn_partial_bf16(AttnParams p, int work, Bf16Ld
   auto step = [&](auto prefetch, int t, u32x4_t* kr, u32x4_t* vr, u32x4_t* kpf,
                   u32x4_t* vpf) {
     if constexpr (decltype(prefetch)::value) load_tile(min(t + NW, sr.t1 - 1), kpf, vpf);
-    // Read the query operand from LDS every tile (an opaque lane index keeps the reads
-    // inside the loop, so the 48 registers they need are not held across it).
-    int ql_idx = lane;
-    asm volatile("" : "+v"(ql_idx));
-    u32x4_t qh[NC], qm[NC], ql[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      qh[c] = sm_q[0][c][ql_idx];
-      qm[c] = sm_q[1][c][ql_idx];
-      ql[c] = sm_q[2][c][ql_idx];
-    }
     const int pos0 = t * kPage;
     const bool full = pos0 >= sr.row_lo && pos0 + kPage <= sr.row_hi;
     if (!full) {
