@@ -339,6 +339,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_assign(UpdArgs a) {
   __shared__ int sh[5];
   __shared__ int l_pos[kChunk];
   __shared__ int l_slot[kChunk];
+  __shared__ int l_page[kChunk];
   const Ig r = ig_of(a, blockIdx.x, a.nc_sel);
   if (r.b < 0) return;
   if (threadIdx.x == 0) {
@@ -400,17 +401,22 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_assign(UpdArgs a) {
   }
   if (threadIdx.x == 0 && r.chunk == 0) a.plen[r.bg] = a.n_sink + keff;
   __syncthreads();
+  // physical page of every listed row, staged once: the copy loop below then issues its
+  // row loads without waiting for a block-table load first
+  const int32_t* btb = a.bt + (size_t)r.b * a.max_pages;
+  for (int e = threadIdx.x; e < (int)tot; e += kChunkThreads)
+    l_page[e] = l_pos[e] >= 0 ? btb[l_pos[e] / kPage] : 0;
+  __syncthreads();
   // copy the rows listed in LDS (and, for a rebuild, the sink rows in chunk 0): LPR lanes
   // per row, 16 bytes per lane
   constexpr int RPB = kChunkThreads / LPR;
   const int sub = threadIdx.x % LPR, rsub = threadIdx.x / LPR;
   const size_t rb = (size_t)a.row_bytes;
-  const int32_t* btb = a.bt + (size_t)r.b * a.max_pages;
   const int n_sink_copy = (rebuild && r.chunk == 0) ? a.n_sink : 0;
   const int nl = (int)tot + n_sink_copy;
   // kCopyBatch rows per lane group are loaded before any of them is stored (a rebuild
   // copies a whole chunk)
-  constexpr int kCopyBatch = 4;
+  constexpr int kCopyBatch = 8;
   for (int e0 = rsub; e0 < nl; e0 += kCopyBatch * RPB) {
     u32x4_t kv[kCopyBatch], vv[kCopyBatch];
     size_t dst[kCopyBatch];
@@ -426,7 +432,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_assign(UpdArgs a) {
           ppos[pos] = pos;
           if (in_map(a, pos)) map[pos] = pos;
         }
-        const int page = btb[pos / kPage];
+        const int page = sink ? btb[pos / kPage] : l_page[e];
         const size_t src =
             (((size_t)page * a.Hkv + r.g) * kPage + pos % kPage) * rb + 16 * sub;
         dst[u] = (r.bg * a.cap + slot) * rb + 16 * sub;
