@@ -90,6 +90,11 @@ def _parse():
     ap.add_argument("--evidence-window", type=int, default=None,
                     help="decode queries pooled into the Selector's evidence at a slow step "
                          "(default: the workload's, 1)")
+    ap.add_argument("--lambda-clip", type=float, default=None,
+                    help="adaptive fusion weight min(lambda_clip, H(f)/ln N) per (row, KV head) "
+                         "instead of the workload's fixed lambda")
+    ap.add_argument("--nms-greedy", action="store_true",
+                    help="greedy soft-NMS in the Selector instead of the one-pass reading")
     ap.add_argument("--pack", choices=("auto", "full", "incremental"), default="auto",
                     help="full: re-pack every selected row at each slow step (sfi_pack); "
                          "incremental: copy only the newly selected ones (sfi_pack_update); "
@@ -188,6 +193,10 @@ def main():
     pace = {"auto": None, "on": True, "off": False}[args.pace]
     if args.evidence_window is not None:
         w = w.replace(evidence_window=args.evidence_window)
+    if args.lambda_clip is not None:
+        w = w.replace(lambda_clip=args.lambda_clip)
+    if args.nms_greedy:
+        w = w.replace(nms_greedy=True)
     steps = args.steps if args.steps is not None else w.steps
     t_setup = time.perf_counter()
     d0 = None
@@ -359,6 +368,8 @@ def main():
                    "streams": 1 if args.one_stream else 1 + args.sel_streams,
                    "fast_step_graph": eng.graph is not None,
                    "evidence_window": w.evidence_window,
+                   "lambda_clip": w.lambda_clip if w.lambda_clip >= 0 else None,
+                   "nms_greedy": bool(w.nms_greedy),
                    "device_control": bool(args.device_control),
                    "pack": "incremental" if eng.incremental_pack else "full",
                    "paced": paced_on,

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SFI_ABI_VERSION 6
+#define SFI_ABI_VERSION 7
 
 enum sfi_status {
   SFI_OK = 0,
@@ -97,6 +97,14 @@ typedef struct {
   float lambda;         /* fusion weight of the prior, in [0, 1]                          */
   float alpha_soft;     /* soft-NMS penalty: a dominated score is scaled by 1 - alpha     */
   float alpha_cross;    /* exclusivity penalty: a non-owner score is scaled by 1 - alpha  */
+  float lambda_clip;    /* < 0: the fusion weight is `lambda`.  In [0, 1]: it adapts per
+                           (row, KV head) to the evidence, lambda_g = min(lambda_clip,
+                           H(f_g) / ln N) with H the entropy of f_g, and `lambda` is unused */
+  int32_t nms_greedy;   /* 0: one-pass soft-NMS (dominance on the unrefined score).  1: greedy
+                           soft-NMS: per head, the candidate with the largest current score
+                           (lower position on ties) is taken and keeps that score; every
+                           untaken candidate within nms_radius is scaled by 1 - alpha_soft;
+                           repeated until all are taken; Top-K of the taken scores */
 } sfi_select_params;
 
 /* ABI version (SFI_ABI_VERSION) and a static description of a status code. */
@@ -179,8 +187,13 @@ int sfi_slow_attn_window(const sfi_shape* shape, int32_t window, const float* q_
  *   r(g,j)  = phi_key * phi_pos / sum_{j'<N} phi_key * phi_pos,
  *             phi_key = 1 / max(key_norm, 1e-6), phi_pos = 1 + ln(1 + (N - 1 - j))
  *   s       = (1 - lambda) f + lambda r                       (the closed-form fusion)
+ *             with lambda_clip >= 0: lambda_g = min(lambda_clip, H(f_g) / ln N) per (b, g),
+ *             H(f) = -sum_j f_j ln f_j (0 ln 0 = 0); lambda_g = 0 when N = 1 (the ablation
+ *             of the pages names the fusion knob lambda_clip, zh "4. 实验结果")
  *   on candidates C = [n_sink, N - n_recent):
  *   s'      = s * (1-alpha_soft)^dom * (1-alpha_cross)^exc   (log-score refinement)
+ *             (with nms_greedy = 1 the soft-NMS factor is the greedy one described at
+ *             sfi_select_params instead of (1-alpha_soft)^dom)
  *             dom: a candidate within nms_radius in the same head has a strictly larger s
  *             exc: g is not the owner of j (the head with the largest s at j, lowest g
  *                  on ties)

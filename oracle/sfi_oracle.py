@@ -27,8 +27,11 @@ Parity status of each function:
       of the two factors is a reading the pages do not fix -- parity unpinned for the form.
   refine: special cases pinned (identity at α=0, local maxima at α_soft=1, ownership at
       α_cross=1); intermediate α -- parity unpinned beyond those cases.
-  refine_greedy (an alternative reading, host only): pinned by a worked example, a plain
+  refine_greedy (an alternative reading): pinned by a worked example, a plain
       quadratic simulation, its reductions (α_soft = 0 or R = 0) and hard NMS at α_soft = 1.
+  adaptive_lambda, fuse_per_head (the clipped adaptive fusion weight, a reading): pinned by
+      hand-worked entropies, the point-mass and uniform limits, λclip = 0 (evidence only)
+      and the per-head fusion staying a distribution.
 """
 from __future__ import annotations
 
@@ -230,6 +233,33 @@ def fuse(f: np.ndarray, r: np.ndarray, lam: float) -> np.ndarray:
     return (1.0 - lam) * np.asarray(f, F64) + lam * np.asarray(r, F64)
 
 
+def adaptive_lambda(f: np.ndarray, lambda_clip: float) -> np.ndarray:
+    """Per-KV-head fusion weight of the clipped, adaptive reading of the prior fusion.
+
+    The pages name the prior fusion's knob λclip in the Selector ablation (zh "4. 实验结果")
+    and give no rule for it.  Reading: the weight of the prior follows how little the
+    evidence says, measured by the normalised entropy of f, and is clipped at λclip:
+      λ_g = min(λclip, H(f_g) / ln N),   H(f) = -sum_j f_j ln f_j  (0 ln 0 = 0),
+    so a flat evidence (H = ln N) leans on the prior up to λclip and a point mass (H = 0)
+    keeps the evidence alone.  With N = 1 there is nothing to weigh and λ_g = 0.
+    f [Hkv, N] -> λ [Hkv]."""
+    f = np.asarray(f, F64)
+    Hkv, N = f.shape
+    if N <= 1:
+        return np.zeros(Hkv, F64)
+    t = np.zeros_like(f)
+    pos = f > 0
+    t[pos] = f[pos] * np.log(f[pos])
+    H = -t.sum(axis=1)
+    return np.minimum(float(lambda_clip), H / math.log(N))
+
+
+def fuse_per_head(f: np.ndarray, r: np.ndarray, lam: np.ndarray) -> np.ndarray:
+    """The closed-form fusion with one weight per KV head: s_g = (1 - λ_g) f_g + λ_g r_g."""
+    lam = np.asarray(lam, F64)[:, None]
+    return (1.0 - lam) * np.asarray(f, F64) + lam * np.asarray(r, F64)
+
+
 def candidates(N: int, n_sink: int, n_recent: int) -> Tuple[int, int]:
     """Candidate range C = [n_sink, N - W) of the selected memory (empty if N-W <= n_sink).
     Sink [0, n_sink) and the recent window are always in the fast memory
@@ -368,27 +398,33 @@ class Selection:
 
 def select(p: np.ndarray, norms: np.ndarray, N: int, num_kv_heads: int, n_sink: int,
            n_recent: int, top_k: int, R: int, alpha_soft: float, alpha_cross: float,
-           lam: float) -> Selection:
+           lam: float, lambda_clip: Optional[float] = None) -> Selection:
     """The whole Selector of one slow step: evidence, prior, fusion, refinement, Top-K.
-    p [Hq, N] slow-step softmax probabilities; norms [Hkv, N] cached key norms."""
+    p [Hq, N] slow-step softmax probabilities; norms [Hkv, N] cached key norms.  With
+    lambda_clip (not None) the fusion weight is adaptive_lambda per KV head and lam is
+    not used."""
     return select_from_evidence(evidence(p, num_kv_heads), norms, N, n_sink, n_recent, top_k,
-                                R, alpha_soft, alpha_cross, lam)
+                                R, alpha_soft, alpha_cross, lam, lambda_clip)
 
 
 def select_window(P: np.ndarray, norms: np.ndarray, N: int, num_kv_heads: int, n_sink: int,
                   n_recent: int, top_k: int, R: int, alpha_soft: float, alpha_cross: float,
-                  lam: float) -> Selection:
+                  lam: float, lambda_clip: Optional[float] = None) -> Selection:
     """The Selector with evidence pooled over a window of queries, P [window, Hq, N]."""
     return select_from_evidence(window_evidence(P, num_kv_heads), norms, N, n_sink, n_recent,
-                                top_k, R, alpha_soft, alpha_cross, lam)
+                                top_k, R, alpha_soft, alpha_cross, lam, lambda_clip)
 
 
 def select_from_evidence(f: np.ndarray, norms: np.ndarray, N: int, n_sink: int,
                          n_recent: int, top_k: int, R: int, alpha_soft: float,
-                         alpha_cross: float, lam: float) -> Selection:
+                         alpha_cross: float, lam: float,
+                         lambda_clip: Optional[float] = None) -> Selection:
     """Prior, fusion, refinement and Top-K on given evidence f [Hkv, N]."""
     r = prior(norms[:, :N])
-    s = fuse(f, r, lam)
+    if lambda_clip is None:
+        s = fuse(f, r, lam)
+    else:
+        s = fuse_per_head(f, r, adaptive_lambda(f, lambda_clip))
     lo, hi = candidates(N, n_sink, n_recent)
     ref = refine(s, lo, hi, R, alpha_soft, alpha_cross)
     sel = topk(ref.ellp, lo, top_k)

@@ -31,6 +31,8 @@ int check_params(const sfi_select_params* p) {
   if (!(p->lambda >= 0.f && p->lambda <= 1.f)) return SFI_E_ARG;
   if (!(p->alpha_soft >= 0.f && p->alpha_soft <= 1.f)) return SFI_E_ARG;
   if (!(p->alpha_cross >= 0.f && p->alpha_cross <= 1.f)) return SFI_E_ARG;
+  if (!(p->lambda_clip < 0.f || p->lambda_clip <= 1.f)) return SFI_E_ARG;  // NaN fails too
+  if (p->nms_greedy != 0 && p->nms_greedy != 1) return SFI_E_ARG;
   if ((int64_t)p->n_sink + p->top_k > (1 << 28)) return SFI_E_CAPACITY;
   return SFI_OK;
 }
@@ -91,7 +93,7 @@ size_t sfi_select_ws(const sfi_shape* shape, const sfi_select_params* params, in
   if (check_shape(shape) != SFI_OK || check_params(params) != SFI_OK ||
       check_rows(shape, n_seqs, max_seq_len) != SFI_OK || max_seq_len > sfi::kSelectMaxLen)
     return 0;
-  return sfi::select_layout(*shape, n_seqs, max_seq_len).total;
+  return sfi::select_layout(*shape, n_seqs, max_seq_len, params->nms_greedy != 0).total;
 }
 
 int sfi_key_norms(const sfi_shape* shape, const void* k_cache, const int32_t* block_table,

@@ -70,12 +70,12 @@ struct SelectLayout {
   int nchunk = 0;        // prior-normaliser chunks per (row, KV head)
   int64_t kstride = 0;   // key slots per (row, KV head)
   int nslice = 0;        // top-K slices of 4096 candidates per (row, KV head)
-  size_t zpart_off = 0, keys_off = 0, hist_off = 0, state_off = 0, above_off = 0,
+  size_t zpart_off = 0, hpart_off = 0, taken_off = 0, ready_off = 0, keys_off = 0, hist_off = 0, state_off = 0, above_off = 0,
          sloff_off = 0, ckey_off = 0, cidx_off = 0, total = 0;
 };
 // Longest KV length the Selector takes: 1024 top-K slices of 4096 candidates.
 constexpr int kSelectMaxLen = 1 << 22;
-SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len);
+SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len, bool greedy);
 // LDS of one scoring block: s for every KV head over `tile` positions plus a halo of
 // nms_radius on each side, the prior normalisers and the lse of every query head.
 size_t score_lds_bytes(int num_kv_heads, int num_q_heads, int nms_radius, int tile);

@@ -5,7 +5,9 @@
 //   evidence  f(g,j) = (1/G) sum_h exp(z(h,j) - lse(h))           (slow-step softmax)
 //   prior     r(g,j) = phi_key * phi_pos / Z_g,  phi_key = 1/max(||k||, 1e-6),
 //             phi_pos = 1 + ln(1 + (N-1-j)),  Z_g = sum over [0, N)
-//   fusion    s = (1 - lambda) f + lambda r                        (closed form)
+//   fusion    s = (1 - lambda) f + lambda r                        (closed form); with
+//             lambda_clip >= 0 the weight adapts per (b, g):
+//             lambda_g = min(lambda_clip, H(f_g) / ln N), H(f) = -sum_j f_j ln f_j
 //   refine    on candidates C = [n_sink, N - W):
 //             s' = s * (1-alpha_soft)^dom * (1-alpha_cross)^exc, where dom = a candidate
 //             within R in the same head has strictly larger s, exc = g is not the head
@@ -16,12 +18,15 @@
 //             written ascending and padded with -1.
 //
 // Kernels:
-//   k_sel_zsum   Z_g partial sums over chunks of 4096 positions.
+//   k_sel_zsum   Z_g partial sums over chunks of 4096 positions (and, with an adaptive
+//                weight, partial sums of f ln f).
 //   k_sel_score  one block per tile of 256 - 2R positions plus an R-position halo, all
 //                KV heads at once (NMS couples neighbours, exclusivity couples heads):
 //                one thread per position computes s of every head into LDS, then the
 //                refined score s' as an order-preserving uint32 key (s' >= 0, so its IEEE
 //                bits already order like the value).
+//   k_greedy_nms (greedy soft-NMS only) one workgroup per (row, KV head): the greedy
+//                takes in rounds, keys rewritten in place with the taken scores.
 //   k_topk_*     radix select of the K-th largest key spread over slices of 4096
 //                candidates (histogram, boundary-bin gather, a one-block select on the
 //                gathered bin in LDS, ordered parallel write); see the top-K section.
@@ -109,13 +114,52 @@ __device__ __forceinline__ float prior_weight(float norm, int N, int j) {
   return (1.f / fmaxf(norm, 1e-6f)) * (1.f + logf(1.f + (float)(N - 1 - j)));
 }
 
-__global__ __launch_bounds__(256) void k_sel_zsum(const float* __restrict__ key_norm,
-                                                  int64_t norm_stride,
-                                                  const int32_t* __restrict__ seq_lens,
-                                                  const int32_t* __restrict__ seq_ids, int Hkv,
-                                                  int nchunk, float* __restrict__ zpart,
-                                                  uint32_t* __restrict__ topk_hist,
-                                                  uint32_t* __restrict__ topk_state) {
+struct ZsumArgs {
+  const float* key_norm;
+  int64_t norm_stride;
+  const int32_t* seq_lens;
+  const int32_t* seq_ids;
+  int Hkv, nchunk;
+  float* zpart;
+  uint32_t* topk_hist;
+  uint32_t* topk_state;
+  // adaptive fusion weight only (hpart == nullptr otherwise): partial sums of f ln f
+  const float* logits;
+  int64_t logits_stride;
+  const float* lse;
+  int Hq, G;
+  float* hpart;
+};
+
+// Evidence f at positions j .. j + 3 of KV head g (the same sum, in the same order, as the
+// scoring kernel's): the mean over the group's rows of exp(z - lse).
+__device__ __forceinline__ float4 evidence4(const ZsumArgs& a, int b, int g, int j) {
+  float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int hh = 0; hh < a.G; ++hh) {
+    const int h = g * a.G + hh;
+    const float4 z = *reinterpret_cast<const float4*>(
+        a.logits + ((size_t)b * a.Hq + h) * a.logits_stride + j);
+    const float l = a.lse[(size_t)b * a.Hq + h];
+    f.x += expf(z.x - l);
+    f.y += expf(z.y - l);
+    f.z += expf(z.z - l);
+    f.w += expf(z.w - l);
+  }
+  const float invG = 1.f / (float)a.G;
+  return make_float4(f.x * invG, f.y * invG, f.z * invG, f.w * invG);
+}
+
+__device__ __forceinline__ float flogf(float f) { return f > 0.f ? f * logf(f) : 0.f; }
+
+__global__ __launch_bounds__(256) void k_sel_zsum(ZsumArgs za) {
+  const float* __restrict__ key_norm = za.key_norm;
+  const int64_t norm_stride = za.norm_stride;
+  const int32_t* __restrict__ seq_lens = za.seq_lens;
+  const int32_t* __restrict__ seq_ids = za.seq_ids;
+  const int Hkv = za.Hkv, nchunk = za.nchunk;
+  float* __restrict__ zpart = za.zpart;
+  uint32_t* __restrict__ topk_hist = za.topk_hist;
+  uint32_t* __restrict__ topk_state = za.topk_state;
   __shared__ float red[8];
   const int chunk = blockIdx.x % nchunk;
   const int ig = blockIdx.x / nchunk;
@@ -150,6 +194,29 @@ __global__ __launch_bounds__(256) void k_sel_zsum(const float* __restrict__ key_
   }
   acc = block_sum<256>(acc, red);
   if (threadIdx.x == 0) zpart[blockIdx.x] = acc;
+  if (za.hpart) {
+    float h = 0.f;
+    for (int k = 0; k < 4; ++k) {
+      const int j = j0 + 1024 * k;
+      if (j + 3 < N) {
+        const float4 f = evidence4(za, b, g, j);
+        h += flogf(f.x) + flogf(f.y) + flogf(f.z) + flogf(f.w);
+      } else if (j < N) {
+        // the logits row holds at least N entries; read the tail one by one
+        for (int q = 0; q < 4 && j + q < N; ++q) {
+          float f = 0.f;
+          for (int hh = 0; hh < za.G; ++hh) {
+            const int hq = g * za.G + hh;
+            f += expf(za.logits[((size_t)b * za.Hq + hq) * za.logits_stride + j + q] -
+                      za.lse[(size_t)b * za.Hq + hq]);
+          }
+          h += flogf(f * (1.f / (float)za.G));
+        }
+      }
+    }
+    h = block_sum<256>(h, red);
+    if (threadIdx.x == 0) za.hpart[blockIdx.x] = h;
+  }
 }
 
 // ------------------------------------------------------------------------ fused scoring
@@ -162,13 +229,15 @@ struct ScoreArgs {
   const int32_t* seq_lens;
   const int32_t* seq_ids;
   const float* zpart;
+  const float* hpart;  // partial sums of f ln f (adaptive weight), or nullptr
   uint32_t* keys;
   int64_t kstride;
   float* dbg;
+  int greedy;  // greedy soft-NMS: the keys carry s with exclusivity only
   int Hq, Hkv, G, nchunk, ntile, tile;
   int n_work;  // rows x tiles
   int n_sink, n_recent, R;
-  float lam, a_soft, a_cross;
+  float lam, a_soft, a_cross, lam_clip;
 };
 
 // One block per (row, tile of `tile` positions).  Every thread computes the fused score s
@@ -186,7 +255,8 @@ __device__ __forceinline__ void score_block(const ScoreArgs& a, int work, float*
   const int W = TILE + 2 * R;
   float* s_t = lds;                   // [Hkv][W]  fused scores, column c = position t0 - R + c
   float* zs = s_t + a.Hkv * W;        // [Hkv]     prior normalisers
-  float* lses = zs + a.Hkv;           // [Hq]
+  float* lams = zs + a.Hkv;           // [Hkv]     fusion weights
+  float* lses = lams + a.Hkv;         // [Hq]
   const int tid = threadIdx.x;
   const int i = work / a.ntile;
   const int tile = work % a.ntile;
@@ -209,6 +279,18 @@ __device__ __forceinline__ void score_block(const ScoreArgs& a, int work, float*
     z += __shfl_xor(z, 2, 8);
     z += __shfl_xor(z, 4, 8);
     if (part == 0) zs[g] = z;
+    // fusion weight: fixed, or min(lambda_clip, H / ln N) from the f ln f partials
+    float lam = a.lam;
+    if (a.hpart) {
+      const float* hp = a.hpart + ((size_t)i * a.Hkv + g) * a.nchunk;
+      float t = 0.f;
+      for (int c = part; c < a.nchunk; c += 8) t += hp[c];
+      t += __shfl_xor(t, 1, 8);
+      t += __shfl_xor(t, 2, 8);
+      t += __shfl_xor(t, 4, 8);
+      lam = N > 1 ? fminf(a.lam_clip, -t / logf((float)N)) : 0.f;
+    }
+    if (part == 0) lams[g] = lam;
   }
   for (int h = tid; h < a.Hq; h += 256) lses[h] = a.lse[(size_t)b * a.Hq + h];
   __syncthreads();
@@ -238,7 +320,7 @@ __device__ __forceinline__ void score_block(const ScoreArgs& a, int work, float*
       }
       f *= invG;
       const float r = (1.f / fmaxf(nrow[(size_t)g * a.norm_stride], 1e-6f)) * phi_pos / zs[g];
-      const float s = (1.f - a.lam) * f + a.lam * r;
+      const float s = (1.f - lams[g]) * f + lams[g] * r;
       if (in && a.dbg && body) a.dbg[((size_t)b * a.Hkv + g) * a.logits_stride + j] = s;
       s_t[g * W + col] = in ? s : -1.f;
     }
@@ -265,7 +347,8 @@ __device__ __forceinline__ void score_block(const ScoreArgs& a, int work, float*
       const float* row = s_t + g * W + col;
       const float sj = row[0];
       bool dom = false;
-      for (int d = dlo; d <= dhi; ++d) dom |= (d != 0) && (row[d] > sj);
+      if (!a.greedy)
+        for (int d = dlo; d <= dhi; ++d) dom |= (d != 0) && (row[d] > sj);
       float sp = sj;
       if (dom) sp *= ws;
       if (a.Hkv > 1 && g != own) sp *= wc;
@@ -277,6 +360,93 @@ __device__ __forceinline__ void score_block(const ScoreArgs& a, int work, float*
 // Grid-stride over (row, tile) blocks: the grid is capped at one block per CU so the
 // scoring leaves room for the attention that runs at the same time.
 constexpr int kScoreMaxBlocks = 256;
+
+// ------------------------------------------------------------------- greedy soft-NMS
+// The greedy reading takes, per head, the candidate with the largest current score (the
+// lower position on ties); it keeps that score, and every untaken candidate within R is
+// scaled by 1 - alpha_soft; repeated until all are taken.  The takes are made here in
+// rounds: a candidate that beats every untaken candidate within R (larger score, or equal
+// score and lower position) is taken before any of them in the greedy order and keeps
+// its current score, so every such local maximum is taken at once, and the untaken
+// candidates are scaled once per neighbour taken in the round.  Every round takes the
+// largest untaken candidate, so there are at most |C| rounds.  The result is the greedy
+// one exactly: a candidate's score is scaled once for each neighbour taken before it in
+// either order.
+struct GreedyArgs {
+  uint32_t* keys;   // in: s with exclusivity (IEEE bits of a score >= 0); out: taken scores
+  int64_t kstride;
+  int32_t* taken;   // [units][kstride]: round in which the candidate was taken, 0 = not yet
+  int32_t* ready;   // [units][kstride]: round in which it was found ready
+  const int32_t* seq_lens;
+  const int32_t* seq_ids;
+  int Hkv, n_sink, n_recent, R;
+  float decay;      // 1 - alpha_soft
+};
+constexpr int kGreedyThreads = 1024;
+
+__global__ __launch_bounds__(kGreedyThreads) void k_greedy_nms(GreedyArgs a) {
+  __shared__ int s_taken;
+  const int ig = blockIdx.x;
+  const int b = a.seq_ids[ig / a.Hkv];
+  if (b < 0) return;  // unused slot of the row list (block-uniform)
+  const int N = a.seq_lens[b];
+  const int lo = a.n_sink, hi = max(lo, N - a.n_recent);
+  const int n = hi - lo;
+  const int R = a.R;
+  uint32_t* key = a.keys + (size_t)ig * a.kstride;
+  int32_t* tk = a.taken + (size_t)ig * a.kstride;
+  int32_t* rd = a.ready + (size_t)ig * a.kstride;
+  const int tid = threadIdx.x;
+  for (int c = tid; c < n; c += kGreedyThreads) {
+    tk[c] = 0;
+    rd[c] = 0;
+  }
+  if (tid == 0) s_taken = 0;
+  __syncthreads();
+  int left = n;
+  for (int round = 1; left > 0 && round <= n; ++round) {
+    // Ready: untaken and larger than every untaken neighbour (lower position on ties).
+    for (int c = tid; c < n; c += kGreedyThreads) {
+      if (tk[c]) continue;
+      const float vc = u2f(key[c]);
+      bool ready = true;
+      for (int d = -R; d <= R && ready; ++d) {
+        const int k = c + d;
+        if (d == 0 || k < 0 || k >= n || tk[k]) continue;
+        const float vk = u2f(key[k]);
+        if (vk > vc || (vk == vc && k < c)) ready = false;
+      }
+      if (ready) rd[c] = round;
+    }
+    __syncthreads();
+    // Take the ready ones (their key is their final score); scale the others once per
+    // neighbour taken now.
+    int took = 0;
+    for (int c = tid; c < n; c += kGreedyThreads) {
+      if (tk[c]) continue;
+      if (rd[c] == round) {
+        tk[c] = round;
+        ++took;
+        continue;
+      }
+      int cnt = 0;
+      for (int d = -R; d <= R; ++d) {
+        const int k = c + d;
+        cnt += (d != 0 && k >= 0 && k < n && rd[k] == round) ? 1 : 0;
+      }
+      if (cnt) {
+        float v = u2f(key[c]);
+        for (int q = 0; q < cnt; ++q) v *= a.decay;
+        key[c] = f2u(v) & 0x7fffffffu;
+      }
+    }
+    took = (int)wave_sum_xor((float)took, kWave);
+    if ((tid & 63) == 0 && took) atomicAdd(&s_taken, took);
+    __syncthreads();
+    left = n - s_taken;
+    __syncthreads();
+  }
+}
 
 template <int GT>
 __global__ __launch_bounds__(256) void k_sel_score(ScoreArgs a) {
@@ -775,7 +945,7 @@ hipError_t launch_key_norms(const sfi_shape& s, const void* kc, const int32_t* b
   return hipGetLastError();
 }
 
-SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len) {
+SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len, bool greedy) {
   SelectLayout L;
   L.nchunk = (max_seq_len + kZChunk - 1) / kZChunk;
   L.kstride = ((int64_t)max_seq_len + 63) / 64 * 64;
@@ -788,7 +958,12 @@ SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len) {
     return at;
   };
   L.zpart_off = take(units * L.nchunk * sizeof(float));
+  L.hpart_off = take(units * L.nchunk * sizeof(float));
   L.keys_off = take(units * (size_t)L.kstride * sizeof(uint32_t));
+  if (greedy) {
+    L.taken_off = take(units * (size_t)L.kstride * sizeof(int32_t));
+    L.ready_off = take(units * (size_t)L.kstride * sizeof(int32_t));
+  }
   L.hist_off = take(units * kHistBins * sizeof(uint32_t));
   L.state_off = take(units * kStWords * sizeof(uint32_t));
   L.above_off = take(units * L.nslice * sizeof(uint32_t));
@@ -801,7 +976,7 @@ SelectLayout select_layout(const sfi_shape& s, int n_seqs, int max_seq_len) {
 
 size_t score_lds_bytes(int num_kv_heads, int num_q_heads, int nms_radius, int tile) {
   const size_t W = (size_t)tile + 2 * (size_t)nms_radius;
-  return sizeof(float) * ((size_t)num_kv_heads * W + num_kv_heads + num_q_heads);
+  return sizeof(float) * ((size_t)num_kv_heads * W + 2 * num_kv_heads + num_q_heads);
 }
 
 int score_tile(int num_kv_heads, int num_q_heads, int nms_radius) {
@@ -833,15 +1008,31 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm, const
                          int64_t norm_stride, const int32_t* seq_lens, const int32_t* seq_ids,
                          int n_seqs, int max_seq_len, int32_t* sel_idx, float* dbg, void* ws,
                          hipStream_t st) {
-  const SelectLayout L = select_layout(s, n_seqs, max_seq_len);
+  const bool greedy = prm.nms_greedy != 0;
+  const SelectLayout L = select_layout(s, n_seqs, max_seq_len, greedy);
   char* w = reinterpret_cast<char*>(ws);
   float* zpart = reinterpret_cast<float*>(w + L.zpart_off);
+  const bool adaptive = prm.lambda_clip >= 0.f;
+  float* hpart = adaptive ? reinterpret_cast<float*>(w + L.hpart_off) : nullptr;
   uint32_t* keys = reinterpret_cast<uint32_t*>(w + L.keys_off);
   const int Hkv = s.num_kv_heads, Hq = s.num_q_heads;
-  hipLaunchKernelGGL(k_sel_zsum, dim3(n_seqs * Hkv * L.nchunk), dim3(256), 0, st, key_norm,
-                     norm_stride, seq_lens, seq_ids, Hkv, L.nchunk, zpart,
-                     reinterpret_cast<uint32_t*>(w + L.hist_off),
-                     reinterpret_cast<uint32_t*>(w + L.state_off));
+  ZsumArgs za;
+  za.key_norm = key_norm;
+  za.norm_stride = norm_stride;
+  za.seq_lens = seq_lens;
+  za.seq_ids = seq_ids;
+  za.Hkv = Hkv;
+  za.nchunk = L.nchunk;
+  za.zpart = zpart;
+  za.topk_hist = reinterpret_cast<uint32_t*>(w + L.hist_off);
+  za.topk_state = reinterpret_cast<uint32_t*>(w + L.state_off);
+  za.logits = logits;
+  za.logits_stride = logits_stride;
+  za.lse = lse;
+  za.Hq = Hq;
+  za.G = Hq / Hkv;
+  za.hpart = hpart;
+  hipLaunchKernelGGL(k_sel_zsum, dim3(n_seqs * Hkv * L.nchunk), dim3(256), 0, st, za);
   ScoreArgs a;
   a.logits = logits;
   a.logits_stride = logits_stride;
@@ -851,9 +1042,11 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm, const
   a.seq_lens = seq_lens;
   a.seq_ids = seq_ids;
   a.zpart = zpart;
+  a.hpart = hpart;
   a.keys = keys;
   a.kstride = L.kstride;
   a.dbg = dbg;
+  a.greedy = greedy ? 1 : 0;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = Hq / Hkv;
@@ -864,9 +1057,25 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm, const
   a.lam = prm.lambda;
   a.a_soft = prm.alpha_soft;
   a.a_cross = prm.alpha_cross;
+  a.lam_clip = prm.lambda_clip;
   a.tile = score_tile(Hkv, Hq, prm.nms_radius);
   a.ntile = (max_seq_len + a.tile - 1) / a.tile;
   launch_score(a, n_seqs, score_lds_bytes(Hkv, Hq, prm.nms_radius, a.tile), st);
+  if (greedy) {
+    GreedyArgs gr;
+    gr.keys = keys;
+    gr.kstride = L.kstride;
+    gr.taken = reinterpret_cast<int32_t*>(w + L.taken_off);
+    gr.ready = reinterpret_cast<int32_t*>(w + L.ready_off);
+    gr.seq_lens = seq_lens;
+    gr.seq_ids = seq_ids;
+    gr.Hkv = Hkv;
+    gr.n_sink = prm.n_sink;
+    gr.n_recent = prm.n_recent;
+    gr.R = prm.nms_radius;
+    gr.decay = 1.f - prm.alpha_soft;
+    hipLaunchKernelGGL(k_greedy_nms, dim3(n_seqs * Hkv), dim3(kGreedyThreads), 0, st, gr);
+  }
   TopkArgs t;
   t.keys = keys;
   t.kstride = L.kstride;

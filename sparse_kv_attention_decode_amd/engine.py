@@ -213,7 +213,8 @@ class Engine:
         self.shape = L.make_shape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                   w.pages_per_seq, w.dtype)
         self.params = L.make_params(w.n_sink, w.n_recent, w.top_k, w.nms_radius, w.lam,
-                                    w.alpha_soft, w.alpha_cross)
+                                    w.alpha_soft, w.alpha_cross, w.lambda_clip,
+                                    w.nms_greedy)
         self.packed_cap = L.sfi_packed_cap(self.params)
         self.max_len = w.total_len
         self.stride = (self.max_len + 63) // 64 * 64

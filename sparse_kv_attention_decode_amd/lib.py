@@ -39,7 +39,8 @@ class SfiSelectParams(ctypes.Structure):
     _fields_ = [("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("nms_radius", ctypes.c_int32),
                 ("lambda_", ctypes.c_float), ("alpha_soft", ctypes.c_float),
-                ("alpha_cross", ctypes.c_float)]
+                ("alpha_cross", ctypes.c_float), ("lambda_clip", ctypes.c_float),
+                ("nms_greedy", ctypes.c_int32)]
 
 
 class SfiError(RuntimeError):
@@ -126,8 +127,12 @@ def make_shape(batch, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, dt
                     dt.get(dtype, dtype))
 
 
-def make_params(n_sink, n_recent, top_k, nms_radius, lam, alpha_soft, alpha_cross) -> SfiSelectParams:
-    return SfiSelectParams(n_sink, n_recent, top_k, nms_radius, lam, alpha_soft, alpha_cross)
+def make_params(n_sink, n_recent, top_k, nms_radius, lam, alpha_soft, alpha_cross,
+                lambda_clip=-1.0, nms_greedy=False) -> SfiSelectParams:
+    """lambda_clip < 0: fixed fusion weight lam; in [0, 1]: the clipped adaptive weight.
+    nms_greedy: greedy soft-NMS instead of the one-pass reading."""
+    return SfiSelectParams(n_sink, n_recent, top_k, nms_radius, lam, alpha_soft, alpha_cross,
+                           lambda_clip, int(bool(nms_greedy)))
 
 
 def _ptr(t) -> Optional[int]:

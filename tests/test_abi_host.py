@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert sorted(L.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert L.sfi_abi_version() == 6
+    assert L.sfi_abi_version() == 7
 
 
 def test_status_strings():
@@ -121,6 +121,15 @@ def test_select_validation():
     assert _select(s, _params(top_k=0)) == L.SFI_E_ARG
     assert _select(s, _params(nms_radius=-1)) == L.SFI_E_ARG
     assert _select(s, _params(lam=1.5)) == L.SFI_E_ARG
+    assert _select(s, _params(lambda_clip=1.5)) == L.SFI_E_ARG
+    assert _select(s, _params(lambda_clip=float("nan"))) == L.SFI_E_ARG
+    assert _select(s, _params(lambda_clip=-1.0, lam=1.5)) == L.SFI_E_ARG
+    bad = _params()
+    bad.nms_greedy = 2
+    assert _select(s, bad) == L.SFI_E_ARG
+    # the greedy soft-NMS needs two more arrays per candidate in the workspace
+    assert L.sfi_select_ws(s, _params(nms_greedy=True), 2, 1000) > \
+        L.sfi_select_ws(s, _params(), 2, 1000)
     assert _select(s, _params(lam=float("nan"))) == L.SFI_E_ARG
     assert _select(s, _params(alpha_soft=-0.1)) == L.SFI_E_ARG
     assert _select(s, _params(alpha_cross=2.0)) == L.SFI_E_ARG

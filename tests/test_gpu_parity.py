@@ -41,6 +41,11 @@ def _slow(eng, lb, q, N, ids=None):
 SMALL = ["tiny_fp32_1k", "qwen3_0p6b_8k"]
 
 
+def _lc(w):
+    """The oracle's lambda_clip argument for a workload (None: the fixed weight lam)."""
+    return w.lambda_clip if w.lambda_clip >= 0 else None
+
+
 def _bits(t: torch.Tensor) -> torch.Tensor:
     """Bit pattern of a bf16 / fp32 tensor, for byte-exact comparisons."""
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
@@ -112,7 +117,7 @@ def _select_and_check(w, d, eng, lb, s):
         q, K, V = oracle_layer_arrays(d, b)
         _, _, _, p = O.attention(q[s], K[:, :N], V[:, :N])
         sel = O.select(p, O.key_norms(K[:, :N]), N, w.num_kv_heads, w.n_sink, w.n_recent,
-                       w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam)
+                       w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam, _lc(w))
         np.testing.assert_allclose(s_gpu, sel.s, rtol=1e-3, atol=1e-12)
         stats.append(explain_selection_diff(sel_gpu, sel, N))
     return stats
@@ -125,6 +130,53 @@ def test_select(name):
     for s in (0, 9):
         stats = _select_and_check(w, d, eng, lb, s)
         print(name, "step", s, "(diff, kth-ties, decision-ties) per row:", stats)
+
+
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("clip", [0.3, 0.9])
+def test_select_adaptive_lambda(name, clip):
+    """The clipped adaptive fusion weight (lambda_clip): fused scores against the oracle,
+    exact Top-K on the device's own scores, the near-tie rule end to end."""
+    w = get(name).replace(lambda_clip=clip, name=f"{name}_clip{clip}")
+    d, eng, lb = _setup(w, dbg=True)
+    for s in (0, 9):
+        stats = _select_and_check(w, d, eng, lb, s)
+        print(name, "clip", clip, "step", s, "(diff, kth, decision, score) per row:", stats)
+
+
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("clip", [None, 0.3])
+def test_select_greedy_soft_nms(name, clip):
+    """Greedy soft-NMS on the device (nms_greedy = 1): the selection equals the oracle's
+    greedy reading (refine_greedy, then Top-K) run on the device's own fused scores, and
+    the fused scores match the oracle's; also with the adaptive fusion weight."""
+    w = get(name).replace(nms_greedy=True, lambda_clip=-1.0 if clip is None else clip,
+                          name=f"{name}_greedy")
+    d, eng, lb = _setup(w, dbg=True)
+    for s in (0, 9):
+        N = w.seq_len(s)
+        seq_len = _slow(eng, lb, d["q"][s], N)
+        L.sfi_select(eng.shape, eng.params, lb.logits, eng.stride, lb.lse, lb.key_norm,
+                     eng.stride, seq_len, eng.all_ids_d, w.batch, eng.max_len, lb.sel_idx,
+                     eng.dbg_buf, eng.ws_sel)
+        torch.cuda.synchronize()
+        for b in range(w.batch):
+            sel_gpu = lb.sel_idx[b].cpu().numpy()
+            s_gpu = host64(eng.dbg_buf[b, :, :N])
+            ref = O.select_greedy_from_scores(s_gpu, N, w.n_sink, w.n_recent, w.top_k,
+                                              w.nms_radius, w.alpha_soft, w.alpha_cross)
+            np.testing.assert_array_equal(sel_gpu, ref)
+            q, K, V = oracle_layer_arrays(d, b)
+            _, _, _, p = O.attention(q[s], K[:, :N], V[:, :N])
+            sel = O.select(p, O.key_norms(K[:, :N]), N, w.num_kv_heads, w.n_sink, w.n_recent,
+                           w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam, _lc(w))
+            np.testing.assert_allclose(s_gpu, sel.s, rtol=1e-3, atol=1e-12)
+            one_pass = O.select_from_scores(s_gpu, N, w.n_sink, w.n_recent, w.top_k,
+                                            w.nms_radius, w.alpha_soft, w.alpha_cross)
+            jac = [len(set(a) & set(c)) / max(1, len(set(a) | set(c)))
+                   for a, c in zip(sel_gpu, one_pass)]
+            print(name, "step", s, "row", b, "greedy vs one-pass Jaccard per head:",
+                  np.round(jac, 3).tolist())
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -170,7 +222,10 @@ RAGGED_RECENT = dict(batch=4, context=6000, n_recent=600, top_k=1500, steps=40, 
                           ("tiny_fp32_1k", 1, False, True, None),
                           ("qwen3_0p6b_8k", 1, False, True, None),
                           pytest.param("qwen3_0p6b_8k", 1, False, True, RAGGED_RECENT,
-                                       id="ragged_recent_b4")])
+                                       id="ragged_recent_b4"),
+                          pytest.param("qwen3_0p6b_8k", 1, False, None,
+                                       dict(lambda_clip=0.3, name="lambda_clip_8k"),
+                                       id="lambda_clip")])
 def test_trajectory_lockstep(name, win, sliding, inc, over):
     """Every step of the seeded trajectory through the two-stream engine.  Slow steps:
     dense output and the selection (near-tie rule); the oracle then continues with the
@@ -204,14 +259,14 @@ def test_trajectory_lockstep(name, win, sliding, inc, over):
                 if win == 1:
                     sel = O.select(p, norms[b][:, :N], N, w.num_kv_heads, w.n_sink,
                                    w.n_recent, w.top_k, w.nms_radius, w.alpha_soft,
-                                   w.alpha_cross, w.lam)
+                                   w.alpha_cross, w.lam, _lc(w))
                 else:
                     Qw = O.window_queries(q, s, win)
                     P = np.stack([p] + [O.attention(Qw[k], K[:, :N], V[:, :N])[3]
                                         for k in range(1, win)])
                     sel = O.select_window(P, norms[b][:, :N], N, w.num_kv_heads, w.n_sink,
                                           w.n_recent, w.top_k, w.nms_radius, w.alpha_soft,
-                                          w.alpha_cross, w.lam)
+                                          w.alpha_cross, w.lam, _lc(w))
                 sel_gpu = lb.sel_idx[b].cpu().numpy()
                 explain_selection_diff(sel_gpu, sel, N)
                 packed[b] = [O.packed_positions(sel_gpu[g], w.n_sink)
@@ -267,7 +322,7 @@ def test_slow_attention_and_select_window(name, win):
                 check_logits(z_gpu[:, k].reshape(Hq, N), z, Qw[k], K[:, :N], w.head_dim)
             sel = O.select_window(np.stack(P), O.key_norms(K[:, :N]), N, Hkv, w.n_sink,
                                   w.n_recent, w.top_k, w.nms_radius, w.alpha_soft,
-                                  w.alpha_cross, w.lam)
+                                  w.alpha_cross, w.lam, _lc(w))
             s_gpu = host64(eng.dbg_buf[b, :, :N])
             np.testing.assert_allclose(s_gpu, sel.s, rtol=1e-3, atol=1e-12)
             sel_gpu = lb.sel_idx[b].cpu().numpy()
@@ -438,7 +493,7 @@ def test_edge_cases(case):
         if omode[0, s]:
             o, z, lse, p = O.attention(q[s], K[:, :N], V[:, :N])
             sel = O.select(p, norms[:, :N], N, w.num_kv_heads, w.n_sink, w.n_recent, w.top_k,
-                           w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam)
+                           w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam, _lc(w))
             sel_gpu = lb.sel_idx[0].cpu().numpy()
             explain_selection_diff(sel_gpu, sel, N)
             packed = [O.packed_positions(sel_gpu[g], w.n_sink) for g in range(w.num_kv_heads)]
@@ -552,7 +607,7 @@ def test_full_size_sampled(name):
             sel_gpu, O.select_from_scores(s_gpu, N, w.n_sink, w.n_recent, w.top_k,
                                           w.nms_radius, w.alpha_soft, w.alpha_cross))
         sel = O.select(p, O.key_norms(K[:, :N]), N, w.num_kv_heads, w.n_sink, w.n_recent,
-                       w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam)
+                       w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross, w.lam, _lc(w))
         print(name, "row", b, "selection diff (n, kth, decision):",
               explain_selection_diff(sel_gpu, sel, N))
         pos = [O.packed_positions(sel_gpu[g], w.n_sink) for g in range(w.num_kv_heads)]
@@ -863,7 +918,7 @@ def test_full_stack_in_bench_configuration():
                 check_out(host64(lb.out[0]), o, f"layer {li} step {s}")
                 sel = O.select(p, O.key_norms(K[:, :N]), N, w.num_kv_heads, w.n_sink,
                                w.n_recent, w.top_k, w.nms_radius, w.alpha_soft, w.alpha_cross,
-                               w.lam)
+                               w.lam, _lc(w))
                 sel_gpu = lb.sel_idx[0].cpu().numpy()
                 print(f"layer {li} step {s} selection diff (n, kth, decision, score):",
                       explain_selection_diff(sel_gpu, sel, N))

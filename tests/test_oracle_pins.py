@@ -385,6 +385,44 @@ def test_fusion_worked_example_and_endpoints():
     np.testing.assert_allclose(O.fuse(f, r, 0.3).sum(axis=1), 1.0, atol=1e-14)
 
 
+def test_adaptive_lambda_worked_examples():
+    """The clipped adaptive fusion weight min(λclip, H(f)/ln N) on hand-evaluated entropies
+    (golden), the point-mass and uniform limits, and λclip = 0 (evidence only)."""
+    g = json.load(open(os.path.join(GOLDEN, "adaptive_lambda.json")))
+    f4 = np.array(g["f4"])
+    np.testing.assert_allclose(O.adaptive_lambda(f4, 0.8), g["lam_clip08"], atol=1e-15)
+    np.testing.assert_allclose(O.adaptive_lambda(f4, 0.3), g["lam_clip03"], atol=1e-15)
+    np.testing.assert_allclose(O.adaptive_lambda(np.array(g["f8"]), 1.0), g["lam8_clip1"],
+                               atol=1e-15)
+    np.testing.assert_array_equal(O.adaptive_lambda(np.array([[0.0, 1.0, 0.0]]), 0.9), [0.0])
+    np.testing.assert_array_equal(O.adaptive_lambda(np.array([[1.0]]), 0.9), [0.0])
+    np.testing.assert_array_equal(O.adaptive_lambda(f4, 0.0), [0.0, 0.0])
+    s = O.fuse_per_head(f4[:1], np.full((1, 4), 0.25), [0.5])
+    np.testing.assert_allclose(s[0], g["fused_f0_uniform_half"], atol=1e-15)
+
+
+def test_adaptive_lambda_grows_with_flatness_and_keeps_a_distribution():
+    N = 50
+    point = np.zeros(N)
+    point[7] = 1.0
+    lams = [O.adaptive_lambda(((1 - t) * point + t / N)[None, :], 1.0)[0]
+            for t in np.linspace(0, 1, 11)]
+    assert lams[0] == 0.0 and abs(lams[-1] - 1.0) < 1e-12
+    assert all(b > a for a, b in zip(lams, lams[1:]))
+    q, K, V = _rand_qkv(Hq=8, Hkv=2, n=N, seed=21, scale=2.0)
+    _, _, _, p = O.attention(q, K, V)
+    f = O.evidence(p, 2)
+    r = O.prior(O.key_norms(K))
+    lam = O.adaptive_lambda(f, 0.3)
+    assert ((lam >= 0) & (lam <= 0.3)).all()
+    s = O.fuse_per_head(f, r, lam)
+    np.testing.assert_allclose(s.sum(axis=1), 1.0, atol=1e-14)
+    # the Selector with the adaptive weight equals the fixed-weight Selector at those weights
+    # for one head (per-head weights only differ across heads)
+    sel = O.select_from_evidence(f, O.key_norms(K), N, 4, 8, 10, 2, 0.5, 0.5, 0.7, 0.3)
+    np.testing.assert_allclose(sel.s, s, atol=1e-15)
+
+
 def _kl_objective(s, f, r, lam):
     s = np.clip(s, 1e-300, None)
     return (1 - lam) * np.sum(f * np.log(f / s)) + lam * np.sum(r * np.log(r / s))

@@ -42,6 +42,8 @@ class Workload:
     page_size: int = 16
     evidence_window: int = 1  # decode queries whose attention the Selector pools
     sliding_recent: bool = False  # recent segment = newest W positions at every step
+    lambda_clip: float = -1.0  # < 0: fusion weight lam; in [0, 1]: adaptive, clipped here
+    nms_greedy: bool = False   # greedy soft-NMS instead of the one-pass reading
 
     @property
     def group(self) -> int:
