@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SFI_ABI_VERSION 7
+#define SFI_ABI_VERSION 8
 
 enum sfi_status {
   SFI_OK = 0,
@@ -78,6 +78,21 @@ enum sfi_status {
 };
 
 enum sfi_dtype { SFI_BF16 = 0, SFI_F32 = 1 };
+
+/* Device-side contract violations.  The attention calls and sfi_pack_update take a
+ * `status` pointer (device memory, uint32, may be NULL): a kernel that finds a contract of
+ * its call broken ORs the matching bit into *status and carries on with the documented
+ * safeguard, so the host can see afterwards that the results of those rows are
+ * unspecified.  The library never clears *status; a caller that wants fresh flags zeroes
+ * it first.  The checks cost a few scalar loads per (row, KV head). */
+enum sfi_device_status {
+  SFI_DEV_SEQ_LEN = 1u,     /* a row length outside [0, the call's bound]: clamped          */
+  SFI_DEV_PACKED_LEN = 2u,  /* packed_len outside [0, packed_cap]: clamped                  */
+  SFI_DEV_RECENT = 4u,      /* recent_start outside [0, N], or a recent segment longer than
+                               max_recent: clamped / truncated                             */
+  SFI_DEV_PACK_SLOT = 8u    /* the incremental pack placed a row outside the buffer (state
+                               not maintained by these calls): that row was not written    */
+};
 
 typedef struct {
   int32_t batch;              /* rows of block_table / seq_lens                           */
@@ -156,8 +171,8 @@ int sfi_key_norms(const sfi_shape* shape, const void* k_cache, const int32_t* bl
 int sfi_slow_attn(const sfi_shape* shape, const float* q, const void* k_cache,
                   const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                   const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len, float* out,
-                  float* logits, int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
-                  void* stream);
+                  float* logits, int64_t logits_stride, float* lse, uint32_t* status, void* ws,
+                  size_t ws_bytes, void* stream);
 
 /*
  * sfi_slow_attn_window -- a slow step whose evidence comes from a window of `window`
@@ -178,7 +193,8 @@ int sfi_slow_attn_window(const sfi_shape* shape, int32_t window, const float* q_
                          const void* k_cache, const void* v_cache, const int32_t* block_table,
                          const int32_t* seq_lens, const int32_t* seq_ids, int32_t n_seqs,
                          int32_t max_seq_len, float* out, float* logits, int64_t logits_stride,
-                         float* lse, void* ws, size_t ws_bytes, void* stream);
+                         float* lse, uint32_t* status, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /*
  * sfi_select -- the training-free Selector of a slow step (zh "2.2 训练无感的 Selector",
@@ -262,8 +278,8 @@ int sfi_pack_update(const sfi_shape* shape, const sfi_select_params* params,
                     const void* k_cache, const void* v_cache, const int32_t* block_table,
                     const int32_t* sel_idx, const int32_t* seq_ids, int32_t n_seqs,
                     void* packed_k, void* packed_v, int32_t* packed_pos, int32_t* packed_len,
-                    int32_t packed_cap, int32_t* slot_map, int64_t map_stride, void* ws,
-                    size_t ws_bytes, void* stream);
+                    int32_t packed_cap, int32_t* slot_map, int64_t map_stride, uint32_t* status,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /*
  * sfi_fast_attn -- two-segment attention of a fast step (zh "2.3 系统级优化"): segment A is
@@ -278,7 +294,7 @@ int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
                   const void* k_cache, const void* v_cache, const int32_t* block_table,
                   const int32_t* recent_start, const int32_t* seq_lens,
                   const int32_t* seq_ids, int32_t n_seqs, int32_t max_recent, float* out,
-                  float* lse, void* ws, size_t ws_bytes, void* stream);
+                  float* lse, uint32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * sfi_fast_attn_noalloc -- sfi_fast_attn for callers that cannot allocate device memory:
@@ -299,7 +315,7 @@ int sfi_fast_attn_noalloc(const sfi_shape* shape, const float* q, const void* pa
                           const void* k_cache, const void* v_cache, const int32_t* block_table,
                           const int32_t* recent_start, const int32_t* seq_lens,
                           const int32_t* seq_ids, int32_t n_seqs, int32_t max_recent,
-                          float* out, float* lse, void* stream);
+                          float* out, float* lse, uint32_t* status, void* stream);
 
 /*
  * sfi_decode_attn -- the attention of a whole decode step in one partial launch and one
@@ -318,8 +334,8 @@ int sfi_decode_attn(const sfi_shape* shape, int32_t window, const float* q,
                     const int32_t* recent_start, const int32_t* seq_lens,
                     const int32_t* fast_ids, const int32_t* slow_ids, int32_t n_seqs,
                     int32_t max_recent, int32_t max_seq_len, float* out, float* logits,
-                    int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
-                    void* stream);
+                    int64_t logits_stride, float* lse, uint32_t* status, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /*
  * sfi_step_control -- the slow/fast decision of one decode step for every row of the batch,

@@ -137,8 +137,8 @@ int window_shape(const sfi_shape* shape, int32_t window, sfi_shape* out) {
 int prep_slow(const sfi_shape* shape, int32_t window, const float* q, const void* k_cache,
               const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
               const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len, float* out,
-              float* logits, int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
-              sfi::AttnParams* pp) {
+              float* logits, int64_t logits_stride, float* lse, uint32_t* status, void* ws,
+              size_t ws_bytes, sfi::AttnParams* pp) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !seq_ids || !out || !lse)
@@ -165,6 +165,7 @@ int prep_slow(const sfi_shape* shape, int32_t window, const float* q, const void
   p.seq_ids = seq_ids;
   p.logits = logits;
   p.logits_stride = logits_stride;
+  p.status = status;
   const size_t units = (size_t)n_seqs * shape->num_kv_heads * sp.nsplit *
                        (shape->num_q_heads / shape->num_kv_heads);
   const size_t ml = ((units * sizeof(float) + 255) / 256) * 256;
@@ -190,12 +191,12 @@ int prep_slow(const sfi_shape* shape, int32_t window, const float* q, const void
 int slow_attn(const sfi_shape* shape, int32_t window, const float* q, const void* k_cache,
               const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
               const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len, float* out,
-              float* logits, int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
-              void* stream) {
+              float* logits, int64_t logits_stride, float* lse, uint32_t* status, void* ws,
+              size_t ws_bytes, void* stream) {
   sfi::AttnParams p;
   const int rc = prep_slow(shape, window, q, k_cache, v_cache, block_table, seq_lens, seq_ids,
-                           n_seqs, max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes,
-                           &p);
+                           n_seqs, max_seq_len, out, logits, logits_stride, lse, status, ws,
+                           ws_bytes, &p);
   if (rc || n_seqs == 0) return rc;
   return finish(sfi::launch_attention(p, shape->head_dim, shape->dtype, out, lse,
                                       reinterpret_cast<hipStream_t>(stream)));
@@ -208,10 +209,10 @@ extern "C" {
 int sfi_slow_attn(const sfi_shape* shape, const float* q, const void* k_cache,
                   const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                   const int32_t* seq_ids, int32_t n_seqs, int32_t max_seq_len, float* out,
-                  float* logits, int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
-                  void* stream) {
+                  float* logits, int64_t logits_stride, float* lse, uint32_t* status, void* ws,
+                  size_t ws_bytes, void* stream) {
   return slow_attn(shape, 1, q, k_cache, v_cache, block_table, seq_lens, seq_ids, n_seqs,
-                   max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes, stream);
+                   max_seq_len, out, logits, logits_stride, lse, status, ws, ws_bytes, stream);
 }
 
 size_t sfi_slow_attn_window_ws(const sfi_shape* shape, int32_t window, int32_t n_seqs,
@@ -225,12 +226,13 @@ int sfi_slow_attn_window(const sfi_shape* shape, int32_t window, const float* q_
                          const void* k_cache, const void* v_cache, const int32_t* block_table,
                          const int32_t* seq_lens, const int32_t* seq_ids, int32_t n_seqs,
                          int32_t max_seq_len, float* out, float* logits, int64_t logits_stride,
-                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+                         float* lse, uint32_t* status, void* ws, size_t ws_bytes,
+                         void* stream) {
   sfi_shape sw;
   int rc = window_shape(shape, window, &sw);
   if (rc) return rc;
   return slow_attn(&sw, window, q_win, k_cache, v_cache, block_table, seq_lens, seq_ids, n_seqs,
-                   max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes, stream);
+                   max_seq_len, out, logits, logits_stride, lse, status, ws, ws_bytes, stream);
 }
 
 int sfi_select(const sfi_shape* shape, const sfi_select_params* params, const float* logits,
@@ -291,8 +293,8 @@ int sfi_pack_update(const sfi_shape* shape, const sfi_select_params* params,
                     const void* k_cache, const void* v_cache, const int32_t* block_table,
                     const int32_t* sel_idx, const int32_t* seq_ids, int32_t n_seqs,
                     void* packed_k, void* packed_v, int32_t* packed_pos, int32_t* packed_len,
-                    int32_t packed_cap, int32_t* slot_map, int64_t map_stride, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    int32_t packed_cap, int32_t* slot_map, int64_t map_stride, uint32_t* status,
+                    void* ws, size_t ws_bytes, void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if ((rc = check_params(params))) return rc;
@@ -309,8 +311,8 @@ int sfi_pack_update(const sfi_shape* shape, const sfi_select_params* params,
   if (n_seqs == 0) return SFI_OK;
   return finish(sfi::launch_pack_update(*shape, *params, k_cache, v_cache, block_table, sel_idx,
                                         seq_ids, n_seqs, packed_k, packed_v, packed_pos,
-                                        packed_len, packed_cap, slot_map, map_stride, ws,
-                                        reinterpret_cast<hipStream_t>(stream)));
+                                        packed_len, packed_cap, slot_map, map_stride, status,
+                                        ws, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int sfi_pack(const sfi_shape* shape, const sfi_select_params* params, const void* k_cache,
@@ -381,7 +383,8 @@ int prep_fast(const sfi_shape* shape, const float* q, const void* packed_k, cons
               const int32_t* packed_len, int32_t packed_cap, const void* k_cache,
               const void* v_cache, const int32_t* block_table, const int32_t* recent_start,
               const int32_t* seq_lens, const int32_t* seq_ids, int32_t n_seqs,
-              int32_t max_recent, float* out, void* ws, size_t ws_bytes, sfi::AttnParams* pp) {
+              int32_t max_recent, float* out, uint32_t* status, void* ws, size_t ws_bytes,
+              sfi::AttnParams* pp) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!q || !packed_k || !packed_v || !packed_len || !k_cache || !v_cache || !block_table ||
@@ -412,6 +415,7 @@ int prep_fast(const sfi_shape* shape, const float* q, const void* packed_k, cons
   p.packed_len = packed_len;
   p.recent_start = recent_start;
   p.logits = nullptr;
+  p.status = status;
   const size_t units = (size_t)n_seqs * shape->num_kv_heads * sp.nsplit *
                        (shape->num_q_heads / shape->num_kv_heads);
   const size_t ml = ((units * sizeof(float) + 255) / 256) * 256;
@@ -444,12 +448,12 @@ int sfi_fast_attn(const sfi_shape* shape, const float* q, const void* packed_k,
                   const void* packed_v, const int32_t* packed_len, int32_t packed_cap,
                   const void* k_cache, const void* v_cache, const int32_t* block_table,
                   const int32_t* recent_start, const int32_t* seq_lens, const int32_t* seq_ids,
-                  int32_t n_seqs, int32_t max_recent, float* out, float* lse, void* ws,
-                  size_t ws_bytes, void* stream) {
+                  int32_t n_seqs, int32_t max_recent, float* out, float* lse, uint32_t* status,
+                  void* ws, size_t ws_bytes, void* stream) {
   sfi::AttnParams p;
   const int rc = prep_fast(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache,
                            v_cache, block_table, recent_start, seq_lens, seq_ids, n_seqs,
-                           max_recent, out, ws, ws_bytes, &p);
+                           max_recent, out, status, ws, ws_bytes, &p);
   if (rc || n_seqs == 0) return rc;
   return finish(sfi::launch_attention(p, shape->head_dim, shape->dtype, out, lse,
                                       reinterpret_cast<hipStream_t>(stream)));
@@ -470,8 +474,8 @@ int sfi_decode_attn(const sfi_shape* shape, int32_t window, const float* q,
                     const int32_t* recent_start, const int32_t* seq_lens,
                     const int32_t* fast_ids, const int32_t* slow_ids, int32_t n_seqs,
                     int32_t max_recent, int32_t max_seq_len, float* out, float* logits,
-                    int64_t logits_stride, float* lse, void* ws, size_t ws_bytes,
-                    void* stream) {
+                    int64_t logits_stride, float* lse, uint32_t* status, void* ws,
+                    size_t ws_bytes, void* stream) {
   sfi_shape sw;
   int rc = window_shape(shape, window, &sw);
   if (rc) return rc;
@@ -483,11 +487,11 @@ int sfi_decode_attn(const sfi_shape* shape, int32_t window, const float* q,
   char* w8 = reinterpret_cast<char*>(ws);
   sfi::AttnParams pf, ps;
   if ((rc = prep_fast(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache, v_cache,
-                      block_table, recent_start, seq_lens, fast_ids, n_seqs, max_recent, out, ws,
-                      wf, &pf)))
+                      block_table, recent_start, seq_lens, fast_ids, n_seqs, max_recent, out,
+                      status, ws, wf, &pf)))
     return rc;
   if ((rc = prep_slow(&sw, window, q_win, k_cache, v_cache, block_table, seq_lens, slow_ids,
-                      n_seqs, max_seq_len, out, logits, logits_stride, lse, w8 + wf,
+                      n_seqs, max_seq_len, out, logits, logits_stride, lse, status, w8 + wf,
                       ws_bytes - wf, &ps)))
     return rc;
   if (n_seqs == 0) return SFI_OK;

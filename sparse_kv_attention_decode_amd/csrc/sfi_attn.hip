@@ -74,6 +74,24 @@ __device__ __forceinline__ SplitRange split_range(const AttnParams& p, int b, in
   return sr;
 }
 
+// Device-side contracts of row b (and KV head g): a broken one is clamped by the kernels
+// and reported in the call's status word.  Called by one lane of the first split.
+__device__ void report_contracts(const AttnParams& p, int b, int g) {
+  uint32_t f = 0;
+  const int raw_n = p.seq_lens[b];
+  if (raw_n < 0 || raw_n > p.max_len) f |= SFI_DEV_SEQ_LEN;
+  if (p.fast) {
+    const int N = min(max(raw_n, 0), p.max_len);
+    const int pl = p.packed_len[b * p.Hkv + g];
+    if (pl < 0 || pl > p.packed_cap) f |= SFI_DEV_PACKED_LEN;
+    const int rs = p.recent_start[b];
+    if (rs < 0 || rs > N ||
+        (N + kPage - 1) / kPage - rs / kPage > (p.nsplit - p.nsplit_a) * p.tps_b)
+      f |= SFI_DEV_RECENT;
+  }
+  if (f) atomicOr(p.status, f);
+}
+
 __device__ __forceinline__ void write_empty_partial(const AttnParams& p, size_t pidx, int D,
                                                     int lane) {
   for (int h = lane; h < p.G; h += kWave) {
@@ -129,6 +147,7 @@ __device__ __forceinline__ void attn_partial_bf16(AttnParams p, int work, Bf16Ld
   const int i = ig / p.Hkv;
   const int b = uniform(p.seq_ids[i]);
   if (b < 0) return;  // unused slot of the row list (workgroup-uniform)
+  if (split == 0 && p.status && threadIdx.x == 0) report_contracts(p, b, g);
   const int r = lane & 15;
   const int qd = lane >> 4;
   const size_t pidx = (size_t)ig * p.nsplit + split;
@@ -440,6 +459,7 @@ __device__ __forceinline__ void attn_partial_f32(AttnParams p, int work, F32Lds<
   const int i = ig / p.Hkv;
   const int b = uniform(p.seq_ids[i]);
   if (b < 0) return;  // unused slot of the row list
+  if (split == 0 && p.status && threadIdx.x == 0) report_contracts(p, b, g);
   // clamped: a length past the call's bound cannot send an index out of the buffers
   const int N = min(max(uniform(p.seq_lens[b]), 0), p.max_len);
   const size_t pidx = (size_t)ig * p.nsplit + split;

@@ -38,6 +38,7 @@ struct AttnParams {
   const int32_t* packed_len;   // fast only
   const int32_t* recent_start; // fast only
   float* logits;               // slow only, may be null
+  uint32_t* status;            // device contract flags (sfi_device_status), may be null
   int64_t logits_stride;
   float* part_m;
   float* part_l;
@@ -109,7 +110,7 @@ hipError_t launch_pack_update(const sfi_shape& s, const sfi_select_params& prm,
                               const int32_t* block_table, const int32_t* sel_idx,
                               const int32_t* seq_ids, int n_seqs, void* packed_k, void* packed_v,
                               int32_t* packed_pos, int32_t* packed_len, int packed_cap,
-                              int32_t* slot_map, int64_t map_stride, void* ws,
+                              int32_t* slot_map, int64_t map_stride, uint32_t* status, void* ws,
                               hipStream_t stream);
 
 hipError_t launch_pack(const sfi_shape& s, const sfi_select_params& prm, const void* k_cache,

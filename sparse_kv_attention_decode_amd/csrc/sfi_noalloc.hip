@@ -51,7 +51,7 @@ int sfi_fast_attn_noalloc(const sfi_shape* shape, const float* q, const void* pa
                           const void* k_cache, const void* v_cache, const int32_t* block_table,
                           const int32_t* recent_start, const int32_t* seq_lens,
                           const int32_t* seq_ids, int32_t n_seqs, int32_t max_recent,
-                          float* out, float* lse, void* stream) {
+                          float* out, float* lse, uint32_t* status, void* stream) {
   // Validate every argument against a stand-in workspace of the maximum size (never
   // dereferenced) before touching the device, so argument errors come back exactly as
   // sfi_fast_attn returns them; then reject calls whose partials do not fit the array.
@@ -59,7 +59,7 @@ int sfi_fast_attn_noalloc(const sfi_shape* shape, const float* q, const void* pa
   void* const probe = reinterpret_cast<void*>(uintptr_t(256));
   int rc = sfi_fast_attn(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache,
                          v_cache, block_table, recent_start, seq_lens, seq_ids, 0, max_recent,
-                         out, lse, probe, kScratchBytes, stream);
+                         out, lse, status, probe, kScratchBytes, stream);
   if (rc) return rc;
   if (n_seqs < 0 || n_seqs > shape->batch) return SFI_E_ARG;
   if (n_seqs == 0) return SFI_OK;
@@ -70,7 +70,7 @@ int sfi_fast_attn_noalloc(const sfi_shape* shape, const float* q, const void* pa
   if ((rc = scratch_for(s, &ws))) return rc;
   return sfi_fast_attn(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache, v_cache,
                        block_table, recent_start, seq_lens, seq_ids, n_seqs, max_recent, out,
-                       lse, ws, kScratchBytes, stream);
+                       lse, status, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -148,6 +148,7 @@ struct UpdArgs {
   int32_t* cnt_valid;  // [n_ig][nc_sel]
   int32_t* free_slot;  // [n_ig][K]
   int32_t* plen_old;   // [n_ig] held length before this update (written by kernel 3)
+  uint32_t* status;    // device contract flags, may be null
   int Hkv, K, n_sink, cap, nc_sel, nc_slot, max_pages, row_bytes;
 };
 
@@ -387,9 +388,10 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_assign(UpdArgs a) {
         slot = j < (uint32_t)sh[2] ? fslot[j] : plen + (int)(j - (uint32_t)sh[2]);
       ++j;
       // The counts make every slot < n_sink + K_eff <= cap; a slot outside the buffer can
-      // only come from corrupted state and is dropped (position -1 in the copy list)
-      // rather than written.
+      // only come from state these calls did not maintain: it is dropped (position -1 in
+      // the copy list) rather than written, and reported in the status word.
       const bool in_buf = slot >= a.n_sink && slot < a.cap;
+      if (!in_buf && a.status) atomicOr(a.status, (uint32_t)SFI_DEV_PACK_SLOT);
       if (in_buf) {
         ppos[slot] = q[i];
         if (in_map(a, q[i])) map[q[i]] = slot;
@@ -468,7 +470,7 @@ hipError_t launch_pack_update(const sfi_shape& s, const sfi_select_params& prm,
                               const int32_t* block_table, const int32_t* sel_idx,
                               const int32_t* seq_ids, int n_seqs, void* packed_k, void* packed_v,
                               int32_t* packed_pos, int32_t* packed_len, int packed_cap,
-                              int32_t* slot_map, int64_t map_stride, void* ws,
+                              int32_t* slot_map, int64_t map_stride, uint32_t* status, void* ws,
                               hipStream_t stream) {
   const int n_ig = n_seqs * s.num_kv_heads;
   UpdArgs a;
@@ -496,6 +498,7 @@ hipError_t launch_pack_update(const sfi_shape& s, const sfi_select_params& prm,
   a.plen = packed_len;
   a.map = slot_map;
   a.map_stride = map_stride;
+  a.status = status;
   a.Hkv = s.num_kv_heads;
   a.K = prm.top_k;
   a.n_sink = prm.n_sink;

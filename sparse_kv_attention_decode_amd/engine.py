@@ -271,6 +271,9 @@ class Engine:
         if device_control:
             self._init_device_control(tokens, boundary_tokens)
         self.dbg = dbg_scores
+        # Device contract flags (sfi_device_status) of every call the engine makes; they stay
+        # 0 while the lengths, edges and packed state the engine maintains are consistent.
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.graph = None
         self.graphs = {}
         self._calls = 0
@@ -387,7 +390,7 @@ class Engine:
                 shp, win, P["q"] + s * lb.q_step, P["qw"] + s * lb.qw_step, P["pk"], P["pv"],
                 P["pl"], self.packed_cap, P["k"], P["v"], P["bt"], rs_p, sl_p, fast_p, slow_p,
                 B, self.max_recent, self.max_len, P["out"], P["z"], self.stride, P["lse"],
-                ws_dec, ws_dec_n, h1))
+                self._st, ws_dec, ws_dec_n, h1))
             k = li % len(self.sel_streams)
             s2, h2 = self.sel_streams[k], self._h2[k]
             ws_sel, ws_sel_n = self._ws_sel[k]
@@ -497,6 +500,7 @@ class Engine:
         if self.device_control:
             self._ws["decode"] = (self.ws_decode.data_ptr(), self.ws_decode.numel())
         self._dbg_p = self.dbg_buf.data_ptr() if self.dbg_buf is not None else None
+        self._st = self.status.data_ptr()
         for lb in self.layers:
             lb.ptr = {k: getattr(lb, a).data_ptr() for k, a in (
                 ("k", "k_cache"), ("v", "v_cache"), ("bt", "block_table"), ("q", "q_all"),
@@ -557,7 +561,8 @@ class Engine:
                     self._ok("sfi_fast_attn", lib.sfi_fast_attn(
                         shp, P["q"] + s * lb.q_step, P["pk"], P["pv"], P["pl"],
                         self.packed_cap, P["k"], P["v"], P["bt"], rstart, seq_len, self._all_p,
-                        B, self.max_recent, P["out"], None, ws_fast, ws_fast_n, self._h1))
+                        B, self.max_recent, P["out"], None, self._st, ws_fast, ws_fast_n,
+                        self._h1))
             pool = g.pool()
             self.graphs[s] = g
         self.graph = self.graphs or None
@@ -568,7 +573,8 @@ class Engine:
         if self.incremental_pack:
             self._ok("sfi_pack_update", self._lib.sfi_pack_update(
                 self._shp, self._prm, P["k"], P["v"], P["bt"], P["sel"], ids, n, P["pk"],
-                P["pv"], P["pp"], P["pl"], self.packed_cap, P["map"], self.stride, ws, ws_n, h))
+                P["pv"], P["pp"], P["pl"], self.packed_cap, P["map"], self.stride, self._st, ws,
+                ws_n, h))
         else:
             self._ok("sfi_pack", self._lib.sfi_pack(
                 self._shp, self._prm, P["k"], P["v"], P["bt"], P["sel"], ids, n, P["pk"],
@@ -686,7 +692,8 @@ class Engine:
             if dense_only:
                 timed(li, "dense", db, lambda: ok("sfi_slow_attn", lib.sfi_slow_attn(
                     shp, q, P["k"], P["v"], P["bt"], seq_len, self._all_p, w.batch,
-                    self.max_len, P["out"], None, 0, P["lse"], ws_slow, ws_slow_n, h1)))
+                    self.max_len, P["out"], None, 0, P["lse"], self._st, ws_slow, ws_slow_n,
+                    h1)))
                 continue
             if lb.pack_pending:
                 s1.wait_event(lb.ev_pack)
@@ -695,14 +702,14 @@ class Engine:
                 timed(li, "fast", fb, lambda: ok("sfi_fast_attn", lib.sfi_fast_attn(
                     shp, q, P["pk"], P["pv"], P["pl"], self.packed_cap, P["k"], P["v"],
                     P["bt"], rstart, seq_len, fast_ids, m_fast, self.max_recent, P["out"],
-                    None, ws_fast, ws_fast_n, h1)))
+                    None, self._st, ws_fast, ws_fast_n, h1)))
             if n_slow:
                 qw = P["qw"] + s * lb.qw_step
                 timed(li, "slow", db, lambda: ok(
                     "sfi_slow_attn_window", lib.sfi_slow_attn_window(
                         shp, win, qw, P["k"], P["v"], P["bt"], seq_len, slow_ids, m_slow,
-                        self.max_len, P["out"], P["z"], self.stride, P["lse"], ws_slow,
-                        ws_slow_n, h1)))
+                        self.max_len, P["out"], P["z"], self.stride, P["lse"], self._st,
+                        ws_slow, ws_slow_n, h1)))
                 if pace and self.sel_lookahead > 0:
                     lb.ev_attn.record(s1)
                     pending.append((li, lb, P))
@@ -752,6 +759,12 @@ class Engine:
             if lb.pack_pending:
                 self.stream1.wait_event(lb.ev_pack)
                 lb.pack_pending = False
+
+    def device_status(self) -> int:
+        """The contract flags the engine's calls reported so far (waits for the device)."""
+        self.join()
+        torch.cuda.synchronize(self.device)
+        return int(self.status.item())
 
     def mode(self, s: int) -> np.ndarray:
         return self.plan.mode[:, s]

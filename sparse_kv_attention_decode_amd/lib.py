@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libsfi.so")
 SFI_OK, SFI_E_ARG, SFI_E_UNSUPPORTED, SFI_E_ALIGN, SFI_E_WORKSPACE, SFI_E_CAPACITY, SFI_E_HIP = (
     0, -1, -2, -3, -4, -5, -6)
 SFI_BF16, SFI_F32 = 0, 1
+# device contract flags (enum sfi_device_status)
+SFI_DEV_SEQ_LEN, SFI_DEV_PACKED_LEN, SFI_DEV_RECENT, SFI_DEV_PACK_SLOT = 1, 2, 4, 8
 
 EXPORTS = ["sfi_abi_version", "sfi_status_str", "sfi_slow_attn_ws", "sfi_fast_attn_ws",
            "sfi_select_ws", "sfi_packed_cap", "sfi_key_norms", "sfi_slow_attn", "sfi_select",
@@ -67,14 +69,14 @@ _SIGS = {
     "sfi_packed_cap": (_I32, [_PRM]),
     "sfi_key_norms": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P]),
     "sfi_slow_attn": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I64, _P,
-                                     _P, _SZ, _P]),
+                                     _P, _P, _SZ, _P]),
     "sfi_select": (ctypes.c_int, [_SHP, _PRM, _P, _I64, _P, _P, _I64, _P, _P, _I32, _I32, _P, _P,
                                   _P, _SZ, _P]),
     "sfi_pack": (ctypes.c_int, [_SHP, _PRM, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32, _P]),
     "sfi_slow_attn_window_ws": (_SZ, [_SHP, _I32, _I32, _I32]),
     "sfi_select_window_ws": (_SZ, [_SHP, _PRM, _I32, _I32, _I32]),
     "sfi_slow_attn_window": (ctypes.c_int, [_SHP, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _P,
-                                            _P, _I64, _P, _P, _SZ, _P]),
+                                            _P, _I64, _P, _P, _P, _SZ, _P]),
     "sfi_select_window": (ctypes.c_int, [_SHP, _PRM, _I32, _P, _I64, _P, _P, _I64, _P, _P, _I32,
                                          _I32, _P, _P, _P, _SZ, _P]),
     "sfi_step_control": (ctypes.c_int, [_SHP, _PRM, _I32, _I32, _P, _P, _I32, _P, _P, _P, _P,
@@ -82,14 +84,15 @@ _SIGS = {
     "sfi_kv_append": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I64, _P]),
     "sfi_decode_attn_ws": (_SZ, [_SHP, _I32, _I32, _I32, _I32, _I32]),
     "sfi_decode_attn": (ctypes.c_int, [_SHP, _I32, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
-                                       _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _SZ, _P]),
+                                       _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _P, _P, _SZ,
+                                       _P]),
     "sfi_pack_update_ws": (_SZ, [_SHP, _PRM, _I32]),
     "sfi_pack_update": (ctypes.c_int, [_SHP, _PRM, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32,
-                                       _P, _I64, _P, _SZ, _P]),
+                                       _P, _I64, _P, _P, _SZ, _P]),
     "sfi_fast_attn": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32,
-                                     _I32, _P, _P, _P, _SZ, _P]),
+                                     _I32, _P, _P, _P, _P, _SZ, _P]),
     "sfi_fast_attn_noalloc": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P,
-                                             _I32, _I32, _P, _P, _P]),
+                                             _I32, _I32, _P, _P, _P, _P]),
 }
 
 
@@ -196,23 +199,23 @@ def sfi_key_norms(shape, k_cache, block_table, seq_lens, seq_ids, n_seqs, pos_be
 
 def sfi_slow_attn(shape, q, k_cache, v_cache, block_table, seq_lens, seq_ids, n_seqs,
                   max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes=None,
-                  stream=None) -> None:
+                  stream=None, status=None) -> None:
     ws_bytes = ws.numel() if ws_bytes is None else ws_bytes
     rc = load().sfi_slow_attn(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                               _ptr(block_table), _ptr(seq_lens), _ptr(seq_ids), n_seqs,
                               max_seq_len, _ptr(out), _ptr(logits), logits_stride, _ptr(lse),
-                              _ptr(ws), ws_bytes, _stream(stream))
+                              _ptr(status), _ptr(ws), ws_bytes, _stream(stream))
     _check("sfi_slow_attn", rc)
 
 
 def sfi_slow_attn_window(shape, window, q_win, k_cache, v_cache, block_table, seq_lens, seq_ids,
                          n_seqs, max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes=None,
-                         stream=None) -> None:
+                         stream=None, status=None) -> None:
     ws_bytes = ws.numel() if ws_bytes is None else ws_bytes
     rc = load().sfi_slow_attn_window(ctypes.byref(shape), window, _ptr(q_win), _ptr(k_cache),
                                      _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
                                      _ptr(seq_ids), n_seqs, max_seq_len, _ptr(out), _ptr(logits),
-                                     logits_stride, _ptr(lse), _ptr(ws), ws_bytes,
+                                     logits_stride, _ptr(lse), _ptr(status), _ptr(ws), ws_bytes,
                                      _stream(stream))
     _check("sfi_slow_attn_window", rc)
 
@@ -251,24 +254,25 @@ def sfi_pack(shape, params, k_cache, v_cache, block_table, sel_idx, seq_ids, n_s
 
 def sfi_fast_attn(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache, v_cache,
                   block_table, recent_start, seq_lens, seq_ids, n_seqs, max_recent, out, lse,
-                  ws, ws_bytes=None, stream=None) -> None:
+                  ws, ws_bytes=None, stream=None, status=None) -> None:
     ws_bytes = ws.numel() if ws_bytes is None else ws_bytes
     rc = load().sfi_fast_attn(ctypes.byref(shape), _ptr(q), _ptr(packed_k), _ptr(packed_v),
                               _ptr(packed_len), packed_cap, _ptr(k_cache), _ptr(v_cache),
                               _ptr(block_table), _ptr(recent_start), _ptr(seq_lens),
                               _ptr(seq_ids), n_seqs, max_recent, _ptr(out), _ptr(lse),
-                              _ptr(ws), ws_bytes, _stream(stream))
+                              _ptr(status), _ptr(ws), ws_bytes, _stream(stream))
     _check("sfi_fast_attn", rc)
 
 
 def sfi_fast_attn_noalloc(shape, q, packed_k, packed_v, packed_len, packed_cap, k_cache,
                           v_cache, block_table, recent_start, seq_lens, seq_ids, n_seqs,
-                          max_recent, out, lse, stream=None) -> None:
+                          max_recent, out, lse, stream=None, status=None) -> None:
     rc = load().sfi_fast_attn_noalloc(ctypes.byref(shape), _ptr(q), _ptr(packed_k),
                                       _ptr(packed_v), _ptr(packed_len), packed_cap,
                                       _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                       _ptr(recent_start), _ptr(seq_lens), _ptr(seq_ids), n_seqs,
-                                      max_recent, _ptr(out), _ptr(lse), _stream(stream))
+                                      max_recent, _ptr(out), _ptr(lse), _ptr(status),
+                                      _stream(stream))
     _check("sfi_fast_attn_noalloc", rc)
 
 
@@ -298,15 +302,15 @@ def sfi_decode_attn_ws(shape, window, n_seqs, packed_cap, max_recent, max_seq_le
 def sfi_decode_attn(shape, window, q, q_win, packed_k, packed_v, packed_len, packed_cap, k_cache,
                     v_cache, block_table, recent_start, seq_lens, fast_ids, slow_ids, n_seqs,
                     max_recent, max_seq_len, out, logits, logits_stride, lse, ws, ws_bytes=None,
-                    stream=None) -> None:
+                    stream=None, status=None) -> None:
     ws_bytes = ws.numel() if ws_bytes is None else ws_bytes
     rc = load().sfi_decode_attn(ctypes.byref(shape), window, _ptr(q), _ptr(q_win),
                                 _ptr(packed_k), _ptr(packed_v), _ptr(packed_len), packed_cap,
                                 _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                 _ptr(recent_start), _ptr(seq_lens), _ptr(fast_ids),
                                 _ptr(slow_ids), n_seqs, max_recent, max_seq_len, _ptr(out),
-                                _ptr(logits), logits_stride, _ptr(lse), _ptr(ws), ws_bytes,
-                                _stream(stream))
+                                _ptr(logits), logits_stride, _ptr(lse), _ptr(status), _ptr(ws),
+                                ws_bytes, _stream(stream))
     _check("sfi_decode_attn", rc)
 
 
@@ -316,11 +320,11 @@ def sfi_pack_update_ws(shape, params, n_seqs) -> int:
 
 def sfi_pack_update(shape, params, k_cache, v_cache, block_table, sel_idx, seq_ids, n_seqs,
                     packed_k, packed_v, packed_pos, packed_len, packed_cap, slot_map, map_stride,
-                    ws, ws_bytes=None, stream=None) -> None:
+                    ws, ws_bytes=None, stream=None, status=None) -> None:
     ws_bytes = ws.numel() if ws_bytes is None else ws_bytes
     rc = load().sfi_pack_update(ctypes.byref(shape), ctypes.byref(params), _ptr(k_cache),
                                 _ptr(v_cache), _ptr(block_table), _ptr(sel_idx), _ptr(seq_ids),
                                 n_seqs, _ptr(packed_k), _ptr(packed_v), _ptr(packed_pos),
                                 _ptr(packed_len), packed_cap, _ptr(slot_map), map_stride,
-                                _ptr(ws), ws_bytes, _stream(stream))
+                                _ptr(status), _ptr(ws), ws_bytes, _stream(stream))
     _check("sfi_pack_update", rc)

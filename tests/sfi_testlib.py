@@ -132,3 +132,31 @@ def oracle_schedule(w, flags, plan=None) -> np.ndarray:
 def oracle_layer_arrays(d: dict, b: int):
     """fp64 host copies of row b: q [S, Hq, D], K/V [Hkv, total, D]."""
     return host64(d["q"][:, b]), host64(d["K"][b]), host64(d["V"][b])
+
+
+def model_pack_update(ppos, plen, sel, n_sink):
+    """Slot-by-slot state of one (row, KV head) of the packed buffer after sfi_pack_update,
+    from the order the call documents: ppos [cap] positions per slot (-1 empty), plen the
+    held length before the update, sel the new selection (ascending, valid entries only).
+
+    An empty buffer (plen 0) or a selection smaller than what is held is rebuilt in the
+    full pack's order: sink rows, then sel.  Otherwise every held row whose position stays
+    selected keeps its slot; the slots of the others are freed, in ascending slot order; the
+    newly selected positions, in ascending order, take the freed slots first and then the
+    slots from the old end on.  Returns (ppos', plen')."""
+    ppos = [int(x) for x in ppos]
+    cap = len(ppos)
+    sel = [int(x) for x in sel]
+    keff = len(sel)
+    if plen == 0 or keff < max(0, plen - n_sink):
+        new = list(range(n_sink)) + sel
+        return new + [-1] * (cap - len(new)), n_sink + keff
+    held = {ppos[s]: s for s in range(n_sink, plen)}
+    chosen = set(sel)
+    free = [s for s in range(n_sink, plen) if ppos[s] not in chosen]
+    added = [p for p in sel if p not in held]
+    new = list(ppos)
+    for j, p in enumerate(added):
+        slot = free[j] if j < len(free) else plen + (j - len(free))
+        new[slot] = p
+    return new, n_sink + keff

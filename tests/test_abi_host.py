@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     assert sorted(L.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert L.sfi_abi_version() == 7
+    assert L.sfi_abi_version() == 8
 
 
 def test_status_strings():
@@ -62,7 +62,7 @@ def _slow(shape, **over):
     a.update(over)
     return L.load().sfi_slow_attn(ctypes.byref(shape), a["q"], a["k"], a["v"], a["bt"], a["sl"],
                                   a["ids"], a["n"], a["maxlen"], a["out"], a["logits"],
-                                  a["stride"], a["lse"], a["ws"], a["wsb"], None)
+                                  a["stride"], a["lse"], None, a["ws"], a["wsb"], None)
 
 
 def test_slow_attn_validation():
@@ -166,8 +166,8 @@ def test_window_calls_validate_and_size_like_the_widened_shape():
         a = dict(q=FAKE, n=1, ws=FAKE, wsb=1 << 40)
         a.update(over)
         return lib.sfi_slow_attn_window(ctypes.byref(s), win, a["q"], FAKE, FAKE, FAKE, FAKE,
-                                        FAKE, a["n"], 100, FAKE, FAKE, 128, FAKE, a["ws"],
-                                        a["wsb"], None)
+                                        FAKE, a["n"], 100, FAKE, FAKE, 128, FAKE, None,
+                                        a["ws"], a["wsb"], None)
 
     def select_w(win):
         return lib.sfi_select_window(ctypes.byref(s), ctypes.byref(p), win, FAKE, 128, FAKE, FAKE,
@@ -209,8 +209,8 @@ def _fast(shape, **over):
     a.update(over)
     return L.load().sfi_fast_attn(ctypes.byref(shape), a["q"], a["pk"], a["pv"], a["pl"],
                                   a["cap"], a["k"], a["v"], a["bt"], a["rs"], a["sl"], a["ids"],
-                                  a["n"], a["maxrec"], a["out"], a["lse"], a["ws"], a["wsb"],
-                                  None)
+                                  a["n"], a["maxrec"], a["out"], a["lse"], None, a["ws"],
+                                  a["wsb"], None)
 
 
 def test_fast_attn_validation():
@@ -231,7 +231,8 @@ def _fast_noalloc(shape, **over):
     a.update(over)
     return L.load().sfi_fast_attn_noalloc(
         ctypes.byref(shape), a["q"], a["pk"], a["pv"], a["pl"], a["cap"], a["k"], a["v"],
-        a["bt"], a["rs"], a["sl"], a["ids"], a["n"], a["maxrec"], a["out"], a["lse"], None)
+        a["bt"], a["rs"], a["sl"], a["ids"], a["n"], a["maxrec"], a["out"], a["lse"], None,
+        None)
 
 
 def test_fast_attn_noalloc_validation():

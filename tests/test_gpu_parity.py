@@ -11,7 +11,7 @@ from oracle import sfi_oracle as O
 from workload import get
 from workload.gen import make_layer
 from sfi_testlib import (check_lse, check_logits, check_out, explain_selection_diff,
-                         host64, oracle_layer_arrays, oracle_schedule)
+                         host64, model_pack_update, oracle_layer_arrays, oracle_schedule)
 
 pytestmark = pytest.mark.gpu
 
@@ -278,6 +278,7 @@ def test_trajectory_lockstep(name, win, sliding, inc, over):
                     rstart[b] = O.recent_start_sliding(N, w.n_sink, w.n_recent)
                 o, lse = O.fast_attention(q[s], K, V, packed[b], rstart[b], N)
                 worst = max(worst, check_out(out[b], o, f"fast s={s} b={b}"))
+    assert eng.device_status() == 0
     print(f"{name} window {win} sliding {sliding}: {n_slow} slow / {n_fast} fast steps, "
           f"worst row rel err {worst:.2e}")
 
@@ -501,6 +502,7 @@ def test_edge_cases(case):
         else:
             o, _ = O.fast_attention(q[s], K, V, packed, rstart, N)
         check_out(host64(lb.out[0]), o, f"{case} s={s}")
+    assert eng.device_status() == 0
 
 
 def test_ragged_batch_lengths():
@@ -631,6 +633,7 @@ def test_full_size_sampled(name):
         o, _ = O.fast_attention(q[1], K, V, pos, O.recent_start_at(N, w.n_sink, w.n_recent),
                                 w.seq_len(1))
         check_out(out1[b], o, f"{name} fast b={b}")
+    assert eng.device_status() == 0
 
 
 # ------------------------------------------------------------- Top-K selection paths
@@ -734,6 +737,7 @@ def test_pack_update_keeps_held_rows_and_adds_new_ones():
     ids = torch.tensor([0, 1], dtype=torch.int32, device=dev)
     cur = [[np.sort(rng.choice(np.arange(lo, hi), 200, replace=False)) for _ in range(8)]
            for _ in range(2)]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def apply(sets, ids, n):
         sel = torch.full((w.batch, w.num_kv_heads, w.top_k), -1, dtype=torch.int32)
@@ -741,10 +745,22 @@ def test_pack_update_keeps_held_rows_and_adds_new_ones():
             for g in range(w.num_kv_heads):
                 sel[b, g, :len(sets[b][g])] = torch.from_numpy(sets[b][g].astype(np.int32))
         lb.sel_idx.copy_(sel.to(dev))
+        prev_pos = lb.packed_pos.cpu().numpy()
+        prev_len = lb.packed_len.cpu().numpy()
         L.sfi_pack_update(eng.shape, eng.params, lb.k_cache, lb.v_cache, lb.block_table,
                           lb.sel_idx, ids, n, lb.packed_k, lb.packed_v, lb.packed_pos,
-                          lb.packed_len, eng.packed_cap, lb.slot_map, eng.stride, ws)
+                          lb.packed_len, eng.packed_cap, lb.slot_map, eng.stride, ws,
+                          status=status)
         torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        # the device's slot of every row equals the documented order, slot by slot
+        got = lb.packed_pos.cpu().numpy()
+        for b in [int(x) for x in ids.cpu().numpy() if x >= 0]:
+            for g in range(w.num_kv_heads):
+                want, wlen = model_pack_update(prev_pos[b, g], int(prev_len[b, g]),
+                                               sets[b][g], w.n_sink)
+                np.testing.assert_array_equal(got[b, g], want, err_msg=f"row {b} head {g}")
+                assert int(lb.packed_len[b, g]) == wlen
 
     # first call: an empty buffer is built in the full pack's order
     apply(cur, ids, 2)
@@ -804,6 +820,7 @@ def test_pack_update_rebuilds_beside_a_busy_stream():
     ws = L.workspace(L.sfi_pack_update_ws(eng.shape, eng.params, w.batch), dev)
     ids = torch.tensor([0, 1], dtype=torch.int32, device=dev)
     busy = torch.cuda.Stream()
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     side = torch.cuda.Stream()
@@ -820,7 +837,7 @@ def test_pack_update_rebuilds_beside_a_busy_stream():
             L.sfi_pack_update(eng.shape, eng.params, lb.k_cache, lb.v_cache, lb.block_table,
                               lb.sel_idx, ids, 2, lb.packed_k, lb.packed_v, lb.packed_pos,
                               lb.packed_len, eng.packed_cap, lb.slot_map, eng.stride, ws,
-                              stream=side)
+                              stream=side, status=status)
 
     for rnd in range(6):
         n0 = int(rng.integers(3000, 3900))
@@ -852,6 +869,7 @@ def test_pack_update_rebuilds_beside_a_busy_stream():
         torch.cuda.synchronize()
         for b in range(2):
             _check_pack_state(w, lb, d, b, new[b], N)
+    assert int(status.item()) == 0
 
 
 def test_pack_update_full_size():
@@ -870,6 +888,7 @@ def test_pack_update_full_size():
             sel = lb.sel_idx[0].cpu().numpy()
             want = [sel[g][sel[g] >= 0] for g in range(w.num_kv_heads)]
             _check_pack_state(w, lb, d, 0, want, N, ordered=(s == slow[0]))
+    assert eng.device_status() == 0
     print("slow steps checked:", slow)
 
 
@@ -937,4 +956,47 @@ def test_full_stack_in_bench_configuration():
             else:
                 o, _ = O.fast_attention(q[s], K, V, packed[li], rstart, N)
                 check_out(host64(lb.out[0]), o, f"layer {li} step {s}")
+    assert eng.device_status() == 0
     print(f"checked slow step {s_slow} and graph-replayed fast step {s_fast}")
+
+
+def test_device_status_flags_broken_contracts():
+    """Lengths, packed lengths and recent edges that break a call's contract are clamped by
+    the kernels (no access leaves the buffers) and reported in the status word; consistent
+    arguments leave it at 0."""
+    w = get("qwen3_0p6b_8k").replace(batch=2, context=2000, steps=4, name="status_word")
+    d, eng, lb = _setup(w)
+    eng.step(0)
+    eng.join()
+    torch.cuda.synchronize()
+    assert eng.device_status() == 0
+    N = w.seq_len(1)
+    rs = O.recent_start_at(w.seq_len(0), w.n_sink, w.n_recent)
+    ids = eng.all_ids_d
+
+    def fast(lens, rstart, plen):
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        L.sfi_fast_attn(eng.shape, d["q"][1], lb.packed_k, lb.packed_v, plen, eng.packed_cap,
+                        lb.k_cache, lb.v_cache, lb.block_table, rstart, lens, ids, w.batch,
+                        eng.max_recent, lb.out, None, eng.ws_fast, status=st)
+        torch.cuda.synchronize()
+        return int(st.item())
+
+    full = lambda v: torch.full((w.batch,), v, dtype=torch.int32, device="cuda")  # noqa: E731
+    assert fast(full(N), full(rs), lb.packed_len) == 0
+    # a recent segment longer than max_recent (the edge moved back), an edge past N
+    assert fast(full(N), full(rs - eng.max_recent - 40), lb.packed_len) == L.SFI_DEV_RECENT
+    assert fast(full(N), full(N + 5), lb.packed_len) == L.SFI_DEV_RECENT
+    # packed_len beyond the buffer, negative
+    big = torch.full_like(lb.packed_len, eng.packed_cap + 16)
+    assert fast(full(N), full(rs), big) == L.SFI_DEV_PACKED_LEN
+    assert fast(full(N), full(rs), torch.full_like(lb.packed_len, -3)) == L.SFI_DEV_PACKED_LEN
+    # a row longer than the page table
+    assert fast(full(w.pages_per_seq * 16 + 7), full(rs), lb.packed_len) & L.SFI_DEV_SEQ_LEN
+    # slow call: a row longer than max_seq_len
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L.sfi_slow_attn(eng.shape, d["q"][0], lb.k_cache, lb.v_cache, lb.block_table,
+                    full(eng.max_len + 3), ids, w.batch, eng.max_len, lb.out, lb.logits,
+                    eng.stride, lb.lse, eng.ws_slow, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == L.SFI_DEV_SEQ_LEN

@@ -81,3 +81,41 @@ def test_plan_of_the_seeded_workloads_matches_the_oracle():
                                        w.n_recent, w.top_k, w.sliding_recent)
         np.testing.assert_array_equal(plan.mode, mode, err_msg=name)
         np.testing.assert_array_equal(plan.recent_start, edge, err_msg=name)
+
+
+def test_incremental_pack_slot_model():
+    """The slot arithmetic of the incremental pack (tests' model of the documented order,
+    which the GPU test compares slot by slot with the device) over seeded random selection
+    sequences: the buffer always holds exactly sink + selection, kept rows never move, freed
+    slots are refilled first in slot order, and nothing lies past the new length."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from sfi_testlib import model_pack_update
+    r = np.random.default_rng(9)
+    n_sink, K, lo, hi = 4, 60, 4, 400
+    cap = (n_sink + K + 15) // 16 * 16
+    for trial in range(40):
+        ppos, plen = [-1] * cap, 0
+        sel = np.sort(r.choice(np.arange(lo, hi), int(r.integers(10, K)), replace=False))
+        for step in range(12):
+            prev, prev_len = list(ppos), plen
+            ppos, plen = model_pack_update(ppos, plen, sel, n_sink)
+            assert plen == n_sink + len(sel)
+            assert ppos[:n_sink] == list(range(n_sink))
+            assert sorted(ppos[n_sink:plen]) == sorted(sel.tolist())
+            assert all(x == -1 for x in ppos[plen:])
+            rebuilt = prev_len == 0 or len(sel) < prev_len - n_sink
+            if rebuilt:
+                assert ppos[n_sink:plen] == sel.tolist()
+            else:
+                for s in range(n_sink, prev_len):           # kept rows keep their slot
+                    if prev[s] in set(sel.tolist()):
+                        assert ppos[s] == prev[s]
+                moved_in = [s for s in range(n_sink, plen) if ppos[s] != prev[s]]
+                freed = [s for s in range(n_sink, prev_len) if prev[s] not in set(sel.tolist())]
+                assert moved_in[:len(freed)] == freed        # freed slots are filled first
+            # next selection: keep most, swap a few, grow by 0-3 or shrink now and then
+            keep = r.choice(sel, int(len(sel) * r.uniform(0.7, 1.0)), replace=False)
+            pool = np.setdiff1d(np.arange(lo, hi), keep)
+            n_new = min(K, len(sel) + int(r.integers(-8, 4))) - len(keep)
+            sel = np.sort(np.concatenate([keep, r.choice(pool, max(0, n_new), replace=False)]))
