@@ -61,7 +61,7 @@ def _parse():
                     help="timed decode steps (default: the trajectory length)")
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default=BENCH_WORKLOAD)
-    ap.add_argument("--dense-steps", type=int, default=16,
+    ap.add_argument("--dense-steps", type=int, default=64,
                     help="steps of the Full-KV dense baseline timed after the main run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle CPU baseline sample (0 disables it)")
@@ -298,18 +298,17 @@ def main():
 
     dense = None
     if args.dense_steps > 0:
-        dt = []
+        # timed like the steps above: one event at each step boundary, created beforehand
         dense_timer = []
+        dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.dense_steps + 1)]
+        torch.cuda.synchronize()
         for k in range(args.dense_steps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(eng.stream1)
+            dev_ev[k].record(eng.stream1)
             eng.step(k % S, dense_only=True, timer=dense_timer,
                      time_every=max(1, args.time_every))
-            e1.record(eng.stream1)
-            dt.append((e0, e1))
+        dev_ev[args.dense_steps].record(eng.stream1)
         torch.cuda.synchronize()
-        dms = [a.elapsed_time(b) for a, b in dt]
+        dms = [dev_ev[k].elapsed_time(dev_ev[k + 1]) for k in range(args.dense_steps)]
         dk = [(e0.elapsed_time(e1), nb) for _, e0, e1, nb, _ in dense_timer]
         dense = {"step_ms": sum(dms) / len(dms),
                  "gbs": (sum(b for _, b in dk) / (sum(t for t, _ in dk) * 1e-3) / 1e9)

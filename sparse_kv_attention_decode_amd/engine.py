@@ -480,9 +480,14 @@ class Engine:
             self.paced = dense >= 8 << 20
         if self._lookahead_req is None:
             self.sel_lookahead = 2 if len(self.layers) > 2 else 0
-        # start of each step on stream 1, alternating by the engine's own step count
+        # Start of a step on stream 1, for the pacing of the slow step after it: recorded
+        # only at steps followed by a slow step (an event record costs a few microseconds
+        # of GPU time, as much as a short fast step's attention), alternating between two.
         self._ev_step = [torch.cuda.Event(), torch.cuda.Event()]
         self._nstep = 0
+        self._ev_cur = None   # recorded at the start of the last step issued, or None
+        self._ev_prev = None  # recorded at the start of the step before it, or None
+        self._has_slow = [bool(x) for x in self.plan.mode.any(axis=0)]
         self._shp = ctypes.byref(self.shape)
         self._prm = ctypes.byref(self.params)
         B = self.w.batch
@@ -610,8 +615,13 @@ class Engine:
             self._device_step(s, timer)
             return
         if not dense_only:
-            self._ev_step[self._nstep % 2].record(self.stream1)
-            self._nstep += 1
+            self._ev_prev = self._ev_cur
+            self._ev_cur = None
+            nxt = (s + 1) % self.w.steps
+            if self.paced and self._has_slow[nxt]:
+                self._ev_cur = self._ev_step[self._nstep % 2]
+                self._ev_cur.record(self.stream1)
+                self._nstep += 1
         if s == 0 and not dense_only:
             self._new_sequences()
         # The graph waits for every layer's pending pack before its first call, so the
@@ -670,7 +680,8 @@ class Engine:
                 if pace and not paced_wait[0]:
                     # stream 1 has finished every step before the previous one; the previous
                     # step and this step's first attention keep the GPU busy meanwhile
-                    self._ev_step[(self._nstep - 2) % 2].synchronize()
+                    if self._ev_prev is not None:
+                        self._ev_prev.synchronize()
                     paced_wait[0] = True
                 s2.wait_event(lb.ev_attn)
             ok("sfi_select_window", lib.sfi_select_window(
