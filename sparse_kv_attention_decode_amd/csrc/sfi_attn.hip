@@ -187,10 +187,11 @@ __device__ __forceinline__ void attn_partial_bf16(AttnParams p, int work, Bf16Ld
   };
   // A packed tile's address depends only on the row, the KV head and the tile index, so
   // a packed split requests its wave's first two tiles before the split's extent is known
-  // (indices clamped to the buffer's capacity); their latency overlaps the set-up below.
+  // (indices clamped to the split's share of the buffer's capacity, so no split fetches
+  // another's tiles); their latency overlaps the set-up below.
   u32x4_t ka[NC], va[NC], kb[NC], vb[NC];
   if (packed) {
-    const int last = p.packed_cap / kPage - 1;
+    const int last = min((split + 1) * p.tps, p.packed_cap / kPage) - 1;
     const int t0w = split * p.tps + wave;
     load_rows((size_t)min(t0w, last) * (kPage * D) + lane_off, ka, va);
     load_rows((size_t)min(t0w + NW, last) * (kPage * D) + lane_off, kb, vb);
