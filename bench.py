@@ -260,6 +260,10 @@ def main():
     slow_step = [bool(eng.plan.mode[:, k % S].any()) for k in range(steps)]
     fast_ms = [t for t, sl in zip(step_ms, slow_step) if not sl]
     slow_ms = [t for t, sl in zip(step_ms, slow_step) if sl]
+    # A fast step right after a slow step first waits for that step's Selector and pack (on
+    # their own streams); steady fast steps follow a fast step and carry no such tail.
+    steady_ms = [t for k, (t, sl) in enumerate(zip(step_ms, slow_step))
+                 if not sl and k > 0 and not slow_step[k - 1]]
 
     def agg(kind):
         ts = [(e0.elapsed_time(e1), nb, nc) for kd, e0, e1, nb, nc in timer if kd == kind]
@@ -378,11 +382,15 @@ def main():
         "detail": {
             "stack_steps_per_s": round(steps / (total_ms * 1e-3), 3),
             "fast_step_ms": mean(fast_ms), "slow_step_ms": mean(slow_ms),
+            "steady_fast_step_ms": mean(steady_ms),
             "n_fast_steps": len(fast_ms), "n_slow_steps": len(slow_ms),
+            "n_steady_fast_steps": len(steady_ms),
             "fast_attn": fast, "slow_attn": slow,
             "dense_step_ms": dense["step_ms"] if dense else None,
             "dense_attn_gbs": dense["gbs"] if dense else None,
             "fast_vs_dense": (dense["step_ms"] / mean(fast_ms)) if dense and fast_ms else None,
+            "steady_fast_vs_dense": (dense["step_ms"] / mean(steady_ms))
+            if dense and steady_ms else None,
             "mixed_vs_dense": (dense["step_ms"] / ms_per_step) if dense else None,
             "setup_s": round(setup_s, 1),
             "repeats": repeats,
