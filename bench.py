@@ -105,11 +105,10 @@ def _parse():
                          "unless --no-graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a device copy of known size (for counter calibration)")
-    ap.add_argument("--traffic-json",
-                    default=os.path.join(ROOT, "profiles",
-                                         "fast_attn_traffic_qwen3_4b_128k_36l.json"),
-                    help="HBM traffic per fast call measured with counters; used only when "
-                         "its workload and attention-kernel source hash match this run")
+    ap.add_argument("--traffic-json", default=None,
+                    help="HBM traffic per fast call measured with counters (default: "
+                         "profiles/fast_attn_traffic_<workload>.json); used only when its "
+                         "workload and attention-kernel source hash match this run")
     return ap.parse_args()
 
 
@@ -322,6 +321,8 @@ def main():
     ms_per_step = total_ms / steps
     value = steps * w.layers / (total_ms * 1e-3)
     traffic = None
+    if args.traffic_json is None:
+        args.traffic_json = os.path.join(ROOT, "profiles", f"fast_attn_traffic_{w.name}.json")
     if os.path.exists(args.traffic_json):
         try:
             import hashlib
