@@ -23,10 +23,13 @@ Parity status of each function:
   fast_attention, schedule, boundary_flags, step_control:
       pinned by tests (closed forms, library routines, brute force).
   key_norms: pinned (library norm).
-  prior: invariants pinned (normalisation, positivity, monotonicity); the functional form
-      of the two factors is a reading the pages do not fix -- parity unpinned for the form.
-  refine: special cases pinned (identity at α=0, local maxima at α_soft=1, ownership at
-      α_cross=1); intermediate α -- parity unpinned beyond those cases.
+  prior: pinned to its reading by a hand-derived example (the key-norm floor, the
+      distance N-1-j, the +1 terms and the normalisation) and by invariants (normalisation,
+      positivity, monotonicity).  The functional form itself is a reading the pages do not
+      fix: the pin checks the oracle against the reading, not the reading against the pages.
+  refine: pinned by a hand-derived worked example at α_soft = α_cross = 0.5 (dominance,
+      ownership with a tie, the refined products, Top-K with a tie) and by special cases
+      (identity at α=0, local maxima at α_soft=1, ownership at α_cross=1).
   refine_greedy (an alternative reading): pinned by a worked example, a plain
       quadratic simulation, its reductions (α_soft = 0 or R = 0) and hard NMS at α_soft = 1.
   adaptive_lambda, fuse_per_head (the clipped adaptive fusion weight, a reading): pinned by
@@ -215,7 +218,7 @@ def prior(norms: np.ndarray) -> np.ndarray:
       phi_key(g, j) = 1 / max(||k_{g,j}||, 1e-6)
       phi_pos(j)    = 1 + ln(1 + (N - 1 - j))       (grows with distance from the newest)
       r(g, j)       = phi_key * phi_pos / sum_{j'<N} phi_key * phi_pos
-    norms [Hkv, N] -> r [Hkv, N].  Parity unpinned for the form itself.
+    norms [Hkv, N] -> r [Hkv, N].  The form is a reading; the implementation is pinned to it.
     """
     a = np.asarray(norms, F64)
     Hkv, N = a.shape

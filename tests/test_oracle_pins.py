@@ -352,6 +352,14 @@ def test_key_norms_library():
     np.testing.assert_allclose(O.key_norms(K), np.sqrt((K ** 2).sum(-1)), rtol=1e-14)
 
 
+def test_prior_worked_example():
+    """The prior's form as read (key-norm floor, distance from the newest position counted
+    N-1-j, the +1 terms, the normalisation over [0, N)) against hand-derived values (golden)."""
+    g = json.load(open(os.path.join(GOLDEN, "prior_worked_example.json")))
+    np.testing.assert_allclose(O.prior(np.array(g["norms"])), np.array(g["r"]), rtol=1e-14,
+                               atol=0)
+
+
 def test_prior_invariants():
     norms = np.exp(rng.standard_normal((3, 50)))
     r = O.prior(norms)
