@@ -30,6 +30,8 @@
 //   k_topk_*     radix select of the K-th largest key spread over slices of 4096
 //                candidates (histogram, boundary-bin gather, a one-block select on the
 //                gathered bin in LDS, ordered parallel write); see the top-K section.
+//                Rows of at most four slices take one block per (row, head) instead
+//                (k_topk_small), which ranks the keys in a single launch.
 #include "sfi_device.h"
 #include "sfi_internal.h"
 
@@ -900,6 +902,31 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_final(TopkArgs a) {
   }
 }
 
+// Rows of at most kSmallSlices slices (16384 positions): one block per (row, head) ranks
+// the keys straight from global memory (topk_single_block), so the selection is one launch
+// instead of the four-kernel chain above, whose launches dominate at this size.
+constexpr int kSmallSlices = 4;
+
+__global__ __launch_bounds__(kTopkThreads) void k_topk_small(TopkArgs a) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t ckey[kCandCap];
+  __shared__ uint32_t cidx[kCandCap];
+  __shared__ uint32_t wsum[kTopkThreads / 64 + 1];
+  __shared__ uint32_t res[4];
+  const int tid = threadIdx.x;
+  const int ig = blockIdx.x;
+  const TopkRow row = topk_row(a, ig / a.Hkv);
+  if (row.b < 0) return;  // unused slot of the row list
+  int32_t* out = a.sel + ((size_t)row.b * a.Hkv + ig % a.Hkv) * a.K;
+  for (int k = row.keff + tid; k < a.K; k += kTopkThreads) out[k] = -1;
+  if (row.keff == 0 || row.keff == row.nC) {  // nothing to rank: none or every candidate
+    for (int k = tid; k < row.keff; k += kTopkThreads) out[k] = row.lo + k;
+    return;
+  }
+  topk_single_block(a.keys + (size_t)ig * a.kstride, a.kstride, row.nC, row.keff, row.lo, out,
+                    hist, ckey, cidx, wsum, res);
+}
+
 __global__ __launch_bounds__(kSliceThreads) void k_topk_write(TopkArgs a) {
   __shared__ uint32_t wsum[kSliceThreads / 64 + 1];
   const int tid = threadIdx.x;
@@ -1093,6 +1120,10 @@ hipError_t launch_select(const sfi_shape& s, const sfi_select_params& prm, const
   t.n_sink = prm.n_sink;
   t.n_recent = prm.n_recent;
   t.nslice = L.nslice;
+  if (L.nslice <= kSmallSlices) {
+    hipLaunchKernelGGL(k_topk_small, dim3(n_seqs * Hkv), dim3(kTopkThreads), 0, st, t);
+    return hipGetLastError();
+  }
   const dim3 slices(n_seqs * Hkv * L.nslice);
   hipLaunchKernelGGL(k_topk_hist, slices, dim3(kSliceThreads), 0, st, t);
   hipLaunchKernelGGL(k_topk_gather, slices, dim3(kSliceThreads), 0, st, t);

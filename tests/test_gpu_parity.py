@@ -699,6 +699,38 @@ def test_topk_ties_across_slices(levels):
     np.testing.assert_array_equal(sel[0], ref)
 
 
+@pytest.mark.parametrize("N,batch", [(16384, 2), (16385, 2), (3000, 3)])
+def test_topk_one_block_path_and_its_bound(N, batch):
+    """Rows of at most 16384 positions (four slices) are ranked by one block per (row, head);
+    longer ones by the four-kernel chain.  On both sides of the bound, with exact ties inside
+    the K-th score's level and rows of different lengths, the selection equals the oracle's
+    Top-K on the device's own scores."""
+    Hq, Hkv, D, K = 4, 2, 128, N // 3
+    stride = (N + 63) // 64 * 64
+    shape = L.make_shape(batch, Hq, Hkv, D, (N + 15) // 16, "bf16")
+    params = L.make_params(4, 64, K, 4, 0.0, 0.0, 0.0)  # lambda = 0: s = f; no refinement
+    j = torch.arange(stride, device="cuda")
+    level = (j * 7919) % 5  # five score levels interleaved over positions
+    logits = (-0.2 * level.float()).expand(batch, Hq, stride).contiguous()
+    lse = torch.zeros(batch, Hq, device="cuda")
+    key_norm = torch.ones(batch, Hkv, stride, device="cuda")
+    lens = [N - 97 * b for b in range(batch)]
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ids = torch.arange(batch, dtype=torch.int32, device="cuda")
+    sel = torch.full((batch, Hkv, K), -7, dtype=torch.int32, device="cuda")
+    dbg = torch.zeros(batch, Hkv, stride, dtype=torch.float32, device="cuda")
+    ws = L.workspace(L.sfi_select_ws(shape, params, batch, N), "cuda")
+    L.sfi_select(shape, params, logits, stride, lse, key_norm, stride, seq_lens, ids, batch, N,
+                 sel, dbg, ws)
+    torch.cuda.synchronize()
+    sel = sel.cpu().numpy()
+    for b in range(batch):
+        n = lens[b]
+        s = host64(dbg[b, :, :n])
+        ref = O.select_from_scores(s, n, 4, 64, K, 4, 0.0, 0.0)
+        np.testing.assert_array_equal(sel[b], ref)
+
+
 # ------------------------------------------------------------------ incremental pack
 def _check_pack_state(w, lb, d, b, want_pos, N, ordered=False):
     """Rows [0, packed_len) hold exactly sink + want_pos, each the stored row of its slot's
