@@ -211,7 +211,7 @@ def main():
                              device_control=True, tokens=gen_tokens(w, d["flags"]),
                              boundary_tokens=BOUNDARY_TOKENS, incremental_pack=inc)
             else:
-                eng = Engine(w, d["flags"], two_streams=not args.one_stream,
+                eng = Engine(w, d["flags"], two_streams=False if args.one_stream else None,
                              sel_streams=args.sel_streams,
                              incremental_pack=inc, paced=pace,
                              sel_lookahead=args.sel_lookahead)
@@ -339,7 +339,8 @@ def main():
         except (OSError, ValueError):
             traffic = None
     # pacing acts on host-scheduled steps with separate Selector streams only
-    paced_on = bool(eng.paced) and not args.device_control and not args.one_stream
+    one_stream = eng.sel_streams[0] is eng.stream1
+    paced_on = bool(eng.paced) and not args.device_control and not one_stream
     roof = None
     if fast:
         roof = {"bound": "hbm", "achieved": round(fast["gbs"], 1), "peak": PEAK_HBM_GBS,
@@ -369,7 +370,7 @@ def main():
                    "context": w.context, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "top_k": w.top_k, "n_recent": w.n_recent,
-                   "streams": 1 if args.one_stream else 1 + args.sel_streams,
+                   "streams": 1 if one_stream else 1 + len(eng.sel_streams),
                    "fast_step_graph": eng.graph is not None,
                    "evidence_window": w.evidence_window,
                    "lambda_clip": w.lambda_clip if w.lambda_clip >= 0 else None,

@@ -163,7 +163,7 @@ class LayerBuffers:
 
 
 class Engine:
-    def __init__(self, w, flags, device="cuda", two_streams: bool = True,
+    def __init__(self, w, flags, device="cuda", two_streams: Optional[bool] = None,
                  dbg_scores: bool = False, sel_streams: int = 2,
                  window: Optional[int] = None, device_control: bool = False,
                  tokens=None, boundary_tokens=None, max_recent: Optional[int] = None,
@@ -206,6 +206,15 @@ class Engine:
         # Decode queries pooled into the Selector's evidence at a slow step (1: the current
         # query only).
         self.window = int(w.evidence_window if window is None else window)
+        # two_streams: the Selector and pack run on Selector streams beside stream 1's
+        # attention (True) or on stream 1 itself (False).  None chooses when the stack is
+        # known (first step): Selector streams for several layers, stream 1 for one layer,
+        # whose Selector nothing can overlap (the next step's attention reads its pack) and
+        # where the cross-stream waits only add latency (measured on every one-layer
+        # workload: 8K 49.1K -> 54.0K, 1K 27.5K -> 35.6K, 32K x4 17.8K -> 19.7K, 64K x8
+        # 5.40K -> 5.88K layer steps/s).  Device-controlled engines keep their streams.
+        self._two_streams_req = two_streams
+        two_streams = True if two_streams is None else two_streams
         self.two_streams = two_streams
         flags_np = np.asarray(flags.cpu() if torch.is_tensor(flags) else flags)
         self.plan = make_plan(flags_np, w.context, w.refresh_budget, w.n_sink, w.n_recent,
@@ -264,8 +273,9 @@ class Engine:
         self.ws_sels = [L.workspace(sel_ws, dev) for _ in range(n_sel)]
         self.ws_sel = self.ws_sels[0]
         self.stream1 = torch.cuda.Stream(device=dev)
-        self.sel_streams = ([torch.cuda.Stream(device=dev) for _ in range(n_sel)]
-                            if two_streams else [self.stream1])
+        self._sel_streams_own = ([torch.cuda.Stream(device=dev) for _ in range(n_sel)]
+                                 if two_streams else [self.stream1])
+        self.sel_streams = self._sel_streams_own
         self.stream2 = self.sel_streams[0]
         self.layers: List[LayerBuffers] = []
         if device_control:
@@ -480,6 +490,11 @@ class Engine:
             self.paced = dense >= 8 << 20
         if self._lookahead_req is None:
             self.sel_lookahead = 2 if len(self.layers) > 2 else 0
+        if self._two_streams_req is None and not self.device_control:
+            self.sel_streams = ([self.stream1] if len(self.layers) == 1
+                                else self._sel_streams_own)
+            self.stream2 = self.sel_streams[0]
+            self.two_streams = self.sel_streams[0] is not self.stream1
         # Start of a step on stream 1, for the pacing of the slow step after it: recorded
         # only at steps followed by a slow step (an event record costs a few microseconds
         # of GPU time, as much as a short fast step's attention), alternating between two.
@@ -618,7 +633,7 @@ class Engine:
             self._ev_prev = self._ev_cur
             self._ev_cur = None
             nxt = (s + 1) % self.w.steps
-            if self.paced and self._has_slow[nxt]:
+            if self.paced and self._has_slow[nxt] and self.sel_streams[0] is not self.stream1:
                 self._ev_cur = self._ev_step[self._nstep % 2]
                 self._ev_cur.record(self.stream1)
                 self._nstep += 1
