@@ -731,6 +731,38 @@ def test_topk_one_block_path_and_its_bound(N, batch):
         np.testing.assert_array_equal(sel[b], ref)
 
 
+def test_select_at_maximum_length():
+    """The Selector at its longest KV length (2^22 positions: 1024 top-K slices of 4096
+    candidates, 1024 prior-normaliser chunks), from seeded logits, lse and key norms: fused
+    scores against the oracle pipeline, exact Top-K on the device's own scores, and the
+    near-tie rule end to end."""
+    Hq, Hkv, D, N, K = 2, 1, 128, 1 << 22, 65536
+    n_sink, n_recent, R, lam, a_soft, a_cross = 4, 1024, 4, 0.3, 0.5, 0.5
+    rng = np.random.default_rng(20261203)
+    z = (3.0 * rng.standard_normal((Hq, N))).astype(np.float32)
+    zmax = z.max(axis=1, keepdims=True).astype(np.float64)
+    lse64 = zmax[:, 0] + np.log(np.exp(z.astype(np.float64) - zmax).sum(axis=1))
+    lse32 = lse64.astype(np.float32)
+    norms = rng.lognormal(0.0, 0.5, (Hkv, N)).astype(np.float32)
+    stride = N
+    shape = L.make_shape(1, Hq, Hkv, D, N // 16, "bf16")
+    params = L.make_params(n_sink, n_recent, K, R, lam, a_soft, a_cross)
+    logits = torch.from_numpy(z).reshape(1, Hq, N).cuda()
+    lse = torch.from_numpy(lse32).reshape(1, Hq).cuda()
+    key_norm = torch.from_numpy(norms).reshape(1, Hkv, N).cuda()
+    sel, dbg = _select_direct(shape, params, logits, lse, key_norm, N, stride)
+    s_gpu = dbg[0]
+    ref_sel = O.select_from_scores(s_gpu, N, n_sink, n_recent, K, R, a_soft, a_cross)
+    np.testing.assert_array_equal(sel[0], ref_sel)
+    # the oracle pipeline on the same inputs (p from the logits and the stored lse)
+    p = np.exp(z.astype(np.float64) - lse32.astype(np.float64)[:, None])
+    oracle_sel = O.select(p, norms.astype(np.float64), N, Hkv, n_sink, n_recent, K, R, a_soft,
+                          a_cross, lam, None)
+    np.testing.assert_allclose(s_gpu, oracle_sel.s, rtol=1e-3, atol=1e-12)
+    print("maximum length (diff, kth-ties, decision-ties, score-ties):",
+          explain_selection_diff(sel[0], oracle_sel, N))
+
+
 # ------------------------------------------------------------------ incremental pack
 def _check_pack_state(w, lb, d, b, want_pos, N, ordered=False):
     """Rows [0, packed_len) hold exactly sink + want_pos, each the stored row of its slot's
