@@ -110,12 +110,20 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack(PackArgs a) {
 //
 // Each (listed row, KV head) "ig" has two lists: its selection (K entries) and its slots
 // (n_sink + K).  Both are cut into chunks of kChunk entries, one workgroup per chunk, so the
-// scattered map accesses of one ig spread over many CUs.  Four kernels, each needing the
-// previous one complete:
-//   1. mark     held positions that stay selected get kKeepBit in the map;
-//   2. count    slot chunks free the held rows not marked (and clear the marks), sel chunks
-//               flag the selected positions not held; per-chunk counts of both and of the
-//               valid selection entries;
+// scattered map accesses of one ig spread over many CUs.  The map (one word per position,
+// megabytes per layer) is read at scattered places once per update, by kernel 1, and
+// written only where a row changes hands; the other kernels read two small per-ig lists
+// in the workspace instead: the old slot of each selection entry, and for each slot the
+// index of the selection entry that claimed it.  Four kernels, each needing the previous
+// one complete:
+//   1. mark     sel chunks record each entry's old slot (map value, -1 if not held), claim
+//               that slot with the entry's index, and count the entries not held and the
+//               valid ones per chunk;
+//   2. count    slot chunks find the held rows whose position is no longer selected: a
+//               slot is kept when its claim names a selection entry holding its position
+//               (a claim left over from an earlier update passes that test only if its
+//               position is selected again, so the claims need no clearing); dropped
+//               positions leave the map, and each chunk counts its free slots;
 //   3. free     slot chunks write their free slots at (earlier chunks' count + in-chunk
 //               prefix), so the free list is in slot order;
 //   4. assign   sel chunks give the j-th new position the j-th free slot (past the old end
@@ -129,7 +137,6 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack(PackArgs a) {
 
 constexpr int kChunk = 1024;           // list entries per workgroup
 constexpr int kChunkThreads = 256;     // four consecutive entries per thread
-constexpr int32_t kKeepBit = 1 << 30;  // marks a held position that stays selected
 
 struct UpdArgs {
   const int32_t* sel;
@@ -148,6 +155,9 @@ struct UpdArgs {
   int32_t* cnt_valid;  // [n_ig][nc_sel]
   int32_t* free_slot;  // [n_ig][K]
   int32_t* plen_old;   // [n_ig] held length before this update (written by kernel 3)
+  int32_t* old_slot;   // [n_ig][K]: slot of each selection entry before the update, or -1
+  int32_t* claim;      // [n_ig][nc_slot * kChunk]: index of the selection entry holding the
+                       // slot's position (valid only where it says so, see is_kept)
   uint32_t* status;    // device contract flags, may be null
   int Hkv, K, n_sink, cap, nc_sel, nc_slot, max_pages, row_bytes;
 };
@@ -188,77 +198,75 @@ __device__ __forceinline__ bool in_map(const UpdArgs& a, int p) {
   return p >= 0 && p < a.map_stride;
 }
 
-// Kernel 1: mark.
+// Slots of one ig's claim list.
+__device__ __forceinline__ int claim_len(const UpdArgs& a) { return a.nc_slot * kChunk; }
+
+// Whether held slot sl, holding position q, keeps its row: q is in the map and the slot's
+// claim names a selection entry equal to q.  Kernel 1 claimed sl for the entry holding q if
+// there is one; a claim from an earlier update that still names an entry equal to q is
+// equally right, and any other value fails the test.
+__device__ __forceinline__ bool is_kept(const UpdArgs& a, const Ig& r, int sl, int q) {
+  if (!in_map(a, q)) return false;
+  const int c = a.claim[(size_t)r.ig * claim_len(a) + sl];
+  return c >= 0 && c < a.K && a.sel[r.bg * a.K + c] == q;
+}
+
+// Kernel 1: mark (sel chunks).
 __global__ __launch_bounds__(kChunkThreads) void k_upd_mark(UpdArgs a) {
+  __shared__ uint32_t red[kChunkThreads / 64];
   const Ig r = ig_of(a, blockIdx.x, a.nc_sel);
   if (r.b < 0) return;
   const int32_t* sel = a.sel + r.bg * a.K;
-  int32_t* map = a.map + r.bg * a.map_stride;
+  const int32_t* map = a.map + r.bg * a.map_stride;
+  int32_t* old_slot = a.old_slot + (size_t)r.ig * a.K;
+  int32_t* claim = a.claim + (size_t)r.ig * claim_len(a);
   const int k0 = r.chunk * kChunk + 4 * (int)threadIdx.x;
   int q[4], v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) q[i] = k0 + i < a.K ? sel[k0 + i] : -1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = in_map(a, q[i]) ? map[q[i]] : -1;
+  uint32_t c_add = 0, c_valid = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (v[i] >= 0) map[q[i]] = v[i] | kKeepBit;
+  for (int i = 0; i < 4; ++i) {
+    if (k0 + i < a.K) old_slot[k0 + i] = v[i] >= 0 ? v[i] : -1;
+    if (v[i] >= 0 && v[i] < claim_len(a)) claim[v[i]] = k0 + i;
+    c_add += (q[i] >= 0 && v[i] < 0) ? 1u : 0u;  // selected, not held
+    c_valid += q[i] >= 0 ? 1u : 0u;              // valid entry
+  }
+  const uint32_t t1 = block_sum_u32(c_add, red), t2 = block_sum_u32(c_valid, red);
+  if (threadIdx.x == 0) {
+    a.cnt_add[(size_t)r.ig * a.nc_sel + r.chunk] = (int32_t)t1;
+    a.cnt_valid[(size_t)r.ig * a.nc_sel + r.chunk] = (int32_t)t2;
+  }
 }
 
-// Kernel 2: count.  Workgroups [0, n_ig * nc_slot) take slot chunks, the rest sel chunks.
-__global__ __launch_bounds__(kChunkThreads) void k_upd_count(UpdArgs a, int n_ig) {
+// Kernel 2: count (slot chunks).
+__global__ __launch_bounds__(kChunkThreads) void k_upd_count(UpdArgs a) {
   __shared__ uint32_t red[kChunkThreads / 64];
-  const bool slots = (int)blockIdx.x < n_ig * a.nc_slot;
-  const int x = slots ? (int)blockIdx.x : (int)blockIdx.x - n_ig * a.nc_slot;
-  const Ig r = ig_of(a, x, slots ? a.nc_slot : a.nc_sel);
+  const Ig r = ig_of(a, blockIdx.x, a.nc_slot);
   if (r.b < 0) return;
   int32_t* map = a.map + r.bg * a.map_stride;
   const int k0 = r.chunk * kChunk + 4 * (int)threadIdx.x;
-  uint32_t c1 = 0, c2 = 0;
-  int q[4], v[4];
-  if (slots) {
-    const int plen = held_len(a, r.bg);
-    const int32_t* ppos = a.ppos + r.bg * a.cap;
+  const int plen = held_len(a, r.bg);
+  const int32_t* ppos = a.ppos + r.bg * a.cap;
+  int q[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sl = k0 + i;
-      q[i] = (sl >= a.n_sink && sl < plen) ? ppos[sl] : -2;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int sl = k0 + i;
+    q[i] = (sl >= a.n_sink && sl < plen) ? ppos[sl] : -2;
+  }
+  uint32_t c_free = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = in_map(a, q[i]) ? map[q[i]] : 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (q[i] == -2) continue;
-      if (v[i] & kKeepBit) {
-        map[q[i]] = v[i] & ~kKeepBit;
-      } else {
-        if (in_map(a, q[i])) map[q[i]] = -1;
-        ++c1;
-      }
-    }
-  } else {
-    const int32_t* sel = a.sel + r.bg * a.K;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = k0 + i < a.K ? sel[k0 + i] : -1;
-    // A position not held reads -1 whatever the slot chunks do: they write held positions
-    // only, and the held positions that are not selected any more are not in this list.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = in_map(a, q[i]) ? map[q[i]] : 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c1 += (q[i] >= 0 && v[i] < 0) ? 1u : 0u;  // selected, not held
-      c2 += q[i] >= 0 ? 1u : 0u;                // valid entry
+  for (int i = 0; i < 4; ++i) {
+    if (q[i] == -2) continue;
+    if (!is_kept(a, r, k0 + i, q[i])) {
+      if (in_map(a, q[i])) map[q[i]] = -1;
+      ++c_free;
     }
   }
-  const uint32_t t1 = block_sum_u32(c1, red), t2 = block_sum_u32(c2, red);
-  if (threadIdx.x == 0) {
-    if (slots) {
-      a.cnt_free[(size_t)r.ig * a.nc_slot + r.chunk] = (int32_t)t1;
-    } else {
-      a.cnt_add[(size_t)r.ig * a.nc_sel + r.chunk] = (int32_t)t1;
-      a.cnt_valid[(size_t)r.ig * a.nc_sel + r.chunk] = (int32_t)t2;
-    }
-  }
+  const uint32_t t = block_sum_u32(c_free, red);
+  if (threadIdx.x == 0) a.cnt_free[(size_t)r.ig * a.nc_slot + r.chunk] = (int32_t)t;
 }
 
 // Sums of one ig's chunk counts: before chunk `upto` and in all.
@@ -312,7 +320,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_free(UpdArgs a) {
     }
     return;
   }
-  // free slots of this chunk: the held rows whose position is no longer in the map
+  // free slots of this chunk: the held rows that kernel 2 found not kept
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sl = k0 + i;
@@ -322,7 +330,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_free(UpdArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (q[i] == -2) continue;
-    if (!in_map(a, q[i]) || map[q[i]] < 0) fmask |= 1u << i;
+    if (!is_kept(a, r, k0 + i, q[i])) fmask |= 1u << i;
   }
   uint32_t tot;
   uint32_t j = (uint32_t)sh[0] +
@@ -369,9 +377,10 @@ __global__ __launch_bounds__(kChunkThreads) void k_upd_assign(UpdArgs a) {
     for (int i = 0; i < 4; ++i)
       if (q[i] >= 0) amask |= 1u << i;
   } else {
+    const int32_t* old_slot = a.old_slot + (size_t)r.ig * a.K;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (q[i] >= 0 && (!in_map(a, q[i]) || map[q[i]] < 0)) amask |= 1u << i;
+      if (q[i] >= 0 && old_slot[k0 + i] < 0) amask |= 1u << i;
   }
   uint32_t tot;
   const uint32_t first = block_exscan<kChunkThreads>(__builtin_popcount(amask), wsum, &tot);
@@ -462,7 +471,8 @@ size_t pack_update_ws(const sfi_shape& s, const sfi_select_params& prm, int n_se
   const size_t nc_slot = ceil_div(prm.n_sink + prm.top_k + 15, kChunk);  // >= packed_cap
   auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
   return r256(n_ig * nc_slot * 4) + 2 * r256(n_ig * nc_sel * 4) +
-         r256(n_ig * (size_t)prm.top_k * 4) + r256(n_ig * 4);
+         2 * r256(n_ig * (size_t)prm.top_k * 4) + r256(n_ig * 4) +
+         r256(n_ig * nc_slot * kChunk * 4);
 }
 
 hipError_t launch_pack_update(const sfi_shape& s, const sfi_select_params& prm,
@@ -487,6 +497,10 @@ hipError_t launch_pack_update(const sfi_shape& s, const sfi_select_params& prm,
   a.free_slot = reinterpret_cast<int32_t*>(w);
   w += r256((size_t)n_ig * prm.top_k * 4);
   a.plen_old = reinterpret_cast<int32_t*>(w);
+  w += r256((size_t)n_ig * 4);
+  a.old_slot = reinterpret_cast<int32_t*>(w);
+  w += r256((size_t)n_ig * prm.top_k * 4);
+  a.claim = reinterpret_cast<int32_t*>(w);
   a.sel = sel_idx;
   a.seq_ids = seq_ids;
   a.kc = reinterpret_cast<const uint8_t*>(k_cache);
@@ -507,7 +521,7 @@ hipError_t launch_pack_update(const sfi_shape& s, const sfi_select_params& prm,
   a.row_bytes = s.head_dim * (s.dtype == SFI_BF16 ? 2 : 4);
   const dim3 blk(kChunkThreads);
   hipLaunchKernelGGL(k_upd_mark, dim3(n_ig * a.nc_sel), blk, 0, stream, a);
-  hipLaunchKernelGGL(k_upd_count, dim3(n_ig * (a.nc_slot + a.nc_sel)), blk, 0, stream, a, n_ig);
+  hipLaunchKernelGGL(k_upd_count, dim3(n_ig * a.nc_slot), blk, 0, stream, a);
   hipLaunchKernelGGL(k_upd_free, dim3(n_ig * a.nc_slot), blk, 0, stream, a);
   const dim3 g_sel(n_ig * a.nc_sel);
   switch (a.row_bytes / 16) {
