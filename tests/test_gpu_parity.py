@@ -790,7 +790,9 @@ def _check_pack_state(w, lb, d, b, want_pos, N, ordered=False):
 
 def test_pack_update_keeps_held_rows_and_adds_new_ones():
     """A run of selections through sfi_pack_update: growing K_eff with 0-100% turnover, a
-    shrink (rebuilt in sfi_pack's order), an emptied buffer, and a row the list skips."""
+    shrink (rebuilt in sfi_pack's order), an emptied buffer, and a row the list skips.
+    Before every call the workspace is filled with seeded integers in [-2, top_k + 2), so
+    that leftover per-slot claims look valid: the result must not depend on them."""
     w = get("qwen3_0p6b_8k").replace(batch=2, top_k=300, name="pack_update")
     d, eng, lb = _setup(w)
     dev = "cuda"
@@ -798,6 +800,8 @@ def test_pack_update_keeps_held_rows_and_adds_new_ones():
     lo, hi = O.candidates(N, w.n_sink, w.n_recent)
     rng = np.random.default_rng(5)
     ws = L.workspace(L.sfi_pack_update_ws(eng.shape, eng.params, w.batch), dev)
+    scramble = torch.Generator(device=dev)
+    scramble.manual_seed(11)
     ids = torch.tensor([0, 1], dtype=torch.int32, device=dev)
     cur = [[np.sort(rng.choice(np.arange(lo, hi), 200, replace=False)) for _ in range(8)]
            for _ in range(2)]
@@ -809,6 +813,7 @@ def test_pack_update_keeps_held_rows_and_adds_new_ones():
             for g in range(w.num_kv_heads):
                 sel[b, g, :len(sets[b][g])] = torch.from_numpy(sets[b][g].astype(np.int32))
         lb.sel_idx.copy_(sel.to(dev))
+        ws.view(torch.int32).random_(-2, w.top_k + 2, generator=scramble)
         prev_pos = lb.packed_pos.cpu().numpy()
         prev_len = lb.packed_len.cpu().numpy()
         L.sfi_pack_update(eng.shape, eng.params, lb.k_cache, lb.v_cache, lb.block_table,
