@@ -20,8 +20,14 @@ in the docstring of the function that applies it.
 
 Parity status of each function:
   attention, merge_segments, evidence, window_evidence, window_queries, fuse, topk, pack,
-  fast_attention, schedule, boundary_flags, step_control:
-      pinned by tests (closed forms, library routines, brute force).
+  packed_positions, fast_attention, fast_attention_single_pass, schedule, boundary_flags,
+  step_control, candidates, recent_start_at, recent_start_sliding, run_sequence:
+      pinned by tests (closed forms, library routines, brute force, partition and
+      equivalence invariants).
+  select, select_window, select_from_evidence, select_from_scores,
+  select_greedy_from_scores: compositions of the pinned steps, each also checked end to
+      end (worked examples, K covering the candidates, the greedy reading's reduction to
+      the one-pass one without soft-NMS).
   key_norms: pinned (library norm).
   prior: pinned to its reading by a hand-derived example (the key-norm floor, the
       distance N-1-j, the +1 terms and the normalisation) and by invariants (normalisation,

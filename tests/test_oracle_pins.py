@@ -597,3 +597,48 @@ def test_fast_memory_partitions_history():
             N = N0 + c
             cover = list(range(0, ns)) + list(range(lo, hi)) + list(range(rs, N))
             assert sorted(cover) == list(range(N)) or N0 < ns
+
+
+def test_packed_positions_brute_force():
+    """The compact buffer's positions are the sink tokens, then the selection in the order
+    sfi_select writes it (ascending), with the -1 padding dropped; pack gathers exactly those
+    rows."""
+    r = np.random.default_rng(23)
+    for n_sink, K, N in ((4, 6, 40), (0, 5, 12), (3, 1, 9), (2, 7, 7)):
+        keff = int(r.integers(0, K + 1))
+        chosen = np.sort(r.choice(np.arange(n_sink, N), min(keff, N - n_sink), replace=False))
+        sel = np.full(K, -1)
+        sel[:len(chosen)] = chosen
+        want = []
+        for p in range(n_sink):
+            want.append(p)
+        for p in chosen:
+            want.append(int(p))
+        assert O.packed_positions(sel, n_sink).tolist() == want
+        Kt = r.standard_normal((1, N, 3))
+        Vt = r.standard_normal((1, N, 3))
+        pos, pk, pv = O.pack(Kt, Vt, sel[None, :], n_sink)
+        assert pos[0].tolist() == want
+        for i, p in enumerate(want):
+            assert (pk[0][i] == Kt[0, p]).all() and (pv[0][i] == Vt[0, p]).all()
+
+
+def test_greedy_selection_without_soft_nms_is_the_one_pass_selection():
+    """With alpha_soft = 0 neither reading of soft-NMS scales a score, so the greedy
+    selection equals the one-pass one (exclusivity applies the same in both)."""
+    r = np.random.default_rng(29)
+    for Hkv, N, K, R, a_c in ((1, 50, 10, 2, 0.5), (3, 80, 17, 4, 0.3), (2, 30, 40, 1, 1.0)):
+        s = r.random((Hkv, N))
+        s[:, 7] = s[:, 8]  # an exact tie between neighbours
+        np.testing.assert_array_equal(
+            O.select_greedy_from_scores(s, N, 3, 5, K, R, 0.0, a_c),
+            O.select_from_scores(s, N, 3, 5, K, R, 0.0, a_c))
+
+
+def test_sliding_recent_segment():
+    """The sliding reading keeps exactly the newest min(W, N - n_sink) positions (never a
+    sink position), and at a slow step it starts where the frozen reading does."""
+    for N, ns, W in ((100, 4, 10), (12, 4, 10), (4, 4, 3), (50, 0, 50), (51, 0, 50)):
+        rs = O.recent_start_sliding(N, ns, W)
+        assert N - rs == min(W, max(N - ns, 0)) and rs >= ns
+        assert rs == O.recent_start_at(N, ns, W)
