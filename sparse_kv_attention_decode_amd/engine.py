@@ -15,7 +15,8 @@ attention of every layer is issued on stream 1; the Selector and pack of layer i
 issued on a Selector stream after an event recorded behind layer i's slow attention, so
 they run while stream 1 continues with layer i+1.  There are two Selector streams, used by
 alternate layers, so that the short dependent kernels of two layers' Selectors overlap
-each other too.  Before layer i's next attention, stream 1 waits for layer i's pack event.
+each other too.  A one-layer stack runs its Selector and pack on stream 1 by default:
+nothing could run beside them, and the cross-stream waits would only add latency.  Before layer i's next attention, stream 1 waits for layer i's pack event.
 All streams have the default priority.  Before a slow step queues its first Selector-stream
 wait, the host lets stream 1 come within one step of it (`paced`), so that no such wait sits in a
 queue far ahead of the attention it depends on.
