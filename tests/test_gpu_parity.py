@@ -225,7 +225,12 @@ RAGGED_RECENT = dict(batch=4, context=6000, n_recent=600, top_k=1500, steps=40, 
                                        id="ragged_recent_b4"),
                           pytest.param("qwen3_0p6b_8k", 1, False, None,
                                        dict(lambda_clip=0.3, name="lambda_clip_8k"),
-                                       id="lambda_clip")])
+                                       id="lambda_clip"),
+                          pytest.param("qwen3_0p6b_8k", 1, False, True,
+                                       dict(batch=48, context=1536, num_q_heads=8,
+                                            num_kv_heads=4, top_k=256, n_recent=128, steps=10,
+                                            name="batch48"),
+                                       id="batch48_incremental")])
 def test_trajectory_lockstep(name, win, sliding, inc, over):
     """Every step of the seeded trajectory through the two-stream engine.  Slow steps:
     dense output and the selection (near-tie rule); the oracle then continues with the
